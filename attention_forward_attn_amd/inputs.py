@@ -1,0 +1,126 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module holds no attention arithmetic: it only draws random tensors and
+lays them out.  Both the HIP path and the fp64 oracle receive exactly the
+tensors produced here (the oracle upcasts the bf16 values exactly).
+
+Recipe: ``torch.Generator('cpu').manual_seed(seed)``; draw order is decode
+lengths first (decode only), then Q, K, V, then sink logits.  Values are fp32
+N(0, 1) rounded to bf16 with round-to-nearest-even; sinks stay fp32 N(0, 1).
+Prefill tensors are [b, h, s, d] contiguous; the decode KV cache is packed
+token-major, [sum_b L_b, h_kv, d], contiguous per sequence, with ``kv_start``
+the exclusive prefix sum of the lengths.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+BASE_SEED = 1234
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: shapes, mask and the seed its inputs use."""
+
+    name: str
+    kind: str  # "prefill" or "decode"
+    seed: int
+    d: int
+    h_q: int
+    h_kv: int
+    b: int = 1
+    s_q: int = 0
+    s_k: int = 0
+    causal: bool = False
+    window: int = 0
+    sinks: bool = False
+    # decode only
+    len_lo: int = 0
+    len_hi: int = 0
+    split: int = 512
+    notes: dict = field(default_factory=dict, compare=False)
+
+
+def _w(*args, **kw) -> Workload:
+    return Workload(*args, **kw)
+
+
+# The five workload families; seed = BASE_SEED + family index.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        # family 0: tiny single head
+        _w("tiny_b1_h1_s256_d64", "prefill", BASE_SEED + 0, 64, 1, 1, b=1, s_q=256, s_k=256),
+        # family 1: dense MHA prefill, both masks
+        _w("mha_b2_h16_s4096_d128", "prefill", BASE_SEED + 1, 128, 16, 16, b=2, s_q=4096, s_k=4096),
+        _w("mha_b2_h16_s4096_d128_causal", "prefill", BASE_SEED + 1, 128, 16, 16, b=2, s_q=4096,
+           s_k=4096, causal=True),
+        _w("mha_b1_h16_s8192_d128", "prefill", BASE_SEED + 1, 128, 16, 16, b=1, s_q=8192, s_k=8192),
+        _w("mha_b1_h16_s8192_d128_causal", "prefill", BASE_SEED + 1, 128, 16, 16, b=1, s_q=8192,
+           s_k=8192, causal=True),
+        _w("mha_b4_h32_s2048_d64", "prefill", BASE_SEED + 1, 64, 32, 32, b=4, s_q=2048, s_k=2048),
+        _w("mha_b4_h32_s2048_d64_causal", "prefill", BASE_SEED + 1, 64, 32, 32, b=4, s_q=2048,
+           s_k=2048, causal=True),
+        # family 2: GQA causal with LSE; sliding window + sink variant
+        _w("gqa_b2_hq32_hkv8_s4096_d128_causal", "prefill", BASE_SEED + 2, 128, 32, 8, b=2,
+           s_q=4096, s_k=4096, causal=True),
+        _w("gqa_b2_hq32_hkv8_s4096_d128_swa1024_sink", "prefill", BASE_SEED + 2, 128, 32, 8, b=2,
+           s_q=4096, s_k=4096, causal=True, window=1024, sinks=True),
+        # family 3: MQA decode, split-KV in chunks of 512
+        _w("mqa_decode_B64_hq128_d128", "decode", BASE_SEED + 3, 128, 128, 1, b=64,
+           len_lo=1024, len_hi=8192),
+        _w("mqa_decode_B64_hq128_d256", "decode", BASE_SEED + 3, 256, 128, 1, b=64,
+           len_lo=1024, len_hi=8192),
+        # family 4: large head dims, long context
+        _w("long_b1_h8_s16384_d256_causal", "prefill", BASE_SEED + 4, 256, 8, 8, b=1,
+           s_q=16384, s_k=16384, causal=True),
+        _w("wide_b1_h4_s4096_d512_causal", "prefill", BASE_SEED + 4, 512, 4, 4, b=1,
+           s_q=4096, s_k=4096, causal=True),
+    ]
+}
+
+
+def _randn_bf16(shape, gen: torch.Generator) -> torch.Tensor:
+    return torch.randn(*shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
+def prefill_inputs(b: int, h_q: int, h_kv: int, s_q: int, s_k: int, d: int, seed: int,
+                   with_sinks: bool = False):
+    """Return dict(q, k, v, sinks) on the CPU: bf16 [b,h,s,d] and fp32 [h_q] (or None)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    q = _randn_bf16((b, h_q, s_q, d), gen)
+    k = _randn_bf16((b, h_kv, s_k, d), gen)
+    v = _randn_bf16((b, h_kv, s_k, d), gen)
+    sinks = torch.randn(h_q, generator=gen, dtype=torch.float32) if with_sinks else None
+    return {"q": q, "k": k, "v": v, "sinks": sinks}
+
+
+def decode_inputs(B: int, h_q: int, h_kv: int, d: int, len_lo: int, len_hi: int, seed: int,
+                  with_sinks: bool = False):
+    """Return dict(q, k, v, kv_start, kv_len, sinks) on the CPU.
+
+    Lengths are uniform integers in [len_lo, len_hi]; q is bf16 [B,h_q,d];
+    k and v are bf16 [sum L, h_kv, d]; kv_start int64 [B]; kv_len int32 [B].
+    """
+    gen = torch.Generator("cpu").manual_seed(seed)
+    kv_len = torch.randint(len_lo, len_hi + 1, (B,), generator=gen, dtype=torch.int64)
+    kv_start = torch.zeros(B, dtype=torch.int64)
+    if B > 1:
+        kv_start[1:] = torch.cumsum(kv_len, 0)[:-1]
+    total = int(kv_len.sum())
+    q = _randn_bf16((B, h_q, d), gen)
+    k = _randn_bf16((total, h_kv, d), gen)
+    v = _randn_bf16((total, h_kv, d), gen)
+    sinks = torch.randn(h_q, generator=gen, dtype=torch.float32) if with_sinks else None
+    return {"q": q, "k": k, "v": v, "kv_start": kv_start, "kv_len": kv_len.to(torch.int32),
+            "sinks": sinks}
+
+
+def workload_inputs(w: Workload):
+    """Inputs of a named workload (see WORKLOADS)."""
+    if w.kind == "prefill":
+        return prefill_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed, w.sinks)
+    return decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed, w.sinks)
