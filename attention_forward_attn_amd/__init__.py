@@ -1,0 +1,17 @@
+"""Fused attention forward for MI355X (gfx950): prefill, split-KV decode, LSE merge.
+
+The computation lives in hand-written HIP kernels behind a C ABI
+(``include/attn_fwd.h``, built as ``libattnfwd.so``); this package only
+marshals torch device tensors into that ABI.  Importing it does not load the
+library; the first call does, and raises if the library has not been built.
+"""
+
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    AttnError,
+    combine,
+    decode,
+    decode_workspace_size,
+    load_library,
+    prefill,
+)

@@ -1,0 +1,271 @@
+"""ctypes binding of ``libattnfwd.so`` (C ABI declared in include/attn_fwd.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch tensors are used as device memory and for the
+current stream; there is no fallback of any kind -- if the library is missing
+or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattnfwd.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_STRIDE",
+    4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_UNSUPPORTED", 6: "ATTN_ERR_WORKSPACE", 7: "ATTN_ERR_HIP",
+}
+
+
+class AttnError(RuntimeError):
+    """A non-OK status returned by the C ABI."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("sinks", ctypes.c_void_p),
+        ("b", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+        ("s_q", ctypes.c_int32), ("s_k", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_ss", ctypes.c_int64),
+        ("k_sb", ctypes.c_int64), ("k_sh", ctypes.c_int64), ("k_ss", ctypes.c_int64),
+        ("v_sb", ctypes.c_int64), ("v_sh", ctypes.c_int64), ("v_ss", ctypes.c_int64),
+        ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64), ("o_ss", ctypes.c_int64),
+        ("lse_sb", ctypes.c_int64), ("lse_sh", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("kv_start", ctypes.c_void_p), ("kv_len", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("sinks", ctypes.c_void_p),
+        ("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32), ("split_size", ctypes.c_int32),
+        ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("k_st", ctypes.c_int64), ("k_sh", ctypes.c_int64),
+        ("v_st", ctypes.c_int64), ("v_sh", ctypes.c_int64),
+        ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("lse_sb", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class CombineArgs(ctypes.Structure):
+    _fields_ = [
+        ("o_parts", ctypes.c_void_p), ("lse_parts", ctypes.c_void_p),
+        ("o_out", ctypes.c_void_p), ("lse_out", ctypes.c_void_p),
+        ("n_parts", ctypes.c_int32), ("rows", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("o_part_stride", ctypes.c_int64), ("o_row_stride", ctypes.c_int64),
+        ("lse_part_stride", ctypes.c_int64), ("lse_row_stride", ctypes.c_int64),
+        ("o_out_row_stride", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is missing: build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` (there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    lib.attn_fwd_prefill.argtypes = [ctypes.POINTER(PrefillArgs), ctypes.c_void_p]
+    lib.attn_fwd_prefill.restype = ctypes.c_int
+    lib.attn_fwd_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_void_p]
+    lib.attn_fwd_decode.restype = ctypes.c_int
+    lib.attn_combine.argtypes = [ctypes.POINTER(CombineArgs), ctypes.c_void_p]
+    lib.attn_combine.restype = ctypes.c_int
+    lib.attn_fwd_decode_workspace_size.argtypes = [ctypes.c_int32] * 5
+    lib.attn_fwd_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = load_library()
+        raise AttnError(status, lib.attn_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _require_cuda_bf16(name, t, ndim):
+    import torch
+
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in the head dim")
+
+
+def prefill_args(q, k, v, out, lse, sinks, scale, causal, window) -> PrefillArgs:
+    """Fill the C argument struct from [b, h, s, d]-indexed tensors (any strides)."""
+    b, h_q, s_q, d = q.shape
+    _, h_kv, s_k, _ = k.shape
+    a = PrefillArgs()
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.b, a.h_q, a.h_kv, a.s_q, a.s_k, a.d = b, h_q, h_kv, s_q, s_k, d
+    a.q_sb, a.q_sh, a.q_ss = q.stride(0), q.stride(1), q.stride(2)
+    a.k_sb, a.k_sh, a.k_ss = k.stride(0), k.stride(1), k.stride(2)
+    a.v_sb, a.v_sh, a.v_ss = v.stride(0), v.stride(1), v.stride(2)
+    a.o_sb, a.o_sh, a.o_ss = out.stride(0), out.stride(1), out.stride(2)
+    if lse is not None:
+        a.lse_sb, a.lse_sh = lse.stride(0), lse.stride(1)
+    a.scale = scale
+    a.causal = 1 if causal else 0
+    a.window = int(window)
+    return a
+
+
+def prefill(q, k, v, *, scale: float | None = None, causal: bool = False, window: int = 0,
+            sinks=None, out=None, lse=None, return_lse: bool = True, stream=None):
+    """Fused attention forward over [b, h, s, d]-indexed bf16 device tensors.
+
+    q is [b, h_q, s_q, d]; k and v are [b, h_kv, s_k, d] (any strides with a
+    unit head-dim stride, e.g. a transposed [b, s, h, d] view).  Returns
+    (O, LSE): O bf16 shaped like q, LSE fp32 [b, h_q, s_q] (None when
+    ``return_lse`` is False and no ``lse`` buffer is given).
+    """
+    import torch
+
+    lib = load_library()
+    _require_cuda_bf16("q", q, 4)
+    _require_cuda_bf16("k", k, 4)
+    _require_cuda_bf16("v", v, 4)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    b, h_q, s_q, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((b, h_q, s_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
+    if lse is not None and lse.stride(-1) != 1:
+        raise ValueError("lse must have unit stride along the sequence")
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
+        raise ValueError("sinks must be a contiguous float32 device tensor")
+    a = prefill_args(q, k, v, out, lse, sinks, scale, causal, window)
+    _check(lib.attn_fwd_prefill(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def decode_workspace_size(B: int, h_q: int, d: int, max_kv_len: int, split_size: int = 512) -> int:
+    return int(load_library().attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
+
+
+def decode(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = None, sinks=None,
+           split_size: int = 512, workspace=None, out=None, lse=None, return_lse: bool = True,
+           stream=None):
+    """Single-token decode over a per-sequence contiguous KV cache (split-KV + LSE merge).
+
+    q: bf16 [B, h_q, d]; k, v: bf16 [T, h_kv, d] (token-major cache; any token
+    and head strides with a unit head-dim stride); kv_start: int64 [B];
+    kv_len: int32 [B]; max_kv_len: host upper bound on kv_len.
+    Returns (O bf16 [B, h_q, d], LSE fp32 [B, h_q] or None).
+    """
+    import torch
+
+    lib = load_library()
+    _require_cuda_bf16("q", q, 3)
+    _require_cuda_bf16("k", k, 3)
+    _require_cuda_bf16("v", v, 3)
+    if kv_start.dtype != torch.int64 or kv_len.dtype != torch.int32:
+        raise ValueError("kv_start must be int64 and kv_len int32")
+    B, h_q, d = q.shape
+    h_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = int(lib.attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, h_q), dtype=torch.float32, device=q.device)
+    if lse is not None and lse.stride(-1) != 1:
+        raise ValueError("lse must have unit stride along the heads")
+    a = DecodeArgs()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.kv_start, a.kv_len = kv_start.data_ptr(), kv_len.data_ptr()
+    a.o = out.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.B, a.h_q, a.h_kv, a.d = B, h_q, h_kv, d
+    a.max_kv_len, a.split_size = int(max_kv_len), int(split_size)
+    a.q_sb, a.q_sh = q.stride(0), q.stride(1)
+    a.k_st, a.k_sh = k.stride(0), k.stride(1)
+    a.v_st, a.v_sh = v.stride(0), v.stride(1)
+    a.o_sb, a.o_sh = out.stride(0), out.stride(1)
+    a.lse_sb = lse.stride(0) if lse is not None else 0
+    a.scale = scale
+    _check(lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
+                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def combine(o_parts, lse_parts, *, out=None, lse=None, return_lse: bool = True, stream=None):
+    """Merge partial results over disjoint key sets: o_parts fp32 [n, rows, d], lse_parts fp32 [n, rows]."""
+    import torch
+
+    lib = load_library()
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts and lse_parts must be float32")
+    if o_parts.dim() != 3 or lse_parts.dim() != 2 or o_parts.stride(-1) != 1:
+        raise ValueError("o_parts must be [n, rows, d] with unit last stride, lse_parts [n, rows]")
+    n, rows, d = o_parts.shape
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device=o_parts.device)
+    if lse is None and return_lse:
+        lse = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    a = CombineArgs()
+    a.o_parts, a.lse_parts = o_parts.data_ptr(), lse_parts.data_ptr()
+    a.o_out = out.data_ptr()
+    a.lse_out = lse.data_ptr() if lse is not None else None
+    a.n_parts, a.rows, a.d = n, rows, d
+    a.o_part_stride, a.o_row_stride = o_parts.stride(0), o_parts.stride(1)
+    a.lse_part_stride, a.lse_row_stride = lse_parts.stride(0), lse_parts.stride(1)
+    a.o_out_row_stride = out.stride(0)
+    _check(lib.attn_combine(ctypes.byref(a), _stream(stream)))
+    return out, lse

@@ -1,0 +1,282 @@
+// C ABI of the attention forward library: argument validation, instance
+// selection, grid sizing and launch.  Every check runs on the host before any
+// HIP call, so a rejected call has no side effect.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/attn_fwd.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+attn_status fail(attn_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+attn_status ok() {
+  g_err[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool bf16_stride_ok(int64_t s) { return s >= 0 && (s % 8) == 0; }
+constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
+
+// Largest element offset reachable through (extent, stride) pairs, plus the row length.
+int64_t span(std::initializer_list<std::pair<int64_t, int64_t>> dims, int64_t last) {
+  int64_t s = last;
+  for (auto &d : dims)
+    if (d.first > 0) s += (d.first - 1) * d.second;
+  return s;
+}
+
+attn_status hip_fail(hipError_t e, const char *what) {
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_abi_version(void) { return ATTN_FWD_ABI_VERSION; }
+
+const char *attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_NULL: return "ATTN_ERR_NULL";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE";
+    case ATTN_ERR_STRIDE: return "ATTN_ERR_STRIDE";
+    case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+  }
+  return "ATTN_ERR_UNKNOWN";
+}
+
+const char *attn_last_error(void) { return g_err; }
+
+attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
+  if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
+  if (a->b < 1 || a->h_q < 1 || a->h_kv < 1 || a->s_q < 0 || a->s_k < 0)
+    return fail(ATTN_ERR_SHAPE, "need b, h_q, h_kv >= 1 and s_q, s_k >= 0 (got b=%d h_q=%d h_kv=%d s_q=%d s_k=%d)",
+                a->b, a->h_q, a->h_kv, a->s_q, a->s_k);
+  if (a->h_q % a->h_kv != 0)
+    return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
+  if (a->d != 64 && a->d != 128 && a->d != 256 && a->d != 512)
+    return fail(ATTN_ERR_SHAPE, "d must be 64, 128, 256 or 512 (got %d)", a->d);
+  if (!(std::isfinite(a->scale) && a->scale > 0.0f))
+    return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1");
+  if (a->window < 0) return fail(ATTN_ERR_SHAPE, "window must be >= 0");
+  if (a->window > 0 && !a->causal) return fail(ATTN_ERR_SHAPE, "a window requires causal = 1");
+  if (a->s_q == 0) return ok();
+  if (!a->q || !a->o || (a->s_k > 0 && (!a->k || !a->v)))
+    return fail(ATTN_ERR_NULL, "q, o (and k, v when s_k > 0) must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->o) || (a->s_k > 0 && (!aligned16(a->k) || !aligned16(a->v))))
+    return fail(ATTN_ERR_ALIGN, "q, k, v, o must be 16-byte aligned");
+  if ((a->lse && !aligned4(a->lse)) || (a->sinks && !aligned4(a->sinks)))
+    return fail(ATTN_ERR_ALIGN, "lse and sinks must be 4-byte aligned");
+  const int64_t st[] = {a->q_sb, a->q_sh, a->q_ss, a->k_sb, a->k_sh, a->k_ss,
+                        a->v_sb, a->v_sh, a->v_ss, a->o_sb, a->o_sh, a->o_ss};
+  for (int64_t s : st)
+    if (!bf16_stride_ok(s)) return fail(ATTN_ERR_STRIDE, "bf16 strides must be non-negative multiples of 8 elements");
+  if (a->lse && (a->lse_sb < 0 || a->lse_sh < 0)) return fail(ATTN_ERR_STRIDE, "lse strides must be >= 0");
+  const int64_t bmax = span({{a->b, a->q_sb}, {a->h_q, a->q_sh}, {a->s_q, a->q_ss}}, a->d);
+  const int64_t kmax = span({{a->b, a->k_sb}, {a->h_kv, a->k_sh}, {a->s_k, a->k_ss}}, a->d);
+  const int64_t vmax = span({{a->b, a->v_sb}, {a->h_kv, a->v_sh}, {a->s_k, a->v_ss}}, a->d);
+  const int64_t omax = span({{a->b, a->o_sb}, {a->h_q, a->o_sh}, {a->s_q, a->o_ss}}, a->d);
+  if (bmax > (int64_t(1) << 40) || kmax > (int64_t(1) << 40) || vmax > (int64_t(1) << 40) ||
+      omax > (int64_t(1) << 40))
+    return fail(ATTN_ERR_SHAPE, "tensor extent exceeds 2^40 elements");
+  if (a->d == 512) return fail(ATTN_ERR_UNSUPPORTED, "d = 512 prefill is not built yet");
+
+  const int bm = attn::prefill_block_rows(a->d);
+  const int64_t n_qtiles = (a->s_q + bm - 1) / bm;
+  const int64_t n_units = n_qtiles * a->b * a->h_q;
+  if (n_units > kMaxIndex) return fail(ATTN_ERR_SHAPE, "too many work units (%lld)", (long long)n_units);
+
+  attn::PrefillParams p;
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k = static_cast<const uint16_t *>(a->k);
+  p.v = static_cast<const uint16_t *>(a->v);
+  p.o = static_cast<uint16_t *>(a->o);
+  p.lse = a->lse;
+  p.sinks = a->sinks;
+  p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_ss = a->q_ss;
+  p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_ss = a->k_ss;
+  p.v_sb = a->v_sb; p.v_sh = a->v_sh; p.v_ss = a->v_ss;
+  p.o_sb = a->o_sb; p.o_sh = a->o_sh; p.o_ss = a->o_ss;
+  p.lse_sb = a->lse_sb; p.lse_sh = a->lse_sh;
+  p.b = a->b; p.h_q = a->h_q; p.h_kv = a->h_kv; p.s_q = a->s_q; p.s_k = a->s_k;
+  p.ratio = a->h_q / a->h_kv;
+  p.window = a->window;
+  p.n_qtiles = (int32_t)n_qtiles;
+  p.c = a->scale * attn::kLog2e;
+
+  const int mask = a->window > 0 ? attn::kMaskCausalWindow : (a->causal ? attn::kMaskCausal : attn::kMaskNone);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (a->d) {
+    case 64: e = attn::prefill_d64(p, mask, (int)n_units, s); break;
+    case 128: e = attn::prefill_d128(p, mask, (int)n_units, s); break;
+    default: e = attn::prefill_d256(p, mask, (int)n_units, s); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+size_t attn_fwd_decode_workspace_size(int32_t B, int32_t h_q, int32_t d, int32_t max_kv_len,
+                                      int32_t split_size) {
+  if (B < 1 || h_q < 1 || d < 1 || max_kv_len < 0 || split_size < 64 || split_size % 64 != 0) return 0;
+  const int64_t n_split = max_kv_len > 0 ? (max_kv_len + split_size - 1) / split_size : 1;
+  const int64_t parts = (int64_t)B * h_q * n_split;
+  const int64_t o_bytes = parts * d * 4;
+  const int64_t o_aligned = (o_bytes + 255) / 256 * 256;
+  return (size_t)(o_aligned + parts * 4);
+}
+
+attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
+  if (a->B < 1 || a->h_q < 1 || a->h_kv < 1)
+    return fail(ATTN_ERR_SHAPE, "need B, h_q, h_kv >= 1");
+  if (a->h_q % a->h_kv != 0)
+    return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
+  if (a->d != 64 && a->d != 128 && a->d != 256)
+    return fail(ATTN_ERR_SHAPE, "decode d must be 64, 128 or 256 (got %d)", a->d);
+  if (a->max_kv_len < 0) return fail(ATTN_ERR_SHAPE, "max_kv_len must be >= 0");
+  if (a->split_size < 64 || a->split_size % 64 != 0)
+    return fail(ATTN_ERR_SHAPE, "split_size must be a positive multiple of 64 (got %d)", a->split_size);
+  if (!(std::isfinite(a->scale) && a->scale > 0.0f))
+    return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+  if (!a->q || !a->k || !a->v || !a->o || !a->kv_start || !a->kv_len)
+    return fail(ATTN_ERR_NULL, "q, k, v, o, kv_start and kv_len must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(ATTN_ERR_ALIGN, "q, k, v, o must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(a->kv_start) & 7u) || !aligned4(a->kv_len) ||
+      (a->lse && !aligned4(a->lse)) || (a->sinks && !aligned4(a->sinks)))
+    return fail(ATTN_ERR_ALIGN, "kv_start must be 8-byte and kv_len, lse, sinks 4-byte aligned");
+  const int64_t st[] = {a->q_sb, a->q_sh, a->k_st, a->k_sh, a->v_st, a->v_sh, a->o_sb, a->o_sh};
+  for (int64_t s : st)
+    if (!bf16_stride_ok(s)) return fail(ATTN_ERR_STRIDE, "bf16 strides must be non-negative multiples of 8 elements");
+  if (a->lse && a->lse_sb < 0) return fail(ATTN_ERR_STRIDE, "lse_sb must be >= 0");
+  const size_t need = attn_fwd_decode_workspace_size(a->B, a->h_q, a->d, a->max_kv_len, a->split_size);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+  const int bm = attn::decode_block_rows(a->d);
+  const int ratio = a->h_q / a->h_kv;
+  const int64_t n_split = a->max_kv_len > 0 ? (a->max_kv_len + a->split_size - 1) / a->split_size : 1;
+  const int64_t n_hblk = (ratio + bm - 1) / bm;
+  if (n_split > 65535 || (int64_t)a->h_kv * n_hblk > 65535 || a->B > 65535)
+    return fail(ATTN_ERR_SHAPE, "decode grid too large");
+
+  const int64_t parts = (int64_t)a->B * a->h_q * n_split;
+  const int64_t o_bytes = parts * a->d * 4;
+  float *o_part = static_cast<float *>(workspace);
+  float *lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + (o_bytes + 255) / 256 * 256);
+
+  attn::DecodeParams p;
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k = static_cast<const uint16_t *>(a->k);
+  p.v = static_cast<const uint16_t *>(a->v);
+  p.kv_start = a->kv_start;
+  p.kv_len = a->kv_len;
+  p.sinks = a->sinks;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.q_sb = a->q_sb; p.q_sh = a->q_sh;
+  p.k_st = a->k_st; p.k_sh = a->k_sh;
+  p.v_st = a->v_st; p.v_sh = a->v_sh;
+  p.B = a->B; p.h_q = a->h_q; p.h_kv = a->h_kv; p.ratio = ratio;
+  p.n_split = (int32_t)n_split;
+  p.split = a->split_size;
+  p.n_hblk = (int32_t)n_hblk;
+  p.c = a->scale * attn::kLog2e;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = attn::decode_split(a->d, p, s);
+  if (e != hipSuccess) return hip_fail(e, "decode split launch");
+
+  attn::CombineParams c;
+  c.o_parts = o_part;
+  c.lse_parts = lse_part;
+  c.o_out = static_cast<uint16_t *>(a->o);
+  c.lse_out = a->lse;
+  c.n_parts = (int32_t)n_split;
+  c.rows = a->B * a->h_q;
+  c.n2 = a->h_q;
+  c.d = a->d;
+  c.o_part_stride = a->d;
+  c.o_r1 = (int64_t)a->h_q * n_split * a->d;
+  c.o_r2 = n_split * a->d;
+  c.lse_part_stride = 1;
+  c.lse_r1 = (int64_t)a->h_q * n_split;
+  c.lse_r2 = n_split;
+  c.out_r1 = a->o_sb;
+  c.out_r2 = a->o_sh;
+  c.lse_out_r1 = a->lse_sb;
+  c.lse_out_r2 = 1;
+  e = attn::combine(c, s);
+  if (e != hipSuccess) return hip_fail(e, "decode combine launch");
+  return ok();
+}
+
+attn_status attn_combine(const attn_combine_args *a, void *stream) {
+  if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
+  if (a->n_parts < 1 || a->n_parts > 1024) return fail(ATTN_ERR_SHAPE, "n_parts must be in [1, 1024]");
+  if (a->rows < 0) return fail(ATTN_ERR_SHAPE, "rows must be >= 0");
+  if (a->d < 8 || a->d > 512 || a->d % 8 != 0) return fail(ATTN_ERR_SHAPE, "d must be a multiple of 8 in [8, 512]");
+  if (a->rows == 0) return ok();
+  if (!a->o_parts || !a->lse_parts || !a->o_out) return fail(ATTN_ERR_NULL, "o_parts, lse_parts and o_out must be non-NULL");
+  if (!aligned16(a->o_parts) || !aligned16(a->o_out) || !aligned4(a->lse_parts) ||
+      (a->lse_out && !aligned4(a->lse_out)))
+    return fail(ATTN_ERR_ALIGN, "o_parts and o_out must be 16-byte aligned, LSE pointers 4-byte aligned");
+  if (a->o_part_stride < 0 || a->o_row_stride < 0 || a->o_part_stride % 4 || a->o_row_stride % 4)
+    return fail(ATTN_ERR_STRIDE, "o_parts strides must be non-negative multiples of 4 elements");
+  if (a->lse_part_stride < 0 || a->lse_row_stride < 0) return fail(ATTN_ERR_STRIDE, "LSE strides must be >= 0");
+  if (!bf16_stride_ok(a->o_out_row_stride)) return fail(ATTN_ERR_STRIDE, "o_out_row_stride must be a non-negative multiple of 8");
+
+  attn::CombineParams c;
+  c.o_parts = a->o_parts;
+  c.lse_parts = a->lse_parts;
+  c.o_out = static_cast<uint16_t *>(a->o_out);
+  c.lse_out = a->lse_out;
+  c.n_parts = a->n_parts;
+  c.rows = a->rows;
+  c.n2 = 1;
+  c.d = a->d;
+  c.o_part_stride = a->o_part_stride;
+  c.o_r1 = a->o_row_stride;
+  c.o_r2 = 0;
+  c.lse_part_stride = a->lse_part_stride;
+  c.lse_r1 = a->lse_row_stride;
+  c.lse_r2 = 0;
+  c.out_r1 = a->o_out_row_stride;
+  c.out_r2 = 0;
+  c.lse_out_r1 = 1;
+  c.lse_out_r2 = 0;
+  hipError_t e = attn::combine(c, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
+}  // extern "C"
+
+namespace attn {
+int prefill_block_rows(int d) { return (d == 64 || d == 128 || d == 256) ? 128 : 0; }
+}  // namespace attn

@@ -1,0 +1,91 @@
+// Shared device-side types and helpers of the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Device-side parameters of the prefill kernel (derived from attn_prefill_args).
+struct PrefillParams {
+  const uint16_t *q, *k, *v;
+  uint16_t *o;
+  float *lse;
+  const float *sinks;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t lse_sb, lse_sh;
+  int32_t b, h_q, h_kv, s_q, s_k;
+  int32_t ratio;     // h_q / h_kv
+  int32_t window;    // 0 = none
+  int32_t n_qtiles;  // ceil(s_q / BM)
+  float c;           // scale * log2(e): logits in base-2 units
+};
+
+// Device-side parameters of the split-KV decode kernel.
+struct DecodeParams {
+  const uint16_t *q, *k, *v;
+  const int64_t *kv_start;
+  const int32_t *kv_len;
+  const float *sinks;
+  float *o_part;    // [B][h_q][n_split][D] fp32, normalised partial outputs
+  float *lse_part;  // [B][h_q][n_split] fp32, natural-log LSE of each part
+  int64_t q_sb, q_sh;
+  int64_t k_st, k_sh;
+  int64_t v_st, v_sh;
+  int32_t B, h_q, h_kv, ratio;
+  int32_t n_split, split;
+  int32_t n_hblk;  // head blocks per kv group: ceil(ratio / BM)
+  float c;
+};
+
+// Device-side parameters of the LSE-merge kernel.  Rows are addressed as
+// (r1, r2) with r2 < n2, so both flat rows (n2 = 1) and [B][h] rows work.
+struct CombineParams {
+  const float *o_parts;
+  const float *lse_parts;
+  uint16_t *o_out;
+  float *lse_out;
+  int32_t n_parts, rows, n2, d;
+  int64_t o_part_stride, o_r1, o_r2;
+  int64_t lse_part_stride, lse_r1, lse_r2;
+  int64_t out_r1, out_r2;
+  int64_t lse_out_r1, lse_out_r2;
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even fp32 -> bf16 of two values packed in one dword
+// (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 32x32x16 bf16 MFMA, fp32 accumulate: D = A(32x16) * B(16x32) + C.
+// Lane l supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32]; the
+// accumulator register i of lane l holds C[8*(i/4) + 4*(l/32) + i%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+}  // namespace attn

@@ -1,0 +1,20 @@
+// Split-KV decode and LSE-merge instantiations.
+#include "combine.hpp"
+#include "decode.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+
+int decode_block_rows(int d) { return (d == 64 || d == 128 || d == 256) ? 128 : 0; }
+
+hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_decode_split<64, 4, 128>(p, s);
+    case 128: return launch_decode_split<128, 4, 64>(p, s);
+    default: return launch_decode_split<256, 4, 32>(p, s);
+  }
+}
+
+hipError_t combine(const CombineParams &p, hipStream_t s) { return launch_combine(p, s); }
+
+}  // namespace attn

@@ -1,0 +1,24 @@
+// Host-visible entry points of the kernel translation units.
+#pragma once
+
+#include "common.hpp"
+
+namespace attn {
+
+// Mask kinds of the prefill kernel.
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskCausalWindow = 2 };
+
+// Query rows per prefill workgroup for head dim d (0 if unsupported).
+int prefill_block_rows(int d);
+// Enqueue the prefill kernel for head dim d; n_units = b * h_q * n_qtiles.
+hipError_t prefill_d64(const PrefillParams &p, int mask, int n_units, hipStream_t s);
+hipError_t prefill_d128(const PrefillParams &p, int mask, int n_units, hipStream_t s);
+hipError_t prefill_d256(const PrefillParams &p, int mask, int n_units, hipStream_t s);
+
+// Query heads per decode workgroup (0 if unsupported).
+int decode_block_rows(int d);
+hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s);
+
+hipError_t combine(const CombineParams &p, hipStream_t s);
+
+}  // namespace attn

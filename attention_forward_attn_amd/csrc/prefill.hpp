@@ -1,0 +1,149 @@
+// Prefill kernel: one workgroup per (batch, query head, tile of BM query rows).
+//
+// Masks follow the planner page's executable step 7: key tiles outside the
+// visible range [kbeg, kend) of the workgroup are never loaded, tiles fully
+// inside every row's visible range skip the element mask, and only tiles that
+// cross a diagonal, a window edge or the end of the keys are masked
+// element by element.  Causal masking is bottom-right aligned (o = s_k - s_q).
+// A sink (status page row D5c) enters as the initial state of the running
+// softmax: max = sigma * log2(e) and sum = 1, with nothing added to O.
+#pragma once
+
+#include "tile.hpp"
+
+namespace attn {
+
+template <int D, int NW, int BN, bool CAUSAL, bool WINDOW>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
+  using T = Tile<D, NW, BN>;
+  constexpr int BM = T::BM;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE_ELEMS];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hi = lane >> 5;
+
+  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
+  // range of work units so that the query tiles sharing one head's K/V run on
+  // the same L2.  Inside a head, the longest (last) query tiles go first.
+  const int n_units = gridDim.x;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = n_units >> 3, rem = n_units & 7;
+  const int unit = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const int bh = unit / p.n_qtiles;
+  const int qt = p.n_qtiles - 1 - (unit - bh * p.n_qtiles);
+  const int bi = bh / p.h_q, h = bh - bi * p.h_q;
+  const int g = h / p.ratio;
+  const int q0 = qt * BM;
+  const int off = p.s_k - p.s_q;
+
+  // Keys visible to any row of this workgroup.
+  const int i_last = min(p.s_q, q0 + BM) - 1;
+  int kend = p.s_k;
+  if (CAUSAL) kend = max(0, min(kend, i_last + off + 1));
+  int kbeg = 0;
+  if (WINDOW) kbeg = max(0, q0 + off - p.window + 1);
+  const int t_begin = kbeg / BN;
+  const int t_end = kbeg < kend ? (kend + BN - 1) / BN : t_begin;
+
+  // This wave's rows.
+  const int w_lo = q0 + w * 32;
+  const int w_hi = min(w_lo + 31, p.s_q - 1);
+  const int row = w_lo + lr;
+  const bool row_ok = row < p.s_q;
+
+  u32x4 qreg[T::NKK];
+  {
+    const uint16_t *qp = p.q + bi * p.q_sb + h * p.q_sh + (int64_t)row * p.q_ss + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < T::NKK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (row_ok) x = *reinterpret_cast<const u32x4 *>(qp + kk * 16);
+      qreg[kk] = x;
+    }
+  }
+
+  float m = kNegInf, l = 0.0f;
+  if (p.sinks != nullptr) {
+    m = p.sinks[h] * kLog2e;
+    l = hi == 0 ? 1.0f : 0.0f;
+  }
+  f32x16 o[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) o[db] = f32x16{};
+
+  const uint16_t *kbase = p.k + bi * p.k_sb + g * p.k_sh;
+  const uint16_t *vbase = p.v + bi * p.v_sb + g * p.v_sh;
+
+  typename T::Stage st;
+  if (t_begin < t_end) {
+    T::load(st, kbase, p.k_ss, vbase, p.v_ss, t_begin * BN, p.s_k, tid);
+    T::store(st, smem, smem + BN * D, tid);
+  }
+  __syncthreads();
+
+  int cur = 0;
+  for (int t = t_begin; t < t_end; ++t) {
+    const bool more = t + 1 < t_end;
+    if (more) T::load(st, kbase, p.k_ss, vbase, p.v_ss, (t + 1) * BN, p.s_k, tid);
+
+    const int j0 = t * BN;
+    const uint16_t *lk = smem + cur * T::STAGE_ELEMS;
+    const uint16_t *lv = lk + BN * D;
+    bool active = w_lo < p.s_q;
+    if (CAUSAL) active = active && j0 <= w_hi + off;
+    if (WINDOW) active = active && j0 + BN - 1 >= w_lo + off - p.window + 1;
+    if (active) {
+      f32x16 s[T::NKB];
+      T::scores(s, qreg, lk, lr, hi);
+      bool need_mask = j0 + BN > p.s_k;
+      if (CAUSAL) need_mask = need_mask || (j0 + BN - 1 > w_lo + off);
+      if (WINDOW) need_mask = need_mask || (j0 < w_hi + off - p.window + 1);
+      if (need_mask) {
+        const int lim_hi = CAUSAL ? row + off : 0x7fffffff;
+        const int lim_lo = WINDOW ? row + off - p.window + 1 : -0x7fffffff;
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + T::key_of(kb, i, hi);
+            const bool vis = j < p.s_k && j <= lim_hi && j >= lim_lo;
+            if (!vis) s[kb][i] = kNegInf;
+          }
+      }
+      u32x4 pk[T::NPV];
+      T::softmax_step(s, pk, o, m, l, p.c);
+      T::values(o, pk, lv, lr, hi);
+    }
+    if (more) T::store(st, smem + (cur ^ 1) * T::STAGE_ELEMS, smem + (cur ^ 1) * T::STAGE_ELEMS + BN * D, tid);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // Epilogue: O / l once, bf16 round-to-nearest-even; LSE = ln2 * (m + log2 l).
+  const float lt = l + xor32(l);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (row_ok) {
+    uint16_t *op = p.o + bi * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        u32x2 val;
+        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
+        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
+        *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
+      }
+    if (p.lse != nullptr && hi == 0)
+      p.lse[bi * p.lse_sb + h * p.lse_sh + row] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  }
+}
+
+// Host-side launcher of one instantiation.
+template <int D, int NW, int BN, bool CAUSAL, bool WINDOW>
+hipError_t launch_prefill(const PrefillParams &p, int n_units, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_kernel<D, NW, BN, CAUSAL, WINDOW>), dim3(n_units), dim3(NW * 64), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace attn

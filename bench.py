@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the prefill kernel on the dense MHA causal workload (b=2, h=16, s_q=s_k=4096,
+d=128, bottom-right causal, O + LSE) followed by the split-KV decode of the
+MQA decode workload (B=64 sequences, one query token, h_q=128, h_kv=1, d=128,
+KV lengths uniform in [1024, 8192], chunks of 512, then the LSE merge).
+Inputs are resident in HBM before the timed region; prefill inputs rotate over
+2 sets and decode inputs over 4 sets (about 620 MB) so that repeated steps do
+not read K/V out of the 256 MB last-level cache.
+
+`value` is the prefill throughput in TFLOP/s counted as 4*d per visible
+(query, key) pair (causal-adjusted); the decode throughput in GB/s (algorithmic
+bytes: K and V of every cached token plus Q, O and LSE) is reported beside it.
+Kernel times come from HIP events recorded on the stream the kernels run on.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+HEADLINE_PREFILL = "mha_b2_h16_s4096_d128_causal"
+HEADLINE_DECODE = "mqa_decode_B64_hq128_d128"
+
+
+def visible_pairs(s_q: int, s_k: int, causal: bool, window: int) -> int:
+    """Number of (query row, key) pairs the mask keeps (closed form per row)."""
+    off = s_k - s_q
+    total = 0
+    for i in range(s_q):
+        hi = s_k - 1 if not causal else min(s_k - 1, i + off)
+        lo = 0 if window <= 0 else max(0, i + off - window + 1)
+        if hi >= lo:
+            total += hi - lo + 1
+    return total
+
+
+def prefill_flops(w) -> int:
+    return 4 * w.d * w.b * w.h_q * visible_pairs(w.s_q, w.s_k, w.causal, w.window)
+
+
+def decode_bytes(w, total_tokens: int) -> int:
+    kv = total_tokens * w.h_kv * w.d * 2 * 2
+    qo = 2 * w.b * w.h_q * w.d * 2
+    return kv + qo + w.b * w.h_q * 4
+
+
+class PrefillCase:
+    def __init__(self, w, n_sets: int, dev):
+        import torch
+
+        from attention_forward_attn_amd.inputs import prefill_inputs
+
+        self.w = w
+        self.scale = 1.0 / math.sqrt(w.d)
+        self.sets = []
+        for i in range(n_sets):
+            inp = prefill_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed + 7919 * i, w.sinks)
+            self.sets.append({k: (v.to(dev) if v is not None else None) for k, v in inp.items()})
+        self.out = torch.empty((w.b, w.h_q, w.s_q, w.d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.b, w.h_q, w.s_q), dtype=torch.float32, device=dev)
+        self.flops = prefill_flops(w)
+
+    def run(self, i: int):
+        import attention_forward_attn_amd as afa
+
+        s = self.sets[i % len(self.sets)]
+        afa.prefill(s["q"], s["k"], s["v"], scale=self.scale, causal=self.w.causal,
+                    window=self.w.window, sinks=s["sinks"], out=self.out, lse=self.lse)
+
+
+class DecodeCase:
+    def __init__(self, w, n_sets: int, dev):
+        import torch
+
+        import attention_forward_attn_amd as afa
+        from attention_forward_attn_amd.inputs import decode_inputs
+
+        self.w = w
+        base = decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed, w.sinks)
+        self.total = int(base["kv_len"].sum())
+        self.max_len = int(base["kv_len"].max())
+        self.kv_start = base["kv_start"].to(dev)
+        self.kv_len = base["kv_len"].to(dev)
+        self.sets = [{"q": base["q"].to(dev), "k": base["k"].to(dev), "v": base["v"].to(dev)}]
+        gen = torch.Generator(device=dev).manual_seed(w.seed + 1)
+        for _ in range(1, n_sets):  # more sets of the same shapes, drawn on the device
+            self.sets.append({n: torch.randn(t.shape, generator=gen, device=dev).to(torch.bfloat16)
+                              for n, t in self.sets[0].items()})
+        self.sinks = base["sinks"].to(dev) if base["sinks"] is not None else None
+        self.scale = 1.0 / math.sqrt(w.d)
+        self.ws = torch.empty(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
+                              dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.b, w.h_q, w.d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.b, w.h_q), dtype=torch.float32, device=dev)
+        self.bytes = decode_bytes(w, self.total)
+
+    def run(self, i: int):
+        import attention_forward_attn_amd as afa
+
+        s = self.sets[i % len(self.sets)]
+        afa.decode(s["q"], s["k"], s["v"], self.kv_start, self.kv_len, self.max_len,
+                   scale=self.scale, sinks=self.sinks, split_size=self.w.split, workspace=self.ws,
+                   out=self.out, lse=self.lse)
+
+
+def cpu_baseline_prefill(w, budget_s: float = 12.0):
+    """Time the fp64 oracle on whole heads of the same workload until the budget is spent."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from attention_forward_attn_amd.inputs import prefill_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = os.cpu_count() or 1
+    inp = prefill_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed, w.sinks)
+    q = inp["q"].to(torch.float64).numpy()
+    k = inp["k"].to(torch.float64).numpy()
+    v = inp["v"].to(torch.float64).numpy()
+    sig = inp["sinks"].to(torch.float64).numpy() if inp["sinks"] is not None else None
+    ratio = w.h_q // w.h_kv
+    done = 0
+    t0 = time.perf_counter()
+    for bi in range(w.b):
+        for h in range(w.h_q):
+            g = h // ratio
+            oracle.attention_ref(q[bi:bi + 1, h:h + 1], k[bi:bi + 1, g:g + 1], v[bi:bi + 1, g:g + 1],
+                                 1.0 / math.sqrt(w.d), causal=w.causal, window=w.window,
+                                 sinks=None if sig is None else sig[h:h + 1])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4 * w.d * done * visible_pairs(w.s_q, w.s_k, w.causal, w.window)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {w.b * w.h_q} (batch, head) slices of {w.name}, fp64 numpy, "
+                      f"{dt:.1f} s"}
+
+
+def timed(cases, steps: int, warmup: int):
+    """Run warmup + steps; return (per-case mean ms, wall ms per step)."""
+    import torch
+
+    for i in range(warmup):
+        for c in cases:
+            c.run(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(cases) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record()
+        for j, c in enumerate(cases):
+            c.run(warmup + i)
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
+           for j in range(len(cases))]
+    return per, wall_ms
+
+
+def roofline_prefill(flops: int, ms: float):
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+
+def roofline_decode(nbytes: int, ms: float):
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+
+
+def bench_one(name: str, steps: int, warmup: int, dev):
+    """One JSON line for one named workload (prefill or decode) alone."""
+    from attention_forward_attn_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[name]
+    if w.kind == "prefill":
+        c = PrefillCase(w, 2, dev)
+        (ms,), wall = timed([c], steps, warmup)
+        r = roofline_prefill(c.flops, ms)
+        return {"workload": name, "kind": "prefill", "ms": round(ms, 4), "TFLOP/s": r["achieved"],
+                "frac_of_peak": r["frac"], "gflop": round(c.flops / 1e9, 2)}
+    c = DecodeCase(w, 4 if w.d <= 128 else 2, dev)
+    (ms,), wall = timed([c], steps, warmup)
+    r = roofline_decode(c.bytes, ms)
+    return {"workload": name, "kind": "decode", "ms": round(ms, 4), "GB/s": r["achieved"],
+            "frac_of_peak": r["frac"], "MB": round(c.bytes / 1e6, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="bench one named workload alone")
+    ap.add_argument("--all", action="store_true", help="one line per workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_forward_attn_amd as afa
+    from attention_forward_attn_amd.inputs import WORKLOADS
+
+    afa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.workload or args.all:
+        names = [args.workload] if args.workload else [
+            n for n, w in WORKLOADS.items() if not (w.kind == "prefill" and w.d > 256)]
+        for n in names:
+            print(json.dumps(bench_one(n, args.steps, args.warmup, dev)), flush=True)
+        return
+
+    wp = WORKLOADS[HEADLINE_PREFILL]
+    wd = WORKLOADS[HEADLINE_DECODE]
+    pc = PrefillCase(wp, 2, dev)
+    dc = DecodeCase(wd, 4, dev)
+    (pre_ms, dec_ms), wall_ms = timed([pc, dc], args.steps, args.warmup)
+    pre = roofline_prefill(pc.flops, pre_ms)
+    dec = roofline_decode(dc.bytes, dec_ms)
+    line = {
+        "metric": "attn fwd TFLOPS (bf16, causal-adjusted) + decode HBM GB/s, 1xMI355X",
+        "value": pre["achieved"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre_ms + dec_ms, 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) bf16, seeded",
+        "config": {"workload": HEADLINE_PREFILL, "b": wp.b, "h_q": wp.h_q, "h_kv": wp.h_kv,
+                   "s_q": wp.s_q, "s_k": wp.s_k, "d": wp.d, "causal": wp.causal,
+                   "decode_workload": HEADLINE_DECODE, "decode_B": wd.b, "decode_h_q": wd.h_q,
+                   "decode_h_kv": wd.h_kv, "decode_d": wd.d, "decode_split": wd.split,
+                   "decode_tokens": dc.total},
+        "prefill_ms": round(pre_ms, 4),
+        "roofline": pre,
+        "decode": {"value": dec["achieved"], "unit": "GB/s", "ms": round(dec_ms, 4),
+                   "bytes": dc.bytes, "roofline": dec},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(wp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

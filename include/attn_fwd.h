@@ -1,0 +1,198 @@
+/*
+ * attn_fwd.h -- C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * One operation, in two launch shapes plus a merge:
+ *
+ *   O = softmax(scale * Q K^T + mask) V,   LSE = ln(sum over visible keys of exp(logit))
+ *
+ * computed with a streaming (online) softmax: per query row a running max,
+ * a running sum and an O accumulator that is rescaled whenever the max grows,
+ * and divided by the sum only at the very end.  That state machine is the
+ * one the FA4 planner page ("b200-flash-attention4-planner", section A1
+ * "Streaming online softmax" and executable steps 1-8) lays out; the masks,
+ * sink and per-row LSE are rows D3, D4, D5b and D5c of the DSV4 status page
+ * ("archived_plans/2026-05-28_STATUS.md"); the merge of partial results by
+ * their LSE is the workaround paragraph "O rescale (kt>0)" of the STAGE_D.md
+ * page (nvfp4-megamoe-kernel).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    keeps no pointer after a call returns, allocates no device memory and
+ *    never synchronises the host: work is enqueued on `stream` (a hipStream_t
+ *    passed as void*; NULL means the default stream) and runs asynchronously.
+ *  - bf16 tensors hold IEEE bfloat16 bit patterns (uint16).  Strides are in
+ *    ELEMENTS, int64, and the head-dim stride is always 1.
+ *  - Arguments are validated on the host before any HIP call.  A non-zero
+ *    status means nothing was enqueued; attn_last_error() then returns a
+ *    thread-local message naming the offending argument.  ATTN_ERR_HIP means a
+ *    launch was rejected by the runtime.  Faults inside a running kernel are
+ *    reported by the stream, not by these calls.  No C++ exception crosses
+ *    the ABI.
+ *  - Alignment: every bf16 base pointer and every bf16 sequence/head/batch
+ *    stride must be a multiple of 16 bytes (8 elements); fp32 pointers must be
+ *    4-byte aligned.
+ *  - Reentrancy: there is no global mutable state besides the thread-local
+ *    error text, so calls from several host threads are safe as long as they
+ *    do not write the same output buffers.
+ *  - Every output row is written, including rows that see no key.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_FWD_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  ATTN_ERR_STRIDE = 3,      /* a stride is negative or not a multiple of 8 elements */
+  ATTN_ERR_ALIGN = 4,       /* a base pointer is misaligned */
+  ATTN_ERR_UNSUPPORTED = 5, /* a valid request this build has no kernel for */
+  ATTN_ERR_WORKSPACE = 6,   /* decode workspace missing or too small */
+  ATTN_ERR_HIP = 7          /* the HIP runtime rejected a launch */
+} attn_status;
+
+/*
+ * Prefill: one fused forward pass over [b, h_q, s_q] query rows.
+ *
+ * Element (bi, hi, si, t) of q lives at q + bi*q_sb + hi*q_sh + si*q_ss + t,
+ * and likewise for k, v (with h_kv heads and s_k rows) and o (h_q heads, s_q
+ * rows).  A [b, h, s, d] contiguous tensor has sb = h*s*d, sh = s*d, ss = d;
+ * a [b, s, h, d] one has sb = s*h*d, sh = d, ss = h*d.  MQA may be expressed
+ * either as h_kv = 1 or as h_kv = h_q with k_sh = v_sh = 0.
+ *
+ * Semantics (planner page, executable steps 1, 2 and 7; status page D2-D5c):
+ *  - query head h reads kv head h / (h_q / h_kv): contiguous GQA groups;
+ *  - logit(i, j) = scale * sum_t q[i, t] k[j, t]; scale must be finite and > 0;
+ *  - causal = 1 masks with bottom-right alignment: key j is visible to row i
+ *    iff j <= i + (s_k - s_q);
+ *  - window = W > 0 (only together with causal) also requires
+ *    j >= i + (s_k - s_q) - W + 1, i.e. W keys including the diagonal;
+ *  - sinks, if not NULL, holds h_q fp32 logits: each acts as one extra
+ *    softmax column with zero value, its logit taken as is (not scaled);
+ *  - lse, if not NULL, receives the natural-log log-sum-exp of each row's
+ *    scaled logits (sink included) at lse + bi*lse_sb + hi*lse_sh + si;
+ *  - a row that sees no key and has no sink gets O = 0 and LSE = -inf.
+ *
+ * Supported: d in {64, 128, 256, 512}; b, h_q, h_kv >= 1; s_q, s_k >= 0
+ * (s_q = 0 is a no-op); every index must fit in 31 bits.
+ */
+typedef struct {
+  const void *q;      /* bf16 */
+  const void *k;      /* bf16 */
+  const void *v;      /* bf16 */
+  void *o;            /* bf16 output */
+  float *lse;         /* fp32 output [b, h_q, s_q] via lse_sb, lse_sh; NULL = not wanted */
+  const float *sinks; /* fp32 [h_q]; NULL = no sink */
+  int32_t b, h_q, h_kv, s_q, s_k, d;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t lse_sb, lse_sh;
+  float scale;
+  int32_t causal; /* 0 or 1 */
+  int32_t window; /* 0 = none; W > 0 requires causal */
+} attn_prefill_args;
+
+/*
+ * Decode: one query token per sequence against a KV cache that is contiguous
+ * per sequence (the MQA/GQA decode of status-page row D2, with the multi-tile
+ * key range handled by split-KV plus the LSE merge of the STAGE_D.md page).
+ *
+ * q: bf16, element (bi, hi, t) at q + bi*q_sb + hi*q_sh + t.
+ * k, v: bf16; token tok of sequence bi, kv head g is at
+ *       k + (kv_start[bi] + tok)*k_st + g*k_sh (v: v_st, v_sh); head strides
+ *       may be 0 (MQA).
+ * kv_start: DEVICE int64 [B]; kv_len: DEVICE int32 [B], each in [0, max_kv_len].
+ * max_kv_len: host-side upper bound on every kv_len; it sizes the grid and the
+ *       workspace, so no device-to-host copy is needed.
+ * o: bf16 output (bi, hi, t) at o + bi*o_sb + hi*o_sh + t;
+ * lse: fp32 output at lse + bi*lse_sb + hi (NULL = not wanted); sinks as in
+ *       prefill.
+ * split_size: keys per split (a multiple of 64, >= 64).  Split c of sequence
+ *       bi covers keys [c*split_size, min((c+1)*split_size, kv_len[bi])).
+ *
+ * Two kernels run on `stream`: the split kernel writes normalised fp32
+ * partial outputs and their LSE into the workspace, then the combine kernel
+ * merges them into o and lse.  Supported: d in {64, 128, 256}; B, h_q, h_kv
+ * >= 1, h_q % h_kv == 0.
+ */
+typedef struct {
+  const void *q;
+  const void *k;
+  const void *v;
+  const int64_t *kv_start;
+  const int32_t *kv_len;
+  void *o;
+  float *lse;
+  const float *sinks;
+  int32_t B, h_q, h_kv, d;
+  int32_t max_kv_len;
+  int32_t split_size;
+  int64_t q_sb, q_sh;
+  int64_t k_st, k_sh;
+  int64_t v_st, v_sh;
+  int64_t o_sb, o_sh;
+  int64_t lse_sb;
+  float scale;
+} attn_decode_args;
+
+/*
+ * Merge n_parts partial attention results computed over DISJOINT key sets
+ * (STAGE_D.md page, "O rescale (kt>0)" workaround): per row, with
+ * M = max_p lse_p and w_p = exp(lse_p - M),
+ *     O = sum_p w_p O_p / sum_p w_p,   LSE = M + ln sum_p w_p.
+ * A part with lse = -inf has zero weight and its O is not read; a row whose
+ * parts are all -inf gets O = 0, LSE = -inf.  It must not be used to merge
+ * partial dot products over the same keys (head-dim sub-tiles add in logit
+ * space; STAGE_D.md page, section 2).
+ *
+ * o_parts: fp32, element (p, r, t) at o_parts + p*o_part_stride + r*o_row_stride + t;
+ * lse_parts: fp32 (p, r) at lse_parts + p*lse_part_stride + r*lse_row_stride;
+ * o_out: bf16 (r, t) at o_out + r*o_out_row_stride + t;
+ * lse_out: fp32 at lse_out + r (NULL = not wanted).
+ * Supported: n_parts in [1, 1024], rows >= 0, d a multiple of 8 in [8, 512];
+ * fp32 strides non-negative multiples of 4 elements, bf16 row stride a
+ * multiple of 8 elements.
+ */
+typedef struct {
+  const float *o_parts;
+  const float *lse_parts;
+  void *o_out;
+  float *lse_out;
+  int32_t n_parts, rows, d;
+  int64_t o_part_stride, o_row_stride;
+  int64_t lse_part_stride, lse_row_stride;
+  int64_t o_out_row_stride;
+} attn_combine_args;
+
+/* Bytes of device workspace attn_fwd_decode needs for these sizes (0 on invalid sizes). */
+size_t attn_fwd_decode_workspace_size(int32_t B, int32_t h_q, int32_t d, int32_t max_kv_len,
+                                      int32_t split_size);
+
+attn_status attn_fwd_prefill(const attn_prefill_args *args, void *stream);
+attn_status attn_fwd_decode(const attn_decode_args *args, void *workspace, size_t workspace_bytes,
+                            void *stream);
+attn_status attn_combine(const attn_combine_args *args, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *attn_status_str(attn_status s);
+/* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
+const char *attn_last_error(void);
+/* ATTN_FWD_ABI_VERSION of the built library. */
+int32_t attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

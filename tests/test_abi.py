@@ -1,0 +1,206 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any HIP call.
+
+Every call here is invalid on purpose (so no kernel is ever launched): the
+pointers are fake, non-NULL integers.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_forward_attn_amd as afa
+from attention_forward_attn_amd._binding import CombineArgs, DecodeArgs, PrefillArgs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("attn_fwd_prefill", "attn_fwd_decode", "attn_combine",
+                 "attn_fwd_decode_workspace_size", "attn_status_str", "attn_last_error",
+                 "attn_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = afa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
+    assert lib.attn_abi_version() == 1
+
+
+def test_status_strings():
+    lib = afa.load_library()
+    for code, name in enumerate(["ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_STRIDE",
+                                 "ATTN_ERR_ALIGN", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE",
+                                 "ATTN_ERR_HIP"]):
+        assert lib.attn_status_str(code).decode() == name
+
+
+def good_prefill(**over):
+    a = PrefillArgs()
+    a.q = a.k = a.v = a.o = FAKE
+    a.lse = None
+    a.sinks = None
+    a.b, a.h_q, a.h_kv, a.s_q, a.s_k, a.d = 1, 2, 1, 64, 64, 128
+    a.q_sb, a.q_sh, a.q_ss = 2 * 64 * 128, 64 * 128, 128
+    a.k_sb, a.k_sh, a.k_ss = 64 * 128, 64 * 128, 128
+    a.v_sb, a.v_sh, a.v_ss = 64 * 128, 64 * 128, 128
+    a.o_sb, a.o_sh, a.o_ss = 2 * 64 * 128, 64 * 128, 128
+    a.scale = 0.088
+    a.causal = 0
+    a.window = 0
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+PREFILL_BAD = [
+    ("null q", dict(q=None), 1),
+    ("null o", dict(o=None), 1),
+    ("d=96", dict(d=96), 2),
+    ("d=0", dict(d=0), 2),
+    ("b=0", dict(b=0), 2),
+    ("h_kv=0", dict(h_kv=0), 2),
+    ("ratio not integral", dict(h_q=3, h_kv=2), 2),
+    ("negative s_k", dict(s_k=-1), 2),
+    ("zero scale", dict(scale=0.0), 2),
+    ("negative scale", dict(scale=-1.0), 2),
+    ("nan scale", dict(scale=float("nan")), 2),
+    ("window without causal", dict(window=16), 2),
+    ("negative window", dict(causal=1, window=-1), 2),
+    ("causal=2", dict(causal=2), 2),
+    ("odd seq stride", dict(q_ss=130), 3),
+    ("negative stride", dict(k_sh=-8), 3),
+    ("misaligned q", dict(q=FAKE + 2), 4),
+    ("misaligned v", dict(v=FAKE + 8), 4),
+    ("misaligned lse", dict(lse=FAKE + 2), 4),
+    ("d=512 not built", dict(d=512, q_ss=512, k_ss=512, v_ss=512, o_ss=512), 5),
+]
+
+
+@pytest.mark.parametrize("name,over,code", PREFILL_BAD, ids=[c[0] for c in PREFILL_BAD])
+def test_prefill_rejects(name, over, code):
+    lib = afa.load_library()
+    a = good_prefill(**over)
+    st = lib.attn_fwd_prefill(ctypes.byref(a), None)
+    assert st == code, (st, lib.attn_last_error())
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_prefill_null_args():
+    lib = afa.load_library()
+    assert lib.attn_fwd_prefill(None, None) == 1
+
+
+def test_prefill_empty_query_is_noop():
+    # s_q = 0 is valid and returns before any HIP call
+    lib = afa.load_library()
+    a = good_prefill(s_q=0)
+    assert lib.attn_fwd_prefill(ctypes.byref(a), None) == 0
+
+
+def good_decode(**over):
+    a = DecodeArgs()
+    a.q = a.k = a.v = a.o = FAKE
+    a.kv_start = a.kv_len = FAKE
+    a.lse = None
+    a.sinks = None
+    a.B, a.h_q, a.h_kv, a.d = 4, 128, 1, 128
+    a.max_kv_len, a.split_size = 8192, 512
+    a.q_sb, a.q_sh = 128 * 128, 128
+    a.k_st, a.k_sh, a.v_st, a.v_sh = 128, 0, 128, 0
+    a.o_sb, a.o_sh = 128 * 128, 128
+    a.lse_sb = 128
+    a.scale = 0.088
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+DECODE_BAD = [
+    ("null kv_len", dict(kv_len=None), 1),
+    ("null q", dict(q=None), 1),
+    ("d=512", dict(d=512), 2),
+    ("ratio", dict(h_q=6, h_kv=4), 2),
+    ("split 100", dict(split_size=100), 2),
+    ("split 0", dict(split_size=0), 2),
+    ("negative max len", dict(max_kv_len=-1), 2),
+    ("zero scale", dict(scale=0.0), 2),
+    ("odd token stride", dict(k_st=12), 3),
+    ("misaligned k", dict(k=FAKE + 4), 4),
+    ("misaligned kv_start", dict(kv_start=FAKE + 4), 4),
+]
+
+
+@pytest.mark.parametrize("name,over,code", DECODE_BAD, ids=[c[0] for c in DECODE_BAD])
+def test_decode_rejects(name, over, code):
+    lib = afa.load_library()
+    a = good_decode(**over)
+    st = lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert st == code, (st, lib.attn_last_error())
+
+
+def test_decode_workspace_checks():
+    lib = afa.load_library()
+    a = good_decode()
+    need = lib.attn_fwd_decode_workspace_size(4, 128, 128, 8192, 512)
+    # 4 sequences x 128 heads x 16 splits x (128 fp32 outputs + 1 fp32 LSE)
+    assert need >= 4 * 128 * 16 * (128 + 1) * 4
+    assert lib.attn_fwd_decode(ctypes.byref(a), None, need, None) == 6
+    assert lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
+    assert lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4
+    assert lib.attn_fwd_decode_workspace_size(0, 128, 128, 8192, 512) == 0
+    assert lib.attn_fwd_decode_workspace_size(4, 128, 128, 8192, 100) == 0
+
+
+def good_combine(**over):
+    a = CombineArgs()
+    a.o_parts = a.lse_parts = a.o_out = FAKE
+    a.lse_out = None
+    a.n_parts, a.rows, a.d = 4, 16, 128
+    a.o_part_stride, a.o_row_stride = 16 * 128, 128
+    a.lse_part_stride, a.lse_row_stride = 16, 1
+    a.o_out_row_stride = 128
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+COMBINE_BAD = [
+    ("null parts", dict(o_parts=None), 1),
+    ("zero parts", dict(n_parts=0), 2),
+    ("too many parts", dict(n_parts=5000), 2),
+    ("d=12", dict(d=12), 2),
+    ("d=1024", dict(d=1024), 2),
+    ("part stride", dict(o_part_stride=6), 3),
+    ("out stride", dict(o_out_row_stride=12), 3),
+    ("misaligned out", dict(o_out=FAKE + 2), 4),
+]
+
+
+@pytest.mark.parametrize("name,over,code", COMBINE_BAD, ids=[c[0] for c in COMBINE_BAD])
+def test_combine_rejects(name, over, code):
+    lib = afa.load_library()
+    a = good_combine(**over)
+    assert lib.attn_combine(ctypes.byref(a), None) == code, lib.attn_last_error()
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        afa.prefill(q, q, q)

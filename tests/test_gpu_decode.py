@@ -1,0 +1,112 @@
+"""GPU parity of split-KV decode and of the LSE-merge kernel against the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_forward_attn_amd as afa
+import oracle
+from attention_forward_attn_amd.inputs import WORKLOADS, decode_inputs
+from parity_util import check
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def run_decode(inp, max_len, split=512, sinks=None, d=None):
+    q, k, v = inp["q"].to(DEV), inp["k"].to(DEV), inp["v"].to(DEV)
+    ks, kl = inp["kv_start"].to(DEV), inp["kv_len"].to(DEV)
+    d = q.shape[-1]
+    ws = torch.full((afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split),),
+                    255, dtype=torch.uint8, device=DEV)  # NaN-poisoned partials
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+    sd = None if sinks is None else sinks.to(DEV)
+    afa.decode(q, k, v, ks, kl, max_len, sinks=sd, split_size=split, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def make(B, h_q, h_kv, d, lens, seed):
+    gen = torch.Generator("cpu").manual_seed(seed)
+    lens_t = torch.tensor(lens, dtype=torch.int64)
+    starts = torch.zeros(B, dtype=torch.int64)
+    starts[1:] = torch.cumsum(lens_t, 0)[:-1]
+    T = int(lens_t.sum()) + 5
+    q = torch.randn(B, h_q, d, generator=gen).to(torch.bfloat16)
+    k = torch.randn(T, h_kv, d, generator=gen).to(torch.bfloat16)
+    v = torch.randn(T, h_kv, d, generator=gen).to(torch.bfloat16)
+    return {"q": q, "k": k, "v": v, "kv_start": starts, "kv_len": lens_t.to(torch.int32)}
+
+
+SMALL = [
+    # B, h_q, h_kv, d, lens, split
+    (4, 128, 1, 128, [1, 511, 512, 513], 512),
+    (3, 128, 1, 256, [1000, 64, 1537], 512),
+    (5, 16, 4, 64, [1, 2, 63, 64, 700], 128),
+    (2, 8, 8, 128, [300, 5], 64),
+    (2, 256, 2, 128, [129, 1030], 256),  # 128 query heads per kv head, two kv heads
+    (3, 6, 2, 128, [17, 0, 90], 64),     # an empty sequence
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_decode_small(case, with_sink):
+    B, h_q, h_kv, d, lens, split = case
+    print(f"decode case {case} sink={with_sink}", flush=True)
+    inp = make(B, h_q, h_kv, d, lens, 21)
+    sinks = torch.randn(h_q, generator=torch.Generator().manual_seed(3)) if with_sink else None
+    out, lse = run_decode(inp, max(max(lens), 1), split, sinks)
+    o_ref, l_ref = oracle.decode_ref(inp["q"], inp["k"], inp["v"], inp["kv_start"], inp["kv_len"],
+                                     1 / math.sqrt(d), sinks=sinks)
+    check(out, lse, o_ref, l_ref, str(case))
+
+
+def test_decode_head_stride_zero_matches_mqa():
+    inp = make(3, 16, 1, 128, [100, 700, 1], 22)
+    out1, lse1 = run_decode(inp, 700, 128)
+    # the same cache seen as 16 kv heads with head stride 0
+    k = inp["k"].to(DEV).expand(-1, 16, -1)
+    v = inp["v"].to(DEV).expand(-1, 16, -1)
+    out2, lse2 = afa.decode(inp["q"].to(DEV), k, v, inp["kv_start"].to(DEV), inp["kv_len"].to(DEV),
+                            700, split_size=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_decode_split_size_invariance():
+    inp = make(4, 128, 1, 128, [1500, 3000, 64, 2049], 23)
+    o1, l1 = run_decode(inp, 3000, 512)
+    o2, l2 = run_decode(inp, 3000, 4096)  # a single split per sequence
+    assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
+    assert (l1 - l2).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.kind == "decode"])
+def test_decode_full_size(name):
+    w = WORKLOADS[name]
+    print(f"full-size decode {name}", flush=True)
+    inp = decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed)
+    out, lse = run_decode(inp, w.len_hi, w.split)
+    o_ref, l_ref = oracle.decode_ref(inp["q"], inp["k"], inp["v"], inp["kv_start"], inp["kv_len"],
+                                     1 / math.sqrt(w.d))
+    check(out, lse, o_ref, l_ref, name)
+
+
+@pytest.mark.parametrize("n,rows,d", [(1, 5, 64), (7, 33, 128), (16, 100, 256), (3, 10, 512)])
+def test_combine_matches_merge(n, rows, d):
+    gen = torch.Generator().manual_seed(n * 100 + rows)
+    o_parts = torch.randn(n, rows, d, generator=gen)
+    lse_parts = torch.randn(n, rows, generator=gen) * 3
+    lse_parts[0, 0] = float("-inf")          # one empty part
+    if rows > 2:
+        lse_parts[:, 1] = float("-inf")      # one empty row
+        o_parts[:, 1] = float("nan")         # never read
+    out, lse = afa.combine(o_parts.to(DEV), lse_parts.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.merge_ref(np.nan_to_num(o_parts.double().numpy()), lse_parts.double().numpy())
+    check(out, lse, o_ref, l_ref, "combine")

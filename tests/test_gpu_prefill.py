@@ -1,0 +1,177 @@
+"""GPU parity of the prefill kernel against the fp64 oracle (through the C ABI).
+
+Small problems are compared element by element over every output; they span
+several query and key tiles and end in ragged tails.  The full-size workloads
+run in the launch configuration the bench times and are compared on sampled
+rows (first, last, tile edges, random), which the oracle computes one by one.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_forward_attn_amd as afa
+import oracle
+from attention_forward_attn_amd.inputs import WORKLOADS, prefill_inputs
+from parity_util import check, oracle_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def run_case(b, h_q, h_kv, s_q, s_k, d, causal=False, window=0, sink=False, seed=7, scale=None,
+             layout="bhsd", q_mul=1.0):
+    inp = prefill_inputs(b, h_q, h_kv, s_q, s_k, d, seed, with_sinks=sink)
+    q, k, v, sinks = inp["q"], inp["k"], inp["v"], inp["sinks"]
+    if q_mul != 1.0:
+        q = (q.float() * q_mul).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if layout == "bshd":  # strided views of [b, s, h, d] storage
+        qd = q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+        kd = k.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+        vd = v.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    else:
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    sd = sinks.to(DEV) if sinks is not None else None
+    out = torch.full((b, h_q, s_q, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((b, h_q, s_q), float("nan"), dtype=torch.float32, device=DEV)
+    afa.prefill(qd, kd, vd, scale=scale, causal=causal, window=window, sinks=sd, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_ref(q, k, v, scale, causal=causal, window=window, sinks=sinks)
+    return out, lse, o_ref, l_ref
+
+
+SMALL = [
+    # b, h_q, h_kv, s_q, s_k, d, causal, window, sink
+    (1, 1, 1, 256, 256, 64, False, 0, False),   # the tiny single-head workload shape
+    (1, 2, 2, 300, 300, 64, True, 0, False),
+    (2, 4, 2, 257, 513, 128, False, 0, False),
+    (1, 4, 4, 513, 257, 128, True, 0, False),   # s_q > s_k: leading empty rows
+    (1, 4, 1, 384, 384, 128, True, 100, True),  # MQA + window + sink
+    (2, 8, 2, 200, 777, 128, True, 64, False),
+    (1, 2, 2, 129, 129, 256, False, 0, True),
+    (1, 4, 2, 300, 300, 256, True, 0, False),
+    (1, 2, 1, 1, 1000, 128, True, 0, False),    # one query row
+    (1, 2, 1, 1000, 1, 64, False, 0, False),    # one key
+    (1, 2, 2, 1, 1, 128, False, 0, False),
+    (1, 4, 4, 65, 65, 64, True, 1, False),      # window of one key: O = V on the diagonal
+    (1, 32, 1, 130, 130, 128, True, 0, True),   # GQA ratio 32
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
+def test_prefill_small(case):
+    b, h_q, h_kv, s_q, s_k, d, causal, window, sink = case
+    print(f"prefill case {case}", flush=True)
+    out, lse, o_ref, l_ref = run_case(b, h_q, h_kv, s_q, s_k, d, causal, window, sink)
+    check(out, lse, o_ref, l_ref, str(case))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_prefill_strided_bshd(d):
+    out, lse, o_ref, l_ref = run_case(2, 4, 2, 200, 200, d, causal=True, layout="bshd")
+    check(out, lse, o_ref, l_ref, "bshd")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_prefill_extreme_logits(d):
+    # Q x 30: near one-hot attention rows stress the running-max rescale
+    out, lse, o_ref, l_ref = run_case(1, 2, 2, 200, 333, d, causal=True, q_mul=30.0)
+    check(out, lse, o_ref, l_ref, "extreme")
+
+
+@pytest.mark.parametrize("sig", [-1e4, 0.0, 20.0])
+def test_prefill_sink_values(sig):
+    inp = prefill_inputs(1, 4, 2, 150, 150, 128, 9)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    sinks = torch.full((4,), sig, dtype=torch.float32)
+    out, lse = afa.prefill(q, k, v, causal=True, sinks=sinks.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_ref(inp["q"], inp["k"], inp["v"], 1 / math.sqrt(128),
+                                        causal=True, sinks=sinks)
+    check(out, lse, o_ref, l_ref, f"sink {sig}")
+
+
+def test_gqa_matches_repeated_heads_bitwise():
+    inp = prefill_inputs(1, 8, 2, 190, 190, 128, 11)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o1, l1 = afa.prefill(q, k, v, causal=True)
+    kr = k.repeat_interleave(4, dim=1).contiguous()
+    vr = v.repeat_interleave(4, dim=1).contiguous()
+    o2, l2 = afa.prefill(q, kr, vr, causal=True)
+    # MQA through head stride 0: h_kv = h_q with a broadcast view
+    o3, l3 = afa.prefill(q[:, :4], k[:, :1].expand(1, 4, 190, 128), v[:, :1].expand(1, 4, 190, 128),
+                         causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1[:, :4], o3) and torch.equal(l1[:, :4], l3)
+
+
+def test_prefill_deterministic_and_fully_written():
+    inp = prefill_inputs(2, 4, 4, 333, 333, 128, 12, with_sinks=True)
+    q, k, v, s = inp["q"].to(DEV), inp["k"].to(DEV), inp["v"].to(DEV), inp["sinks"].to(DEV)
+    outs = []
+    for fill in (float("nan"), 7.0):
+        out = torch.full_like(q, fill)
+        lse = torch.full((2, 4, 333), fill, dtype=torch.float32, device=DEV)
+        afa.prefill(q, k, v, causal=True, window=50, sinks=s, out=out, lse=lse)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0][0].float()).all() and torch.isfinite(outs[0][1]).all()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_prefill_empty_keys():
+    q = torch.randn(1, 2, 40, 128, device=DEV).to(torch.bfloat16)
+    k = torch.zeros(1, 2, 0, 128, device=DEV, dtype=torch.bfloat16)
+    out, lse = afa.prefill(q, k, k, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_prefill_shift_invariance_exact():
+    """Adding one head-dim element a to Q and b to every key adds scale*a*b to each logit."""
+    d = 128
+    inp = prefill_inputs(1, 2, 2, 160, 160, d, 13)
+    q, k, v = inp["q"].clone(), inp["k"].clone(), inp["v"]
+    q[..., -1] = 0
+    k[..., -1] = 0
+    o0, l0 = afa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    q[..., -1] = 4.0
+    k[..., -1] = 2.0
+    o1, l1 = afa.prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    assert (o1.float() - o0.float()).abs().max().item() <= 2e-2
+    assert abs(((l1 - l0) - 8.0 / math.sqrt(d)).abs().max().item()) <= 1e-3
+
+
+FULL = [n for n, w in WORKLOADS.items() if w.kind == "prefill" and w.d <= 256]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_prefill_full_size_sampled(name):
+    w = WORKLOADS[name]
+    print(f"full-size prefill {name}", flush=True)
+    inp = prefill_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed, w.sinks)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    sd = inp["sinks"].to(DEV) if inp["sinks"] is not None else None
+    scale = 1.0 / math.sqrt(w.d)
+    out, lse = afa.prefill(q, k, v, scale=scale, causal=w.causal, window=w.window, sinks=sd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    picks = set()
+    for bi in {0, w.b - 1}:
+        for h in {0, w.h_q - 1, int(rng.integers(w.h_q))}:
+            for i in {0, 1, 127, 128, w.s_q // 2, w.s_q - 2, w.s_q - 1, int(rng.integers(w.s_q))}:
+                picks.add((bi, h, i))
+    picks = sorted(picks)
+    o_ref, l_ref = oracle_rows(inp["q"], inp["k"], inp["v"], scale, w.causal, w.window,
+                               inp["sinks"], picks)
+    ib, ih, ii = (torch.as_tensor(c, device=DEV) for c in np.array(picks).T)
+    o_g = out[ib, ih, ii]
+    l_g = lse[ib, ih, ii]
+    check(o_g, l_g, o_ref, l_ref, name)
+    assert torch.isfinite(out.float()).all()
