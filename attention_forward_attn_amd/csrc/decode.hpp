@@ -16,11 +16,12 @@
 
 namespace attn {
 
-template <int D, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeParams p) {
+template <int D, int NW, int BN, int OCC>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void decode_split_kernel(DecodeParams p) {
   using T = Tile<D, NW, BN>;
   constexpr int BM = T::BM;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * T::STAGE_ELEMS];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hi = lane >> 5;
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeParams p) {
 
   const int hig = hb * BM + w * 32 + lr;  // head inside the kv group
   const bool row_ok = hig < p.ratio;
-  const int head = g * p.ratio + hig;
+  const int head = g * p.ratio + min(hig, p.ratio - 1);
   const int64_t part = ((int64_t)bi * p.h_q + head) * p.n_split + split;
 
   if (kbeg >= kend && split != 0) {  // nothing in this split: zero weight in the merge
@@ -42,19 +43,26 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeParams p) {
     return;
   }
 
+  const int64_t start = p.kv_start[bi];
+  const uint16_t *kbase = p.k + (start + kbeg) * p.k_st + g * p.k_sh;
+  const uint16_t *vbase = p.v + (start + kbeg) * p.v_st + g * p.v_sh;
+  const int n_keys = max(kend - kbeg, 0);
+  const int n_tiles = (n_keys + BN - 1) / BN;
+  const bool wave_ok = hb * BM + w * 32 < p.ratio;
+  if (n_tiles > 0) {
+    T::template dma<false>(smem, kbase, p.k_st, 0, n_keys - 1, w, lane);
+    T::template dma<true>(smem + T::TILE_ELEMS, vbase, p.v_st, 0, n_keys - 1, w, lane);
+  }
+
   u32x4 qreg[T::NKK];
   {
     const uint16_t *qp = p.q + bi * p.q_sb + (int64_t)head * p.q_sh + 8 * hi;
 #pragma unroll
-    for (int kk = 0; kk < T::NKK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row_ok) x = *reinterpret_cast<const u32x4 *>(qp + kk * 16);
-      qreg[kk] = x;
-    }
+    for (int kk = 0; kk < T::NKK; ++kk) qreg[kk] = *reinterpret_cast<const u32x4 *>(qp + kk * 16);
   }
 
   float m = kNegInf, l = 0.0f;
-  if (p.sinks != nullptr && split == 0 && row_ok) {  // the sink belongs to exactly one part
+  if (p.sinks != nullptr && split == 0) {  // the sink belongs to exactly one part
     m = p.sinks[head] * kLog2e;
     l = hi == 0 ? 1.0f : 0.0f;
   }
@@ -62,27 +70,18 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) o[db] = f32x16{};
 
-  const int64_t start = p.kv_start[bi];
-  const uint16_t *kbase = p.k + (start + kbeg) * p.k_st + g * p.k_sh;
-  const uint16_t *vbase = p.v + (start + kbeg) * p.v_st + g * p.v_sh;
-  const int n_keys = max(kend - kbeg, 0);
-  const int n_tiles = (n_keys + BN - 1) / BN;
-  const bool wave_ok = hb * BM + w * 32 < p.ratio;
-
-  typename T::Stage st;
-  if (n_tiles > 0) {
-    T::load(st, kbase, p.k_st, vbase, p.v_st, 0, n_keys, tid);
-    T::store(st, smem, smem + BN * D, tid);
-  }
-  __syncthreads();
-
-  int cur = 0;
   for (int t = 0; t < n_tiles; ++t) {
-    const bool more = t + 1 < n_tiles;
-    if (more) T::load(st, kbase, p.k_st, vbase, p.v_st, (t + 1) * BN, n_keys, tid);
+    const int cur = t & 1;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 1 < n_tiles) {
+      uint16_t *nxt = smem + (cur ^ 1) * T::STAGE_ELEMS;
+      T::template dma<false>(nxt, kbase, p.k_st, (t + 1) * BN, n_keys - 1, w, lane);
+      T::template dma<true>(nxt + T::TILE_ELEMS, vbase, p.v_st, (t + 1) * BN, n_keys - 1, w, lane);
+    }
     const int j0 = t * BN;
     const uint16_t *lk = smem + cur * T::STAGE_ELEMS;
-    const uint16_t *lv = lk + BN * D;
+    const uint16_t *lv = lk + T::TILE_ELEMS;
     if (wave_ok) {
       f32x16 s[T::NKB];
       T::scores(s, qreg, lk, lr, hi);
@@ -95,14 +94,11 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeParams p) {
       }
       u32x4 pk[T::NPV];
       T::softmax_step(s, pk, o, m, l, p.c);
-      T::values(o, pk, lv, lr, hi);
+      T::values(o, pk, lv, lane);
     }
-    if (more) T::store(st, smem + (cur ^ 1) * T::STAGE_ELEMS, smem + (cur ^ 1) * T::STAGE_ELEMS + BN * D, tid);
-    __syncthreads();
-    cur ^= 1;
   }
 
-  const float lt = l + xor32(l);
+  const float lt = sum_across_halves(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
     float *op = p.o_part + part * D + 4 * hi;
@@ -118,10 +114,10 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int NW, int BN>
+template <int D, int NW, int BN, int OCC>
 hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream) {
   dim3 grid(p.n_split, p.h_kv * p.n_hblk, p.B);
-  hipLaunchKernelGGL((decode_split_kernel<D, NW, BN>), grid, dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, NW, BN, OCC>), grid, dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -7,17 +7,23 @@
 // element by element.  Causal masking is bottom-right aligned (o = s_k - s_q).
 // A sink (status page row D5c) enters as the initial state of the running
 // softmax: max = sigma * log2(e) and sum = 1, with nothing added to O.
+//
+// Pipeline: two LDS stages.  At the top of iteration t the wave waits for its
+// own DMA loads of tile t and the workgroup barrier publishes the tile (and
+// guarantees every wave is done with tile t-1's stage); the loads of tile t+1
+// into the other stage are then issued and run under the MMAs of tile t.
 #pragma once
 
 #include "tile.hpp"
 
 namespace attn {
 
-template <int D, int NW, int BN, bool CAUSAL, bool WINDOW>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
+template <int D, int NW, int BN, bool CAUSAL, bool WINDOW, int OCC>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void prefill_kernel(PrefillParams p) {
   using T = Tile<D, NW, BN>;
   constexpr int BM = T::BM;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * T::STAGE_ELEMS];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hi = lane >> 5;
@@ -51,15 +57,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
   const int row = w_lo + lr;
   const bool row_ok = row < p.s_q;
 
+  const uint16_t *kbase = p.k + bi * p.k_sb + g * p.k_sh;
+  const uint16_t *vbase = p.v + bi * p.v_sb + g * p.v_sh;
+  const int jmax = p.s_k - 1;
+  if (t_begin < t_end) {
+    T::template dma<false>(smem, kbase, p.k_ss, t_begin * BN, jmax, w, lane);
+    T::template dma<true>(smem + T::TILE_ELEMS, vbase, p.v_ss, t_begin * BN, jmax, w, lane);
+  }
+
   u32x4 qreg[T::NKK];
   {
-    const uint16_t *qp = p.q + bi * p.q_sb + h * p.q_sh + (int64_t)row * p.q_ss + 8 * hi;
+    const uint16_t *qp = p.q + bi * p.q_sb + h * p.q_sh + (int64_t)min(row, p.s_q - 1) * p.q_ss + 8 * hi;
 #pragma unroll
-    for (int kk = 0; kk < T::NKK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row_ok) x = *reinterpret_cast<const u32x4 *>(qp + kk * 16);
-      qreg[kk] = x;
-    }
+    for (int kk = 0; kk < T::NKK; ++kk) qreg[kk] = *reinterpret_cast<const u32x4 *>(qp + kk * 16);
   }
 
   float m = kNegInf, l = 0.0f;
@@ -71,24 +81,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) o[db] = f32x16{};
 
-  const uint16_t *kbase = p.k + bi * p.k_sb + g * p.k_sh;
-  const uint16_t *vbase = p.v + bi * p.v_sb + g * p.v_sh;
-
-  typename T::Stage st;
-  if (t_begin < t_end) {
-    T::load(st, kbase, p.k_ss, vbase, p.v_ss, t_begin * BN, p.s_k, tid);
-    T::store(st, smem, smem + BN * D, tid);
-  }
-  __syncthreads();
-
-  int cur = 0;
   for (int t = t_begin; t < t_end; ++t) {
-    const bool more = t + 1 < t_end;
-    if (more) T::load(st, kbase, p.k_ss, vbase, p.v_ss, (t + 1) * BN, p.s_k, tid);
-
+    const int cur = (t - t_begin) & 1;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 1 < t_end) {
+      uint16_t *nxt = smem + (cur ^ 1) * T::STAGE_ELEMS;
+      T::template dma<false>(nxt, kbase, p.k_ss, (t + 1) * BN, jmax, w, lane);
+      T::template dma<true>(nxt + T::TILE_ELEMS, vbase, p.v_ss, (t + 1) * BN, jmax, w, lane);
+    }
     const int j0 = t * BN;
     const uint16_t *lk = smem + cur * T::STAGE_ELEMS;
-    const uint16_t *lv = lk + BN * D;
+    const uint16_t *lv = lk + T::TILE_ELEMS;
     bool active = w_lo < p.s_q;
     if (CAUSAL) active = active && j0 <= w_hi + off;
     if (WINDOW) active = active && j0 + BN - 1 >= w_lo + off - p.window + 1;
@@ -99,28 +103,24 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
       if (CAUSAL) need_mask = need_mask || (j0 + BN - 1 > w_lo + off);
       if (WINDOW) need_mask = need_mask || (j0 < w_hi + off - p.window + 1);
       if (need_mask) {
-        const int lim_hi = CAUSAL ? row + off : 0x7fffffff;
-        const int lim_lo = WINDOW ? row + off - p.window + 1 : -0x7fffffff;
+        const int lim_hi = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
+        const int lim_lo = WINDOW ? row + off - p.window + 1 : 0;
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = j0 + T::key_of(kb, i, hi);
-            const bool vis = j < p.s_k && j <= lim_hi && j >= lim_lo;
-            if (!vis) s[kb][i] = kNegInf;
+            if (j > lim_hi || j < lim_lo) s[kb][i] = kNegInf;
           }
       }
       u32x4 pk[T::NPV];
       T::softmax_step(s, pk, o, m, l, p.c);
-      T::values(o, pk, lv, lr, hi);
+      T::values(o, pk, lv, lane);
     }
-    if (more) T::store(st, smem + (cur ^ 1) * T::STAGE_ELEMS, smem + (cur ^ 1) * T::STAGE_ELEMS + BN * D, tid);
-    __syncthreads();
-    cur ^= 1;
   }
 
   // Epilogue: O / l once, bf16 round-to-nearest-even; LSE = ln2 * (m + log2 l).
-  const float lt = l + xor32(l);
+  const float lt = sum_across_halves(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
     uint16_t *op = p.o + bi * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss + 4 * hi;
@@ -139,9 +139,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
 }
 
 // Host-side launcher of one instantiation.
-template <int D, int NW, int BN, bool CAUSAL, bool WINDOW>
+template <int D, int NW, int BN, bool CAUSAL, bool WINDOW, int OCC>
 hipError_t launch_prefill(const PrefillParams &p, int n_units, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, NW, BN, CAUSAL, WINDOW>), dim3(n_units), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((prefill_kernel<D, NW, BN, CAUSAL, WINDOW, OCC>), dim3(n_units), dim3(NW * 64), 0,
                      stream, p);
   return hipGetLastError();
 }

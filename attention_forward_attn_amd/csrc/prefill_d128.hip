@@ -6,9 +6,9 @@ namespace attn {
 
 hipError_t prefill_d128(const PrefillParams &p, int mask, int n_units, hipStream_t s) {
   switch (mask) {
-    case kMaskNone: return launch_prefill<128, 4, 64, false, false>(p, n_units, s);
-    case kMaskCausal: return launch_prefill<128, 4, 64, true, false>(p, n_units, s);
-    default: return launch_prefill<128, 4, 64, true, true>(p, n_units, s);
+    case kMaskNone: return launch_prefill<128, 4, 64, false, false, 2>(p, n_units, s);
+    case kMaskCausal: return launch_prefill<128, 4, 64, true, false, 2>(p, n_units, s);
+    default: return launch_prefill<128, 4, 64, true, true, 2>(p, n_units, s);
   }
 }
 
