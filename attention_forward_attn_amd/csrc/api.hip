@@ -32,6 +32,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool bf16_stride_ok(int64_t s) { return s >= 0 && (s % 8) == 0; }
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
+// Key/value row strides are bounded so that byte offsets inside one tile of
+// up to 128 rows fit the 32-bit buffer offsets of the kernels.
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 
 // Largest element offset reachable through (extent, stride) pairs, plus the row length.
 int64_t span(std::initializer_list<std::pair<int64_t, int64_t>> dims, int64_t last) {
@@ -93,6 +96,8 @@ attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
   for (int64_t s : st)
     if (!bf16_stride_ok(s)) return fail(ATTN_ERR_STRIDE, "bf16 strides must be non-negative multiples of 8 elements");
   if (a->lse && (a->lse_sb < 0 || a->lse_sh < 0)) return fail(ATTN_ERR_STRIDE, "lse strides must be >= 0");
+  if (a->k_ss >= kMaxRowStride || a->v_ss >= kMaxRowStride)
+    return fail(ATTN_ERR_STRIDE, "k/v sequence strides must be below 2^24 elements");
   const int64_t bmax = span({{a->b, a->q_sb}, {a->h_q, a->q_sh}, {a->s_q, a->q_ss}}, a->d);
   const int64_t kmax = span({{a->b, a->k_sb}, {a->h_kv, a->k_sh}, {a->s_k, a->k_ss}}, a->d);
   const int64_t vmax = span({{a->b, a->v_sb}, {a->h_kv, a->v_sh}, {a->s_k, a->v_ss}}, a->d);
@@ -172,6 +177,8 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
   for (int64_t s : st)
     if (!bf16_stride_ok(s)) return fail(ATTN_ERR_STRIDE, "bf16 strides must be non-negative multiples of 8 elements");
   if (a->lse && a->lse_sb < 0) return fail(ATTN_ERR_STRIDE, "lse_sb must be >= 0");
+  if (a->k_st >= kMaxRowStride || a->v_st >= kMaxRowStride)
+    return fail(ATTN_ERR_STRIDE, "k/v token strides must be below 2^24 elements");
   const size_t need = attn_fwd_decode_workspace_size(a->B, a->h_q, a->d, a->max_kv_len, a->split_size);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 void decode_split_kernel(DecodeParams p) {
   using T = Tile<D, NW, BN>;
   constexpr int BM = T::BM;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * T::STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * T::STAGE_BYTES / 2];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hi = lane >> 5;
@@ -49,10 +49,9 @@ void decode_split_kernel(DecodeParams p) {
   const int n_keys = max(kend - kbeg, 0);
   const int n_tiles = (n_keys + BN - 1) / BN;
   const bool wave_ok = hb * BM + w * 32 < p.ratio;
-  if (n_tiles > 0) {
-    T::template dma<false>(smem, kbase, p.k_st, 0, n_keys - 1, w, lane);
-    T::template dma<true>(smem + T::TILE_ELEMS, vbase, p.v_st, 0, n_keys - 1, w, lane);
-  }
+  typename T::Lane ln;
+  T::init_lane(ln, smem, p.k_st, p.v_st, w, lane);
+  if (n_tiles > 0) T::dma(ln, smem, kbase, p.k_st, vbase, p.v_st, 0, n_keys, w);
 
   u32x4 qreg[T::NKK];
   {
@@ -74,17 +73,14 @@ void decode_split_kernel(DecodeParams p) {
     const int cur = t & 1;
     wait_vmcnt<0>();
     __syncthreads();
-    if (t + 1 < n_tiles) {
-      uint16_t *nxt = smem + (cur ^ 1) * T::STAGE_ELEMS;
-      T::template dma<false>(nxt, kbase, p.k_st, (t + 1) * BN, n_keys - 1, w, lane);
-      T::template dma<true>(nxt + T::TILE_ELEMS, vbase, p.v_st, (t + 1) * BN, n_keys - 1, w, lane);
-    }
+    if (t + 1 < n_tiles)
+      T::dma(ln, smem + (cur ^ 1) * (T::STAGE_BYTES / 2), kbase, p.k_st, vbase, p.v_st, (t + 1) * BN,
+             n_keys, w);
     const int j0 = t * BN;
-    const uint16_t *lk = smem + cur * T::STAGE_ELEMS;
-    const uint16_t *lv = lk + T::TILE_ELEMS;
+    const uint32_t stage_off = cur * T::STAGE_BYTES;
     if (wave_ok) {
       f32x16 s[T::NKB];
-      T::scores(s, qreg, lk, lr, hi);
+      T::scores(s, qreg, ln, stage_off);
       if (j0 + BN > n_keys) {
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
@@ -94,7 +90,7 @@ void decode_split_kernel(DecodeParams p) {
       }
       u32x4 pk[T::NPV];
       T::softmax_step(s, pk, o, m, l, p.c);
-      T::values(o, pk, lv, lane);
+      T::values(o, pk, ln, stage_off);
     }
   }
 

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 void prefill_kernel(PrefillParams p) {
   using T = Tile<D, NW, BN>;
   constexpr int BM = T::BM;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * T::STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * T::STAGE_BYTES / 2];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hi = lane >> 5;
@@ -59,11 +59,9 @@ void prefill_kernel(PrefillParams p) {
 
   const uint16_t *kbase = p.k + bi * p.k_sb + g * p.k_sh;
   const uint16_t *vbase = p.v + bi * p.v_sb + g * p.v_sh;
-  const int jmax = p.s_k - 1;
-  if (t_begin < t_end) {
-    T::template dma<false>(smem, kbase, p.k_ss, t_begin * BN, jmax, w, lane);
-    T::template dma<true>(smem + T::TILE_ELEMS, vbase, p.v_ss, t_begin * BN, jmax, w, lane);
-  }
+  typename T::Lane ln;
+  T::init_lane(ln, smem, p.k_ss, p.v_ss, w, lane);
+  if (t_begin < t_end) T::dma(ln, smem, kbase, p.k_ss, vbase, p.v_ss, t_begin * BN, p.s_k, w);
 
   u32x4 qreg[T::NKK];
   {
@@ -85,20 +83,17 @@ void prefill_kernel(PrefillParams p) {
     const int cur = (t - t_begin) & 1;
     wait_vmcnt<0>();
     __syncthreads();
-    if (t + 1 < t_end) {
-      uint16_t *nxt = smem + (cur ^ 1) * T::STAGE_ELEMS;
-      T::template dma<false>(nxt, kbase, p.k_ss, (t + 1) * BN, jmax, w, lane);
-      T::template dma<true>(nxt + T::TILE_ELEMS, vbase, p.v_ss, (t + 1) * BN, jmax, w, lane);
-    }
+    if (t + 1 < t_end)
+      T::dma(ln, smem + (cur ^ 1) * (T::STAGE_BYTES / 2), kbase, p.k_ss, vbase, p.v_ss, (t + 1) * BN,
+             p.s_k, w);
     const int j0 = t * BN;
-    const uint16_t *lk = smem + cur * T::STAGE_ELEMS;
-    const uint16_t *lv = lk + T::TILE_ELEMS;
+    const uint32_t stage_off = cur * T::STAGE_BYTES;
     bool active = w_lo < p.s_q;
     if (CAUSAL) active = active && j0 <= w_hi + off;
     if (WINDOW) active = active && j0 + BN - 1 >= w_lo + off - p.window + 1;
     if (active) {
       f32x16 s[T::NKB];
-      T::scores(s, qreg, lk, lr, hi);
+      T::scores(s, qreg, ln, stage_off);
       bool need_mask = j0 + BN > p.s_k;
       if (CAUSAL) need_mask = need_mask || (j0 + BN - 1 > w_lo + off);
       if (WINDOW) need_mask = need_mask || (j0 < w_hi + off - p.window + 1);
@@ -115,7 +110,7 @@ void prefill_kernel(PrefillParams p) {
       }
       u32x4 pk[T::NPV];
       T::softmax_step(s, pk, o, m, l, p.c);
-      T::values(o, pk, lv, lane);
+      T::values(o, pk, ln, stage_off);
     }
   }
 

@@ -18,15 +18,20 @@
 // O divided by the row sum only once at the end), laid out for 64-wide
 // wavefronts and a register-resident accumulator instead of Blackwell's TMEM.
 //
-// K and V tiles are copied HBM -> LDS by direct-to-LDS loads (no register
-// staging), row-major.  The score MMA reads its K operand as one 16-byte row
-// segment per lane; the value MMA needs V transposed and gets it from the
-// gfx950 LDS transpose read (ds_read_b64_tr_b16: inside each 16-lane group,
-// lane 4a+b points at 4 consecutive head-dim elements of key row a, and lane i
-// receives head-dim element i of the 4 keys).  Each access pattern has its own
-// XOR swizzle of the 16-byte chunks of a row so that the lanes serviced
-// together touch distinct LDS banks; the direct-to-LDS load writes each wave's
-// 1 KiB contiguously and applies the swizzle on the global side instead.
+// K and V tiles are copied HBM -> LDS by direct-to-LDS buffer loads (no
+// register staging), row-major.  Each tile gets its own buffer descriptor
+// whose base is the tile's first key and whose size ends at the last valid key,
+// so the per-lane byte offsets are fixed for the whole kernel and the hardware
+// range check zero-fills rows past the end of the keys.  The score MMA reads
+// its K operand as one 16-byte row segment per lane; the value MMA needs V
+// transposed and gets it from the gfx950 LDS transpose read (ds_read_b64_tr_b16:
+// inside each 16-lane group, lane 4a+b points at 4 consecutive head-dim
+// elements of key row a, and lane i receives head-dim element i of the 4
+// keys).  Each access pattern has its own XOR swizzle of the 16-byte chunks of
+// a row so that the lanes serviced together touch distinct LDS banks; the
+// direct-to-LDS load writes each wave's 1 KiB contiguously and applies the
+// swizzle on the global side instead.  All LDS read addresses are per-lane
+// constants plus immediate offsets.
 //
 // The rescale is lazy: the running max used as the exponent base only moves
 // when some row of the wave sees its max grow by more than 2^8.  O and the row
@@ -38,9 +43,7 @@
 
 namespace attn {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // s_waitcnt with vmcnt = n (expcnt and lgkmcnt left at their maxima).
 template <int N>
@@ -64,35 +67,55 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   return (uint32_t)(uintptr_t)q;
 }
 
-// ds_read_b64_tr_b16 issued through inline assembly.  The compiler cannot
-// attach a memory operand to the transpose read, so it would otherwise wait for
-// every outstanding direct-to-LDS load (including the next tile's prefetch)
-// before it.  The read's completion is handled explicitly by lds_wait_all.
+// Buffer descriptor over [base, base + bytes) (gfx9 raw buffer, stride 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// LDS reads issued through inline assembly with an immediate offset.  The
+// compiler cannot attach a memory operand to the transpose read and would
+// otherwise wait for every outstanding direct-to-LDS load (including the next
+// tile's prefetch) before it; completion is handled by lds_wait below.
+template <int OFF>
 __device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
   u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
 }
 
-// Wait for all outstanding LDS reads of this wave; the results are routed
-// through the statement so that no use can be scheduled above the wait.
-template <int N>
-__device__ __forceinline__ void lds_wait_all(u32x2 (&a)[N], u32x2 (&b)[N]) {
-  if constexpr (N == 1) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(b[0]));
-  } else if constexpr (N == 2) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]));
-  } else if constexpr (N == 4) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]), "+v"(a[2]), "+v"(b[2]),
-                   "+v"(a[3]), "+v"(b[3]));
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(N): LDS reads of one wave complete in order, so this
+// guarantees every read issued before the last N has landed.  The registers
+// of those reads are routed through the statement (and through empty
+// statements after it, which keep their order) so that no use can be
+// scheduled above the wait.  No scalar memory loads are in flight inside the
+// tile loops, which would otherwise share the counter.
+template <typename V>
+__device__ __forceinline__ void tie8(V *a, int m) {
+  if (m >= 8) {
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                 "+v"(a[6]), "+v"(a[7]));
+  } else if (m >= 4) {
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+    if (m > 4) tie8(a + 4, m - 4);
   } else {
-    static_assert(N == 8, "unsupported count");
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]), "+v"(a[2]), "+v"(b[2]),
-                   "+v"(a[3]), "+v"(b[3]), "+v"(a[4]), "+v"(b[4]), "+v"(a[5]), "+v"(b[5]),
-                   "+v"(a[6]), "+v"(b[6]), "+v"(a[7]), "+v"(b[7]));
+    for (int i = 0; i < m; ++i) asm volatile("" : "+v"(a[i]));
   }
+}
+template <int N, typename V, int M>
+__device__ __forceinline__ void lds_wait(V (&a)[M]) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
+#pragma unroll
+  for (int i = 0; i < M; i += 8) tie8(a + i, M - i < 8 ? M - i : 8);
 }
 
 template <int D, int NW, int BN>
@@ -105,96 +128,151 @@ struct Tile {
   static constexpr int NKK = D / 16;   // k-steps of the score MMA
   static constexpr int NPV = BN / 16;  // k-steps of the value MMA
   static constexpr int TILE_ELEMS = BN * D;                // one K or V tile, bf16 elements
-  static constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;       // K + V
+  static constexpr int TILE_BYTES = TILE_ELEMS * 2;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;       // K + V
   static constexpr int LOADS = TILE_ELEMS / 8 / 64 / NW;   // 1-KiB DMA loads per wave per tile
   static constexpr int ROWS_PER_256 = 256 / (2 * D) > 0 ? 256 / (2 * D) : 1;
   static constexpr float kLazy = 8.0f;  // log2 of the growth that forces a rescale
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(LOADS * 64 * NW * 8 == TILE_ELEMS, "tile must split into whole 1-KiB wave loads");
+  static_assert(STAGE_BYTES <= 65536, "LDS immediate offsets must stay below 64 KiB");
 
   // Chunk swizzle for the score MMA's K reads: 16 lanes read one chunk of 16
   // consecutive rows.
-  __device__ static __forceinline__ int kswz(int r) {
-    return D == 64 ? ((r >> 1) & 7) : (r & 15);
-  }
+  __device__ static __forceinline__ int kswz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
   // Chunk swizzle for the value MMA's transposed V reads: 16 lanes read 4
   // chunks of 4 consecutive rows.
   __device__ static __forceinline__ int vswz(int r) { return 4 * ((r / ROWS_PER_256) & 3) & (CH - 1); }
 
-  // Issue this wave's share of the DMA loads of one K or V tile: rows
-  // [j0, j0 + BN) of `base` (row stride `rs`), rows past `jmax` clamped to it
-  // (their contents are masked out or multiplied by zero).
-  template <bool IS_V>
-  __device__ static __forceinline__ void dma(uint16_t *lds_tile, const uint16_t *base, int64_t rs,
-                                             int j0, int jmax, int w, int lane) {
+  // Per-lane constants: global byte offsets of this lane's DMA chunks inside a
+  // tile, and LDS byte addresses (stage 0) of its MMA operands.
+  struct Lane {
+    uint32_t kg[LOADS], vg[LOADS];  // global byte offsets (tile-relative)
+    uint32_t kl[NKK];               // LDS address of the K operand of k-step kk, key block 0
+    uint32_t vl[NDB];               // LDS address of the V^T operand of head-dim block db, k-step 0
+  };
+
+  __device__ static __forceinline__ void init_lane(Lane &ln, const uint16_t *smem, int64_t k_rs,
+                                                   int64_t v_rs, int w, int lane) {
+    const int lr = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int blk = u * NW + w;            // which 1-KiB block of the tile
-      const int pch = blk * 64 + lane;       // physical 16-byte chunk written by this lane
+      const int pch = (u * NW + w) * 64 + lane;  // physical 16-byte chunk written by this lane
       const int r = pch / CH;
-      const int c = (pch % CH) ^ (IS_V ? vswz(r) : kswz(r));
-      const int j = min(j0 + r, jmax);
-      const uint16_t *src = base + (int64_t)j * rs + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_tile + blk * 512), 16, 0, 0);
+      ln.kg[u] = (uint32_t)(r * k_rs * 2) + (uint32_t)(((pch % CH) ^ kswz(r)) * 16);
+      ln.vg[u] = (uint32_t)(r * v_rs * 2) + (uint32_t)(((pch % CH) ^ vswz(r)) * 16);
     }
+    const uint32_t base = lds_offset(smem);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      ln.kl[kk] = base + lr * D * 2 + (((2 * kk + hi) ^ kswz(lr)) * 16);
+    const int grp = lane >> 4, s = lane & 15;
+    const int krow = 4 * (grp >> 1) + (s >> 2);     // key row inside a 16-key step
+    const int dcol = 16 * (grp & 1) + 4 * (s & 3);  // head-dim column inside a 32-block
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int col = db * 32 + dcol;
+      ln.vl[db] = base + TILE_BYTES + krow * D * 2 + (((col >> 3) ^ vswz(krow)) * 16) + (col & 7) * 2;
+    }
+  }
+
+  // Issue this wave's share of the DMA loads of the K and V tiles that start
+  // at key j0 (< nkeys) into the given stage; rows at or past `nkeys` read as
+  // zero.  Byte offsets inside a tile must fit in 32 bits (row strides below
+  // 2^24 elements, checked by the host).
+  __device__ static __forceinline__ void dma(const Lane &ln, uint16_t *stage, const uint16_t *kbase,
+                                             int64_t k_rs, const uint16_t *vbase, int64_t v_rs,
+                                             int j0, int nkeys, int w) {
+    // The descriptor ends exactly at the end of the last valid row.
+    const int rows = min(nkeys - j0, BN);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + j0 * k_rs, (uint32_t)((rows - 1) * k_rs * 2 + D * 2));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + j0 * v_rs, (uint32_t)((rows - 1) * v_rs * 2 + D * 2));
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(stage + (u * NW + w) * 512), 16,
+                                               ln.kg[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(stage + TILE_ELEMS + (u * NW + w) * 512),
+                                               16, ln.vg[u], 0, 0, 0);
   }
 
   // S^T block accumulators of this wave for the staged tile.  The K operands
-  // of k-step kk+1 are read while the MMAs of step kk run.
-  __device__ static __forceinline__ u32x4 kread(const uint16_t *lk, int kb, int kk, int lr, int hi) {
-    const int r = kb * 32 + lr;
-    return *reinterpret_cast<const u32x4 *>(lk + r * D + (((2 * kk + hi) ^ kswz(r)) * 8));
+  // of k-step kk+1 are in flight while the MMAs of step kk run.
+  template <int KK>
+  __device__ static __forceinline__ void kreads(u32x4 (&a)[NKB], const Lane &ln, uint32_t stage_off) {
+    const uint32_t ad = ln.kl[KK] + stage_off;
+    a[0] = ds_read_b128<0>(ad);
+    if constexpr (NKB > 1) a[1] = ds_read_b128<1 * 32 * D * 2>(ad);
+    if constexpr (NKB > 2) a[2] = ds_read_b128<2 * 32 * D * 2>(ad);
+    if constexpr (NKB > 3) a[3] = ds_read_b128<3 * 32 * D * 2>(ad);
+    static_assert(NKB <= 4, "at most 128 keys per tile");
+  }
+  template <int KK>
+  __device__ static __forceinline__ void score_steps(f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK],
+                                                     u32x4 (&cur)[NKB], u32x4 (&nxt)[NKB],
+                                                     const Lane &ln, uint32_t stage_off) {
+    if constexpr (KK + 1 < NKK) {
+      kreads<KK + 1>(nxt, ln, stage_off);
+      lds_wait<NKB>(cur);
+    } else {
+      lds_wait<0>(cur);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(cur[kb], qreg[KK], s[kb]);
+    if constexpr (KK + 1 < NKK) score_steps<KK + 1>(s, qreg, nxt, cur, ln, stage_off);
   }
   __device__ static __forceinline__ void scores(f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK],
-                                                const uint16_t *lk, int lr, int hi) {
-    u32x4 a[2][NKB];
+                                                const Lane &ln, uint32_t stage_off) {
+    u32x4 a[NKB], b[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      a[0][kb] = kread(lk, kb, 0, lr, hi);
-    }
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      if (kk + 1 < NKK) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) a[(kk + 1) & 1][kb] = kread(lk, kb, kk + 1, lr, hi);
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(a[kk & 1][kb], qreg[kk], s[kb]);
-    }
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    kreads<0>(a, ln, stage_off);
+    score_steps<0>(s, qreg, a, b, ln, stage_off);
   }
 
-  // Byte offset of (row, col) of a V tile in LDS, swizzled for the transposed read.
-  __device__ static __forceinline__ uint32_t vaddr(const uint16_t *lv, int row, int col) {
-    const int c = (col >> 3) ^ vswz(row);
-    return lds_offset(lv + row * D + c * 8 + (col & 7));
+  // O^T += V^T . P^T, one k-step of 16 keys at a time, with P packed bf16
+  // (8 keys per lane).  The k-slot order of P (8*hi + j <-> key
+  // 16T + 8*(j/4) + 4*hi + j%4) is matched by reading keys 16T + 4*hi + {0..3}
+  // and 16T + 8 + 4*hi + {0..3}.  Work goes in units of (k-step, group of up
+  // to 4 head-dim blocks), 8 transpose reads each, and the reads of unit U+1
+  // are in flight while the MMAs of unit U run.
+  static constexpr int VG = NDB < 4 ? NDB : 4;  // head-dim blocks per unit
+  static constexpr int VUNITS = NPV * (NDB / VG);
+  template <int U>
+  __device__ static __forceinline__ void vreads(u32x2 (&v)[2 * VG], const Lane &ln, uint32_t stage_off) {
+    constexpr int T_ = U / (NDB / VG), G = U % (NDB / VG);
+    constexpr int OFF_LO = T_ * 16 * D * 2;
+    constexpr int OFF_HI = OFF_LO + 8 * D * 2;
+#pragma unroll
+    for (int i = 0; i < VG; ++i) {
+      v[2 * i] = ds_read_tr16<OFF_LO>(ln.vl[G * VG + i] + stage_off);
+      v[2 * i + 1] = ds_read_tr16<OFF_HI>(ln.vl[G * VG + i] + stage_off);
+    }
   }
-
-  // O^T += V^T . P^T with P given as packed bf16 (one u32x4 of 8 keys per k-step).
-  // The k-slot order of P (8*hi + j <-> key 16t + 8*(j/4) + 4*hi + j%4) is
-  // matched by reading keys 16t + 4*hi + {0..3} and 16t + 8 + 4*hi + {0..3}.
-  // The transposed reads of one k-step are issued together and waited for
-  // once (see ds_read_tr16).
+  template <int U>
+  __device__ static __forceinline__ void value_steps(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV],
+                                                     u32x2 (&cur)[2 * VG], u32x2 (&nxt)[2 * VG],
+                                                     const Lane &ln, uint32_t stage_off) {
+    constexpr int T_ = U / (NDB / VG), G = U % (NDB / VG);
+    if constexpr (U + 1 < VUNITS) {
+      vreads<U + 1>(nxt, ln, stage_off);
+      lds_wait<2 * VG>(cur);
+    } else {
+      lds_wait<0>(cur);
+    }
+#pragma unroll
+    for (int i = 0; i < VG; ++i) {
+      const u32x4 a = {cur[2 * i][0], cur[2 * i][1], cur[2 * i + 1][0], cur[2 * i + 1][1]};
+      o[G * VG + i] = mfma32(a, pk[T_], o[G * VG + i]);
+    }
+    if constexpr (U + 1 < VUNITS) value_steps<U + 1>(o, pk, nxt, cur, ln, stage_off);
+  }
   __device__ static __forceinline__ void values(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV],
-                                                const uint16_t *lv, int lane) {
-    const int grp = lane >> 4, s = lane & 15;
-    const int krow = 4 * (grp >> 1) + (s >> 2);       // key row inside a 16-key step
-    const int dcol = 16 * (grp & 1) + 4 * (s & 3);    // head-dim column inside a 32-block
-#pragma unroll
-    for (int t = 0; t < NPV; ++t) {
-      u32x2 lo[NDB], hi2[NDB];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        lo[db] = ds_read_tr16(vaddr(lv, 16 * t + krow, db * 32 + dcol));
-        hi2[db] = ds_read_tr16(vaddr(lv, 16 * t + 8 + krow, db * 32 + dcol));
-      }
-      lds_wait_all(lo, hi2);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x4 a = {lo[db][0], lo[db][1], hi2[db][0], hi2[db][1]};
-        o[db] = mfma32(a, pk[t], o[db]);
-      }
-    }
+                                                const Lane &ln, uint32_t stage_off) {
+    u32x2 a[2 * VG], b[2 * VG];
+    vreads<0>(a, ln, stage_off);
+    value_steps<0>(o, pk, a, b, ln, stage_off);
   }
 
   // Key index (relative to the tile start) held by accumulator register i of block kb.
@@ -224,24 +302,19 @@ struct Tile {
     const float base = (m == kNegInf) ? 0.0f : m;
     float rs = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(fmaf(s[kb][i], c, -base));
-        s[kb][i] = e;
-        rs += e;
-      }
-    l += rs;
-#pragma unroll
     for (int t = 0; t < NPV; ++t) {
       const int kb = t >> 1, r0 = (t & 1) * 8;
       u32x4 x;
-      x[0] = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
-      x[1] = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
-      x[2] = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
-      x[3] = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float e0 = fast_exp2(fmaf(s[kb][r0 + 2 * q], c, -base));
+        const float e1 = fast_exp2(fmaf(s[kb][r0 + 2 * q + 1], c, -base));
+        rs += e0 + e1;
+        x[q] = pack_bf16x2(e0, e1);
+      }
       pk[t] = x;
     }
+    l += rs;
   }
 };
 

@@ -218,6 +218,9 @@ def main():
     ap.add_argument("--workload", default=None, help="bench one named workload alone")
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 512 MiB device copy 3 times (a known-size reference for "
+                         "HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -233,6 +236,14 @@ def main():
     afa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if args.workload or args.all:
         names = [args.workload] if args.workload else [

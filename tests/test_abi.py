@@ -85,6 +85,7 @@ PREFILL_BAD = [
     ("causal=2", dict(causal=2), 2),
     ("odd seq stride", dict(q_ss=130), 3),
     ("negative stride", dict(k_sh=-8), 3),
+    ("huge key stride", dict(k_ss=1 << 24), 3),
     ("misaligned q", dict(q=FAKE + 2), 4),
     ("misaligned v", dict(v=FAKE + 8), 4),
     ("misaligned lse", dict(lse=FAKE + 2), 4),
@@ -141,6 +142,7 @@ DECODE_BAD = [
     ("negative max len", dict(max_kv_len=-1), 2),
     ("zero scale", dict(scale=0.0), 2),
     ("odd token stride", dict(k_st=12), 3),
+    ("huge token stride", dict(v_st=1 << 24), 3),
     ("misaligned k", dict(k=FAKE + 4), 4),
     ("misaligned kv_start", dict(kv_start=FAKE + 4), 4),
 ]
