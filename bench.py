@@ -180,16 +180,58 @@ def timed(cases, steps: int, warmup: int):
     return per, wall_ms
 
 
-def roofline_prefill(flops: int, ms: float):
+def kernel_source_hash() -> str:
+    """Short hash of the HIP sources; a recorded counter profile is valid only for this hash."""
+    import hashlib
+
+    d = os.path.join(ROOT, "attention_forward_attn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hpp", ".hip")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(*profiles: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from committed profile summaries.
+
+    Each summary ends with a `traffic_record:` line naming the kernel-source hash
+    it was measured on; if any summary is missing or was taken on other
+    sources, the traffic is unknown (None).
+    """
+    total = 0
+    want = kernel_source_hash()
+    for name in profiles:
+        path = os.path.join(ROOT, "profiles", name)
+        if not os.path.exists(path):
+            return None
+        rec = None
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith("traffic_record:"):
+                    rec = dict(kv.split("=", 1) for kv in line.split()[1:])
+        if rec is None or rec.get("kernel_src_sha") != want:
+            return None
+        total += int(float(rec["fetch_bytes"])) + int(float(rec["write_bytes"]))
+    return total
+
+
+PREFILL_PROFILE = ("prefill_d128_causal_b2_h16_s4096.md",)
+DECODE_PROFILES = ("decode_split_d128_B64_hq128.md", "decode_combine_d128_B64_hq128.md")
+
+
+def roofline_prefill(flops: int, ms: float, traffic=None):
     achieved = flops / (ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
 
-def roofline_decode(nbytes: int, ms: float):
+def roofline_decode(nbytes: int, ms: float, traffic=None):
     achieved = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
 
 
 def bench_one(name: str, steps: int, warmup: int, dev):
@@ -257,8 +299,8 @@ def main():
     pc = PrefillCase(wp, 2, dev)
     dc = DecodeCase(wd, 4, dev)
     (pre_ms, dec_ms), wall_ms = timed([pc, dc], args.steps, args.warmup)
-    pre = roofline_prefill(pc.flops, pre_ms)
-    dec = roofline_decode(dc.bytes, dec_ms)
+    pre = roofline_prefill(pc.flops, pre_ms, recorded_traffic(*PREFILL_PROFILE))
+    dec = roofline_decode(dc.bytes, dec_ms, recorded_traffic(*DECODE_PROFILES))
     line = {
         "metric": "attn fwd TFLOPS (bf16, causal-adjusted) + decode HBM GB/s, 1xMI355X",
         "value": pre["achieved"],
