@@ -105,7 +105,6 @@ attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
   if (bmax > (int64_t(1) << 40) || kmax > (int64_t(1) << 40) || vmax > (int64_t(1) << 40) ||
       omax > (int64_t(1) << 40))
     return fail(ATTN_ERR_SHAPE, "tensor extent exceeds 2^40 elements");
-  if (a->d == 512) return fail(ATTN_ERR_UNSUPPORTED, "d = 512 prefill is not built yet");
 
   const int bm = attn::prefill_block_rows(a->d);
   const int64_t n_qtiles = (a->s_q + bm - 1) / bm;
@@ -136,7 +135,8 @@ attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
   switch (a->d) {
     case 64: e = attn::prefill_d64(p, mask, (int)n_units, s); break;
     case 128: e = attn::prefill_d128(p, mask, (int)n_units, s); break;
-    default: e = attn::prefill_d256(p, mask, (int)n_units, s); break;
+    case 256: e = attn::prefill_d256(p, mask, (int)n_units, s); break;
+    default: e = attn::prefill_d512(p, mask, (int)n_units, s); break;
   }
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();
@@ -285,5 +285,5 @@ attn_status attn_combine(const attn_combine_args *a, void *stream) {
 }  // extern "C"
 
 namespace attn {
-int prefill_block_rows(int d) { return (d == 64 || d == 128 || d == 256) ? 128 : 0; }
+int prefill_block_rows(int d) { return (d == 64 || d == 128 || d == 256) ? 128 : (d == 512 ? 64 : 0); }
 }  // namespace attn

@@ -14,6 +14,7 @@ int prefill_block_rows(int d);
 hipError_t prefill_d64(const PrefillParams &p, int mask, int n_units, hipStream_t s);
 hipError_t prefill_d128(const PrefillParams &p, int mask, int n_units, hipStream_t s);
 hipError_t prefill_d256(const PrefillParams &p, int mask, int n_units, hipStream_t s);
+hipError_t prefill_d512(const PrefillParams &p, int mask, int n_units, hipStream_t s);
 
 // Query heads per decode workgroup (0 if unsupported).
 int decode_block_rows(int d);

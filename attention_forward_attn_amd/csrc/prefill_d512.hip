@@ -1,0 +1,15 @@
+// Prefill instantiations for head dim 512 (two 256-wide halves per pair of waves).
+#include "kernels.hpp"
+#include "prefill.hpp"
+
+namespace attn {
+
+hipError_t prefill_d512(const PrefillParams &p, int mask, int n_units, hipStream_t s) {
+  switch (mask) {
+    case kMaskNone: return launch_prefill<512, 4, 32, false, false, 1, 256>(p, n_units, s);
+    case kMaskCausal: return launch_prefill<512, 4, 32, true, false, 1, 256>(p, n_units, s);
+    default: return launch_prefill<512, 4, 32, true, true, 1, 256>(p, n_units, s);
+  }
+}
+
+}  // namespace attn

@@ -118,14 +118,18 @@ __device__ __forceinline__ void lds_wait(V (&a)[M]) {
   for (int i = 0; i < M; i += 8) tie8(a + i, M - i < 8 ? M - i : 8);
 }
 
-template <int D, int NW, int BN>
+// DS is the head-dim slice a wave works on: DS = D normally; for D = 512 two
+// waves share the same query rows and each takes one 256-wide half, for the
+// partial scores as well as for the output columns (see prefill.hpp).
+template <int D, int NW, int BN, int DS = D>
 struct Tile {
   static constexpr int NT = NW * 64;   // threads per workgroup
-  static constexpr int BM = NW * 32;   // query rows per workgroup
+  static constexpr int SPLIT = D / DS; // waves sharing one block of query rows
+  static constexpr int BM = NW * 32 / SPLIT;  // query rows per workgroup
   static constexpr int CH = D / 8;     // 16-byte chunks per K / V row
   static constexpr int NKB = BN / 32;  // 32-key blocks per tile (score accumulators)
-  static constexpr int NDB = D / 32;   // 32-wide head-dim blocks (O accumulators)
-  static constexpr int NKK = D / 16;   // k-steps of the score MMA
+  static constexpr int NDB = DS / 32;  // 32-wide head-dim blocks of this wave's slice (O accumulators)
+  static constexpr int NKK = DS / 16;  // k-steps of the score MMA over this wave's slice
   static constexpr int NPV = BN / 16;  // k-steps of the value MMA
   static constexpr int TILE_ELEMS = BN * D;                // one K or V tile, bf16 elements
   static constexpr int TILE_BYTES = TILE_ELEMS * 2;
@@ -153,7 +157,7 @@ struct Tile {
   };
 
   __device__ static __forceinline__ void init_lane(Lane &ln, const uint16_t *smem, int64_t k_rs,
-                                                   int64_t v_rs, int w, int lane) {
+                                                   int64_t v_rs, int w, int lane, int slice = 0) {
     const int lr = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
@@ -165,13 +169,13 @@ struct Tile {
     const uint32_t base = lds_offset(smem);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      ln.kl[kk] = base + lr * D * 2 + (((2 * kk + hi) ^ kswz(lr)) * 16);
+      ln.kl[kk] = base + lr * D * 2 + (((slice * (DS / 8) + 2 * kk + hi) ^ kswz(lr)) * 16);
     const int grp = lane >> 4, s = lane & 15;
     const int krow = 4 * (grp >> 1) + (s >> 2);     // key row inside a 16-key step
     const int dcol = 16 * (grp & 1) + 4 * (s & 3);  // head-dim column inside a 32-block
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int col = db * 32 + dcol;
+      const int col = slice * DS + db * 32 + dcol;
       ln.vl[db] = base + TILE_BYTES + krow * D * 2 + (((col >> 3) ^ vswz(krow)) * 16) + (col & 7) * 2;
     }
   }

@@ -288,8 +288,7 @@ def main():
         del src, dst
 
     if args.workload or args.all:
-        names = [args.workload] if args.workload else [
-            n for n, w in WORKLOADS.items() if not (w.kind == "prefill" and w.d > 256)]
+        names = [args.workload] if args.workload else list(WORKLOADS)
         for n in names:
             print(json.dumps(bench_one(n, args.steps, args.warmup, dev)), flush=True)
         return

@@ -89,7 +89,6 @@ PREFILL_BAD = [
     ("misaligned q", dict(q=FAKE + 2), 4),
     ("misaligned v", dict(v=FAKE + 8), 4),
     ("misaligned lse", dict(lse=FAKE + 2), 4),
-    ("d=512 not built", dict(d=512, q_ss=512, k_ss=512, v_ss=512, o_ss=512), 5),
 ]
 
 

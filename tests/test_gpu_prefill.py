@@ -59,6 +59,10 @@ SMALL = [
     (1, 2, 2, 1, 1, 128, False, 0, False),
     (1, 4, 4, 65, 65, 64, True, 1, False),      # window of one key: O = V on the diagonal
     (1, 32, 1, 130, 130, 128, True, 0, True),   # GQA ratio 32
+    (1, 2, 2, 200, 200, 512, False, 0, False),  # head dim 512: halves summed in logit space
+    (1, 4, 2, 257, 300, 512, True, 0, True),
+    (1, 2, 1, 150, 150, 512, True, 40, False),
+    (1, 2, 2, 70, 33, 512, True, 0, False),     # s_q > s_k
 ]
 
 
@@ -70,13 +74,13 @@ def test_prefill_small(case):
     check(out, lse, o_ref, l_ref, str(case))
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
 def test_prefill_strided_bshd(d):
     out, lse, o_ref, l_ref = run_case(2, 4, 2, 200, 200, d, causal=True, layout="bshd")
     check(out, lse, o_ref, l_ref, "bshd")
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
 def test_prefill_extreme_logits(d):
     # Q x 30: near one-hot attention rows stress the running-max rescale
     out, lse, o_ref, l_ref = run_case(1, 2, 2, 200, 333, d, causal=True, q_mul=30.0)
@@ -148,7 +152,7 @@ def test_prefill_shift_invariance_exact():
     assert abs(((l1 - l0) - 8.0 / math.sqrt(d)).abs().max().item()) <= 1e-3
 
 
-FULL = [n for n, w in WORKLOADS.items() if w.kind == "prefill" and w.d <= 256]
+FULL = [n for n, w in WORKLOADS.items() if w.kind == "prefill"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -165,7 +169,7 @@ def test_prefill_full_size_sampled(name):
     picks = set()
     for bi in {0, w.b - 1}:
         for h in {0, w.h_q - 1, int(rng.integers(w.h_q))}:
-            for i in {0, 1, 127, 128, w.s_q // 2, w.s_q - 2, w.s_q - 1, int(rng.integers(w.s_q))}:
+            for i in {0, 1, 63, 64, 127, 128, w.s_q // 2, w.s_q - 2, w.s_q - 1, int(rng.integers(w.s_q))}:
                 picks.add((bi, h, i))
     picks = sorted(picks)
     o_ref, l_ref = oracle_rows(inp["q"], inp["k"], inp["v"], scale, w.causal, w.window,
