@@ -15,10 +15,6 @@
 // logit space (S = S_0 + S_1) before any softmax; both waves then run the
 // same softmax and each multiplies P by its own 256 columns of V.
 //
-// Pipeline: two LDS stages.  At the top of iteration t the wave waits for its
-// own DMA loads of tile t and the workgroup barrier publishes the tile (and
-// guarantees every wave is done with tile t-1's stage); the loads of tile t+1
-// into the other stage are then issued and run under the MMAs of tile t.
 #pragma once
 
 #include "tile.hpp"
@@ -70,9 +66,6 @@ void prefill_kernel(PrefillParams p) {
 
   const uint16_t *kbase = p.k + bi * p.k_sb + g * p.k_sh;
   const uint16_t *vbase = p.v + bi * p.v_sb + g * p.v_sh;
-  typename T::Lane ln;
-  T::init_lane(ln, smem, p.k_ss, p.v_ss, wave, lane, slice);
-  if (t_begin < t_end) T::dma(ln, smem, kbase, p.k_ss, vbase, p.v_ss, t_begin * BN, p.s_k, wave);
 
   u32x4 qreg[T::NKK];
   {
@@ -91,25 +84,78 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) o[db] = f32x16{};
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int cur = (t - t_begin) & 1;
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (t + 1 < t_end)
-      T::dma(ln, smem + (cur ^ 1) * (T::STAGE_BYTES / 2), kbase, p.k_ss, vbase, p.v_ss, (t + 1) * BN,
-             p.s_k, wave);
+  // Does this wave's row block see any key of tile t, and must it be masked?
+  auto active = [&](int t) {
     const int j0 = t * BN;
-    const uint32_t stage_off = cur * T::STAGE_BYTES;
-    bool active = w_lo < p.s_q;
-    if (CAUSAL) active = active && j0 <= w_hi + off;
-    if (WINDOW) active = active && j0 + BN - 1 >= w_lo + off - p.window + 1;
-    if constexpr (SPLIT > 1) {
-      // Both waves of a pair take part in the exchange (and its barrier), so
-      // the pair's activity is decided together; inactive pairs skip the MMAs.
+    bool a = w_lo < p.s_q;
+    if (CAUSAL) a = a && j0 <= w_hi + off;
+    if (WINDOW) a = a && j0 + BN - 1 >= w_lo + off - p.window + 1;
+    return a;
+  };
+  auto mask = [&](f32x16 (&s)[T::NKB], int t) {
+    const int j0 = t * BN;
+    bool need = j0 + BN > p.s_k;
+    if (CAUSAL) need = need || (j0 + BN - 1 > w_lo + off);
+    if (WINDOW) need = need || (j0 < w_hi + off - p.window + 1);
+    if (need) {
+      const int lim_hi = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
+      const int lim_lo = WINDOW ? row + off - p.window + 1 : 0;
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = j0 + T::key_of(kb, i, hi);
+          if (j > lim_hi || j < lim_lo) s[kb][i] = kNegInf;
+        }
+    }
+  };
+
+  if constexpr (SPLIT == 1) {
+    // Two LDS stages of [K tile][V tile].  At the top of iteration t the
+    // wave waits for its own loads of tile t and the barrier publishes the
+    // tile (and guarantees every wave is done with tile t-1's stage); the loads
+    // of tile t+1 into the other stage then run under the MMAs of tile t.
+    typename T::Lane ln;
+    T::init_lane(ln, smem, p.k_ss, p.v_ss, wave, lane);
+    if (t_begin < t_end) T::dma(ln, smem, kbase, p.k_ss, vbase, p.v_ss, t_begin * BN, p.s_k, wave);
+    for (int t = t_begin; t < t_end; ++t) {
+      const int cur = (t - t_begin) & 1;
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (t + 1 < t_end)
+        T::dma(ln, smem + (cur ^ 1) * (T::STAGE_BYTES / 2), kbase, p.k_ss, vbase, p.v_ss, (t + 1) * BN,
+               p.s_k, wave);
+      const uint32_t stage_off = cur * T::STAGE_BYTES;
+      if (active(t)) {
+        f32x16 s[T::NKB];
+        T::scores(s, qreg, ln, stage_off);
+        mask(s, t);
+        u32x4 pk[T::NPV];
+        T::softmax_step(s, pk, o, m, l, p.c);
+        T::values(o, pk, ln, stage_off);
+      }
+    }
+  } else {
+    // Head dim split over wave pairs (no cross-tile pipelining): two LDS
+    // stages of [K tile][V tile].
+    typename T::Lane ln;
+    T::init_lane(ln, smem, p.k_ss, p.v_ss, wave, lane, slice);
+    if (t_begin < t_end) T::dma(ln, smem, kbase, p.k_ss, vbase, p.v_ss, t_begin * BN, p.s_k, wave);
+    for (int t = t_begin; t < t_end; ++t) {
+      const int cur = (t - t_begin) & 1;
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (t + 1 < t_end)
+        T::dma(ln, smem + (cur ^ 1) * (T::STAGE_BYTES / 2), kbase, p.k_ss, vbase, p.v_ss, (t + 1) * BN,
+               p.s_k, wave);
+      const uint32_t stage_off = cur * T::STAGE_BYTES;
+      const bool act = active(t);
+      // Both waves of a pair take part in the exchange (and its barrier); the
+      // pair's activity is decided together, inactive pairs skip the MMAs.
       f32x16 s[T::NKB];
-      if (active) T::scores(s, qreg, ln, stage_off);
+      if (act) T::scores(s, qreg, ln, stage_off);
       f32x4 *xb = reinterpret_cast<f32x4 *>(reinterpret_cast<char *>(smem) + 2 * T::STAGE_BYTES);
-      if (active) {
+      if (act) {
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
@@ -119,7 +165,7 @@ void prefill_kernel(PrefillParams p) {
           }
       }
       __syncthreads();
-      if (active) {
+      if (act) {
         const int partner = wave ^ 1;
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
@@ -131,44 +177,11 @@ void prefill_kernel(PrefillParams p) {
             s[kb][4 * q4 + 2] += v[2];
             s[kb][4 * q4 + 3] += v[3];
           }
-        bool need_mask = j0 + BN > p.s_k;
-        if (CAUSAL) need_mask = need_mask || (j0 + BN - 1 > w_lo + off);
-        if (WINDOW) need_mask = need_mask || (j0 < w_hi + off - p.window + 1);
-        if (need_mask) {
-          const int lim_hi = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
-          const int lim_lo = WINDOW ? row + off - p.window + 1 : 0;
-#pragma unroll
-          for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = j0 + T::key_of(kb, i, hi);
-              if (j > lim_hi || j < lim_lo) s[kb][i] = kNegInf;
-            }
-        }
+        mask(s, t);
         u32x4 pk[T::NPV];
         T::softmax_step(s, pk, o, m, l, p.c);
         T::values(o, pk, ln, stage_off);
       }
-    } else if (active) {
-      f32x16 s[T::NKB];
-      T::scores(s, qreg, ln, stage_off);
-      bool need_mask = j0 + BN > p.s_k;
-      if (CAUSAL) need_mask = need_mask || (j0 + BN - 1 > w_lo + off);
-      if (WINDOW) need_mask = need_mask || (j0 < w_hi + off - p.window + 1);
-      if (need_mask) {
-        const int lim_hi = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
-        const int lim_lo = WINDOW ? row + off - p.window + 1 : 0;
-#pragma unroll
-        for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = j0 + T::key_of(kb, i, hi);
-            if (j > lim_hi || j < lim_lo) s[kb][i] = kNegInf;
-          }
-      }
-      u32x4 pk[T::NPV];
-      T::softmax_step(s, pk, o, m, l, p.c);
-      T::values(o, pk, ln, stage_off);
     }
   }
 

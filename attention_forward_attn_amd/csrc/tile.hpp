@@ -134,11 +134,11 @@ struct Tile {
   static constexpr int TILE_ELEMS = BN * D;                // one K or V tile, bf16 elements
   static constexpr int TILE_BYTES = TILE_ELEMS * 2;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;       // K + V
-  static constexpr int LOADS = TILE_ELEMS / 8 / 64 / NW;   // 1-KiB DMA loads per wave per tile
+  static constexpr int LOADS_EXACT = TILE_ELEMS / 8 / 64 / NW;
+  static constexpr int LOADS = LOADS_EXACT > 0 ? LOADS_EXACT : 1;  // 1-KiB DMA loads per wave per tile
   static constexpr int ROWS_PER_256 = 256 / (2 * D) > 0 ? 256 / (2 * D) : 1;
   static constexpr float kLazy = 8.0f;  // log2 of the growth that forces a rescale
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(LOADS * 64 * NW * 8 == TILE_ELEMS, "tile must split into whole 1-KiB wave loads");
   static_assert(STAGE_BYTES <= 65536, "LDS immediate offsets must stay below 64 KiB");
 
   // Chunk swizzle for the score MMA's K reads: 16 lanes read one chunk of 16
@@ -156,9 +156,9 @@ struct Tile {
     uint32_t vl[NDB];               // LDS address of the V^T operand of head-dim block db, k-step 0
   };
 
-  __device__ static __forceinline__ void init_lane(Lane &ln, const uint16_t *smem, int64_t k_rs,
-                                                   int64_t v_rs, int w, int lane, int slice = 0) {
-    const int lr = lane & 31, hi = lane >> 5;
+  // DMA offsets: wave w of the NW loading waves, writing a BN x D tile.
+  __device__ static __forceinline__ void init_dma(Lane &ln, int64_t k_rs, int64_t v_rs, int w, int lane) {
+    static_assert(LOADS_EXACT * 64 * NW * 8 == TILE_ELEMS, "tile must split into whole 1-KiB wave loads");
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int pch = (u * NW + w) * 64 + lane;  // physical 16-byte chunk written by this lane
@@ -166,39 +166,66 @@ struct Tile {
       ln.kg[u] = (uint32_t)(r * k_rs * 2) + (uint32_t)(((pch % CH) ^ kswz(r)) * 16);
       ln.vg[u] = (uint32_t)(r * v_rs * 2) + (uint32_t)(((pch % CH) ^ vswz(r)) * 16);
     }
-    const uint32_t base = lds_offset(smem);
+  }
+
+  // MMA operand addresses for the K tile at LDS byte address kbase and the V
+  // tile at vbase (row-major, D columns, swizzled as above; the first row of
+  // each must sit at a multiple of 16 rows of its tile), head-dim slice `slice`.
+  __device__ static __forceinline__ void init_mma(Lane &ln, uint32_t kbase, uint32_t vbase, int lane,
+                                                  int slice = 0) {
+    const int lr = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      ln.kl[kk] = base + lr * D * 2 + (((slice * (DS / 8) + 2 * kk + hi) ^ kswz(lr)) * 16);
+      ln.kl[kk] = kbase + lr * D * 2 + (((slice * (DS / 8) + 2 * kk + hi) ^ kswz(lr)) * 16);
     const int grp = lane >> 4, s = lane & 15;
     const int krow = 4 * (grp >> 1) + (s >> 2);     // key row inside a 16-key step
     const int dcol = 16 * (grp & 1) + 4 * (s & 3);  // head-dim column inside a 32-block
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int col = slice * DS + db * 32 + dcol;
-      ln.vl[db] = base + TILE_BYTES + krow * D * 2 + (((col >> 3) ^ vswz(krow)) * 16) + (col & 7) * 2;
+      ln.vl[db] = vbase + krow * D * 2 + (((col >> 3) ^ vswz(krow)) * 16) + (col & 7) * 2;
     }
   }
 
-  // Issue this wave's share of the DMA loads of the K and V tiles that start
-  // at key j0 (< nkeys) into the given stage; rows at or past `nkeys` read as
-  // zero.  Byte offsets inside a tile must fit in 32 bits (row strides below
-  // 2^24 elements, checked by the host).
+  __device__ static __forceinline__ void init_lane(Lane &ln, const uint16_t *smem, int64_t k_rs,
+                                                   int64_t v_rs, int w, int lane, int slice = 0) {
+    init_dma(ln, k_rs, v_rs, w, lane);
+    const uint32_t base = lds_offset(smem);
+    init_mma(ln, base, base + TILE_BYTES, lane, slice);
+  }
+
+  // Issue this wave's share of the DMA loads of the BN-row tile of `base`
+  // (row stride rs) that starts at key j0, into the LDS tile at `dst`; rows at
+  // or past `nkeys` read as zero.  The descriptor ends exactly at the end of
+  // the last valid row; a tile entirely past the end gets an empty descriptor,
+  // so its loads touch no memory and only write zeros to LDS.  Byte offsets
+  // inside a tile must fit in 32 bits (row strides below 2^24 elements,
+  // checked by the host).
+  template <bool IS_V>
+  __device__ static __forceinline__ void dma1(const Lane &ln, uint16_t *dst, const uint16_t *base,
+                                              int64_t rs, int j0, int nkeys, int w) {
+    const int rows = min(nkeys - j0, BN);
+    const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * rs * 2 + D * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(rows > 0 ? base + j0 * rs : base, bytes);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (u * NW + w) * 512), 16,
+                                               IS_V ? ln.vg[u] : ln.kg[u], 0, 0, 0);
+  }
+  __device__ static __forceinline__ void dma_k(const Lane &ln, uint16_t *dst, const uint16_t *base,
+                                               int64_t rs, int j0, int nkeys, int w) {
+    dma1<false>(ln, dst, base, rs, j0, nkeys, w);
+  }
+  __device__ static __forceinline__ void dma_v(const Lane &ln, uint16_t *dst, const uint16_t *base,
+                                               int64_t rs, int j0, int nkeys, int w) {
+    dma1<true>(ln, dst, base, rs, j0, nkeys, w);
+  }
+  // K and V tiles of one key range into a stage laid out as [K tile][V tile].
   __device__ static __forceinline__ void dma(const Lane &ln, uint16_t *stage, const uint16_t *kbase,
                                              int64_t k_rs, const uint16_t *vbase, int64_t v_rs,
                                              int j0, int nkeys, int w) {
-    // The descriptor ends exactly at the end of the last valid row.
-    const int rows = min(nkeys - j0, BN);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + j0 * k_rs, (uint32_t)((rows - 1) * k_rs * 2 + D * 2));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + j0 * v_rs, (uint32_t)((rows - 1) * v_rs * 2 + D * 2));
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(stage + (u * NW + w) * 512), 16,
-                                               ln.kg[u], 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(stage + TILE_ELEMS + (u * NW + w) * 512),
-                                               16, ln.vg[u], 0, 0, 0);
+    dma1<false>(ln, stage, kbase, k_rs, j0, nkeys, w);
+    dma1<true>(ln, stage + TILE_ELEMS, vbase, v_rs, j0, nkeys, w);
   }
 
   // S^T block accumulators of this wave for the staged tile.  The K operands
@@ -212,27 +239,53 @@ struct Tile {
     if constexpr (NKB > 3) a[3] = ds_read_b128<3 * 32 * D * 2>(ad);
     static_assert(NKB <= 4, "at most 128 keys per tile");
   }
-  template <int KK>
+  struct NoHook {
+    template <int KK>
+    __device__ __forceinline__ void step() {}
+  };
+  // After the MMAs of k-step KK are issued, hook.step<KK>() runs: independent
+  // VALU work placed there overlaps the in-flight MMAs.  K operands are read
+  // two k-steps ahead of their MMAs (three register buffers rotate).
+  template <int KK, bool MMA, typename Hook>
   __device__ static __forceinline__ void score_steps(f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK],
-                                                     u32x4 (&cur)[NKB], u32x4 (&nxt)[NKB],
-                                                     const Lane &ln, uint32_t stage_off) {
-    if constexpr (KK + 1 < NKK) {
-      kreads<KK + 1>(nxt, ln, stage_off);
-      lds_wait<NKB>(cur);
-    } else {
-      lds_wait<0>(cur);
+                                                     u32x4 (&cur)[NKB], u32x4 (&nx1)[NKB], u32x4 (&nx2)[NKB],
+                                                     const Lane &ln, uint32_t stage_off, Hook &hook) {
+    if constexpr (MMA) {
+      if constexpr (KK + 2 < NKK) {
+        kreads<KK + 2>(nx2, ln, stage_off);
+        lds_wait<2 * NKB>(cur);
+      } else if constexpr (KK + 1 < NKK) {
+        lds_wait<NKB>(cur);
+      } else {
+        lds_wait<0>(cur);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(cur[kb], qreg[KK], s[kb]);
     }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(cur[kb], qreg[KK], s[kb]);
-    if constexpr (KK + 1 < NKK) score_steps<KK + 1>(s, qreg, nxt, cur, ln, stage_off);
+    hook.template step<KK>();
+    if constexpr (KK + 1 < NKK) score_steps<KK + 1, MMA>(s, qreg, nx1, nx2, cur, ln, stage_off, hook);
   }
+  // Score MMAs of one tile with a hook between k-steps (MMA = false runs the
+  // hook alone, for a tile this wave does not see).
+  template <typename Hook>
+  __device__ static __forceinline__ void scores_hooked(bool mma, f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK],
+                                                       const Lane &ln, uint32_t stage_off, Hook &hook) {
+    if (mma)
+      scores<true>(s, qreg, ln, stage_off, hook);
+    else
+      scores<false>(s, qreg, ln, stage_off, hook);
+  }
+  template <bool MMA = true, typename Hook = NoHook>
   __device__ static __forceinline__ void scores(f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK],
-                                                const Lane &ln, uint32_t stage_off) {
-    u32x4 a[NKB], b[NKB];
+                                                const Lane &ln, uint32_t stage_off, Hook &&hook = Hook{}) {
+    u32x4 a[NKB], b[NKB], c[NKB];
+    if constexpr (MMA) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-    kreads<0>(a, ln, stage_off);
-    score_steps<0>(s, qreg, a, b, ln, stage_off);
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+      kreads<0>(a, ln, stage_off);
+      if constexpr (NKK > 1) kreads<1>(b, ln, stage_off);
+    }
+    score_steps<0, MMA>(s, qreg, a, b, c, ln, stage_off, hook);
   }
 
   // O^T += V^T . P^T, one k-step of 16 keys at a time, with P packed bf16
@@ -254,10 +307,11 @@ struct Tile {
       v[2 * i + 1] = ds_read_tr16<OFF_HI>(ln.vl[G * VG + i] + stage_off);
     }
   }
-  template <int U>
+  // After the MMAs of the last unit of k-step T are issued, hook.vstep<T>() runs.
+  template <int U, typename Hook>
   __device__ static __forceinline__ void value_steps(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV],
                                                      u32x2 (&cur)[2 * VG], u32x2 (&nxt)[2 * VG],
-                                                     const Lane &ln, uint32_t stage_off) {
+                                                     const Lane &ln, uint32_t stage_off, Hook &hook) {
     constexpr int T_ = U / (NDB / VG), G = U % (NDB / VG);
     if constexpr (U + 1 < VUNITS) {
       vreads<U + 1>(nxt, ln, stage_off);
@@ -270,13 +324,19 @@ struct Tile {
       const u32x4 a = {cur[2 * i][0], cur[2 * i][1], cur[2 * i + 1][0], cur[2 * i + 1][1]};
       o[G * VG + i] = mfma32(a, pk[T_], o[G * VG + i]);
     }
-    if constexpr (U + 1 < VUNITS) value_steps<U + 1>(o, pk, nxt, cur, ln, stage_off);
+    if constexpr (G + 1 == NDB / VG) hook.template vstep<T_>();
+    if constexpr (U + 1 < VUNITS) value_steps<U + 1>(o, pk, nxt, cur, ln, stage_off, hook);
   }
+  struct NoVHook {
+    template <int T_>
+    __device__ __forceinline__ void vstep() {}
+  };
+  template <typename Hook = NoVHook>
   __device__ static __forceinline__ void values(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV],
-                                                const Lane &ln, uint32_t stage_off) {
+                                                const Lane &ln, uint32_t stage_off, Hook &&hook = Hook{}) {
     u32x2 a[2 * VG], b[2 * VG];
     vreads<0>(a, ln, stage_off);
-    value_steps<0>(o, pk, a, b, ln, stage_off);
+    value_steps<0>(o, pk, a, b, ln, stage_off, hook);
   }
 
   // Key index (relative to the tile start) held by accumulator register i of block kb.
@@ -284,16 +344,17 @@ struct Tile {
     return kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
   }
 
-  // One online-softmax step on this wave's scores (already masked to -inf).
-  // m is the exponent base in base-2 units, l this lane's partial row sum.
-  __device__ static __forceinline__ void softmax_step(f32x16 (&s)[NKB], u32x4 (&pk)[NPV],
-                                                      f32x16 (&o)[NDB], float &m, float &l,
-                                                      float c) {
-    float mx = kNegInf;
+  // Online-softmax update, first half: running max over this tile (scores
+  // already masked to -inf), lazy rescale of l and O; returns the exponent base.
+  __device__ static __forceinline__ float softmax_max(const f32x16 (&s)[NKB], f32x16 (&o)[NDB], float &m,
+                                                      float &l, float c) {
+    // four independent chains, then a small tree
+    float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], s[kb][i]);
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     mx = max_across_halves(mx) * c;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {  // wave-uniform
       const float m_new = fmaxf(m, mx);
@@ -303,21 +364,36 @@ struct Tile {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
-    const float base = (m == kNegInf) ? 0.0f : m;
+    return (m == kNegInf) ? 0.0f : m;
+  }
+  // Second half, for the 16 keys of value k-step T: numerators 2^(c*s - base)
+  // packed to bf16 into pk[T], their fp32 sum added to rs.
+  template <int T_>
+  __device__ static __forceinline__ void softmax_exp(const f32x16 (&s)[NKB], u32x4 (&pk)[NPV], float &rs,
+                                                     float c, float base) {
+    constexpr int kb = T_ >> 1, r0 = (T_ & 1) * 8;
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(s[kb][r0 + j], c, -base));
+    u32x4 x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = pack_bf16x2(e[2 * q], e[2 * q + 1]);
+    pk[T_] = x;
+    rs += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  }
+  template <int T_ = 0>
+  __device__ static __forceinline__ void softmax_exp_all(const f32x16 (&s)[NKB], u32x4 (&pk)[NPV], float &rs,
+                                                         float c, float base) {
+    softmax_exp<T_>(s, pk, rs, c, base);
+    if constexpr (T_ + 1 < NPV) softmax_exp_all<T_ + 1>(s, pk, rs, c, base);
+  }
+  // The whole update on one tile (no overlap with other work).
+  __device__ static __forceinline__ void softmax_step(f32x16 (&s)[NKB], u32x4 (&pk)[NPV],
+                                                      f32x16 (&o)[NDB], float &m, float &l,
+                                                      float c) {
+    const float base = softmax_max(s, o, m, l, c);
     float rs = 0.0f;
-#pragma unroll
-    for (int t = 0; t < NPV; ++t) {
-      const int kb = t >> 1, r0 = (t & 1) * 8;
-      u32x4 x;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float e0 = fast_exp2(fmaf(s[kb][r0 + 2 * q], c, -base));
-        const float e1 = fast_exp2(fmaf(s[kb][r0 + 2 * q + 1], c, -base));
-        rs += e0 + e1;
-        x[q] = pack_bf16x2(e0, e1);
-      }
-      pk[t] = x;
-    }
+    softmax_exp_all(s, pk, rs, c, base);
     l += rs;
   }
 };
