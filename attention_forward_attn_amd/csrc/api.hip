@@ -147,7 +147,7 @@ size_t attn_fwd_decode_workspace_size(int32_t B, int32_t h_q, int32_t d, int32_t
   if (B < 1 || h_q < 1 || d < 1 || max_kv_len < 0 || split_size < 64 || split_size % 64 != 0) return 0;
   const int64_t n_split = max_kv_len > 0 ? (max_kv_len + split_size - 1) / split_size : 1;
   const int64_t parts = (int64_t)B * h_q * n_split;
-  const int64_t o_bytes = parts * d * 4;
+  const int64_t o_bytes = parts * d * 2;  // bf16 partial outputs
   const int64_t o_aligned = (o_bytes + 255) / 256 * 256;
   return (size_t)(o_aligned + parts * 4);
 }
@@ -193,8 +193,8 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
     return fail(ATTN_ERR_SHAPE, "decode grid too large");
 
   const int64_t parts = (int64_t)a->B * a->h_q * n_split;
-  const int64_t o_bytes = parts * a->d * 4;
-  float *o_part = static_cast<float *>(workspace);
+  const int64_t o_bytes = parts * a->d * 2;
+  uint16_t *o_part = static_cast<uint16_t *>(workspace);
   float *lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + (o_bytes + 255) / 256 * 256);
 
   attn::DecodeParams p;
@@ -238,7 +238,7 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
   c.out_r2 = a->o_sh;
   c.lse_out_r1 = a->lse_sb;
   c.lse_out_r2 = 1;
-  e = attn::combine(c, s);
+  e = attn::combine_bf16(c, s);
   if (e != hipSuccess) return hip_fail(e, "decode combine launch");
   return ok();
 }

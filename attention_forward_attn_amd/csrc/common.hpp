@@ -42,7 +42,7 @@ struct DecodeParams {
   const int64_t *kv_start;
   const int32_t *kv_len;
   const float *sinks;
-  float *o_part;    // [B][h_q][n_split][D] fp32, normalised partial outputs
+  uint16_t *o_part;  // [B][h_q][n_split][D] bf16, normalised partial outputs
   float *lse_part;  // [B][h_q][n_split] fp32, natural-log LSE of each part
   int64_t q_sb, q_sh;
   int64_t k_st, k_sh;
@@ -56,7 +56,7 @@ struct DecodeParams {
 // Device-side parameters of the LSE-merge kernel.  Rows are addressed as
 // (r1, r2) with r2 < n2, so both flat rows (n2 = 1) and [B][h] rows work.
 struct CombineParams {
-  const float *o_parts;
+  const void *o_parts;  // fp32 (public entry point) or bf16 (decode partials)
   const float *lse_parts;
   uint16_t *o_out;
   float *lse_out;

@@ -6,7 +6,8 @@
 // heads of one kv group (all the heads of an MQA model), and every K/V tile is
 // read once from HBM and used by all of them (the DSV4 status page's
 // "head-packed MQA/GQA", row D2, with MQA as kv head stride 0).  Each split
-// covers a fixed run of keys; its normalised fp32 partial output and LSE are
+// covers a fixed run of keys; its normalised partial output (bf16) and LSE
+// (fp32) are
 // merged afterwards by the combine kernel (the LSE merge of the STAGE_D.md
 // page).  With one query row the bottom-right causal mask admits every cached
 // key, so only the tail of a split is masked.
@@ -26,8 +27,9 @@
 namespace attn {
 
 // HG head groups of 32 heads x KG key groups of BN/KG keys = HG*KG waves.
-template <int D, int HG, int KG, int BN, int STAGES>
-__global__ __launch_bounds__(HG * KG * 64) void decode_split_kernel(DecodeParams p) {
+template <int D, int HG, int KG, int BN, int STAGES, int OCC>
+__global__ __launch_bounds__(HG * KG * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void decode_split_kernel(DecodeParams p) {
   constexpr int NW = HG * KG;
   using TD = Tile<D, NW, BN>;       // DMA geometry: all waves load one BN-key tile
   using TC = Tile<D, NW, BN / KG>;  // MMA view: each wave computes on BN/KG keys of it
@@ -157,23 +159,26 @@ __global__ __launch_bounds__(HG * KG * 64) void decode_split_kernel(DecodeParams
   const float lt = sum_across_halves(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
-    float *op = p.o_part + part * D + 4 * hi;
+    // normalised partial output, bf16 (its rounding is far below the final
+    // bf16 rounding of O after the merge)
+    uint16_t *op = p.o_part + part * D + 4 * hi;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
-        f32x4 val = {o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv, o[db][4 * gi + 2] * inv,
-                     o[db][4 * gi + 3] * inv};
-        *reinterpret_cast<f32x4 *>(op + db * 32 + 8 * gi) = val;
+        u32x2 val;
+        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
+        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
+        *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
       }
     if (hi == 0) p.lse_part[part] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   }
 }
 
-template <int D, int HG, int KG, int BN, int STAGES>
+template <int D, int HG, int KG, int BN, int STAGES, int OCC>
 hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream) {
   dim3 grid(p.n_split, p.h_kv * p.n_hblk, p.B);
-  hipLaunchKernelGGL((decode_split_kernel<D, HG, KG, BN, STAGES>), grid, dim3(HG * KG * 64), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, HG, KG, BN, STAGES, OCC>), grid, dim3(HG * KG * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -20,6 +20,8 @@ hipError_t prefill_d512(const PrefillParams &p, int mask, int n_units, hipStream
 int decode_block_rows(int d);
 hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s);
 
+// LSE merge of fp32 partials (public entry point) / of bf16 partials (decode).
 hipError_t combine(const CombineParams &p, hipStream_t s);
+hipError_t combine_bf16(const CombineParams &p, hipStream_t s);
 
 }  // namespace attn

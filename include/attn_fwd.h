@@ -121,9 +121,11 @@ typedef struct {
  * split_size: keys per split (a multiple of 64, >= 64).  Split c of sequence
  *       bi covers keys [c*split_size, min((c+1)*split_size, kv_len[bi])).
  *
- * Two kernels run on `stream`: the split kernel writes normalised fp32
- * partial outputs and their LSE into the workspace, then the combine kernel
- * merges them into o and lse.  Supported: d in {64, 128, 256}; B, h_q, h_kv
+ * Two kernels run on `stream`: the split kernel writes normalised partial
+ * outputs (rounded to bf16) and their fp32 LSE into the workspace, then the
+ * combine kernel merges them in fp32 into o and lse.  The workspace is owned
+ * by the caller, must stay allocated until the stream has run both kernels,
+ * and must not be shared by calls that may overlap.  Supported: d in {64, 128, 256}; B, h_q, h_kv
  * >= 1, h_q % h_kv == 0.
  */
 typedef struct {

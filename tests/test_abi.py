@@ -159,8 +159,8 @@ def test_decode_workspace_checks():
     lib = afa.load_library()
     a = good_decode()
     need = lib.attn_fwd_decode_workspace_size(4, 128, 128, 8192, 512)
-    # 4 sequences x 128 heads x 16 splits x (128 fp32 outputs + 1 fp32 LSE)
-    assert need >= 4 * 128 * 16 * (128 + 1) * 4
+    # 4 sequences x 128 heads x 16 splits x (128 bf16 outputs + 1 fp32 LSE)
+    assert need >= 4 * 128 * 16 * (128 * 2 + 4)
     assert lib.attn_fwd_decode(ctypes.byref(a), None, need, None) == 6
     assert lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
     assert lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4
