@@ -3,6 +3,7 @@
 // HIP call, so a rejected call has no side effect.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -189,8 +190,8 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
   const int ratio = a->h_q / a->h_kv;
   const int64_t n_split = a->max_kv_len > 0 ? (a->max_kv_len + a->split_size - 1) / a->split_size : 1;
   const int64_t n_hblk = (ratio + bm - 1) / bm;
-  if (n_split > 65535 || (int64_t)a->h_kv * n_hblk > 65535 || a->B > 65535)
-    return fail(ATTN_ERR_SHAPE, "decode grid too large");
+  if (n_split * a->B * a->h_kv * n_hblk > INT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "decode grid too large: splits x B x kv heads x head blocks must fit in int32");
 
   const int64_t parts = (int64_t)a->B * a->h_q * n_split;
   const int64_t o_bytes = parts * a->d * 2;
@@ -238,6 +239,8 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
   c.out_r2 = a->o_sh;
   c.lse_out_r1 = a->lse_sb;
   c.lse_out_r2 = 1;
+  c.kv_len = a->kv_len;
+  c.split = a->split_size;
   e = attn::combine_bf16(c, s);
   if (e != hipSuccess) return hip_fail(e, "decode combine launch");
   return ok();
@@ -259,6 +262,8 @@ attn_status attn_combine(const attn_combine_args *a, void *stream) {
   if (!bf16_stride_ok(a->o_out_row_stride)) return fail(ATTN_ERR_STRIDE, "o_out_row_stride must be a non-negative multiple of 8");
 
   attn::CombineParams c;
+  c.kv_len = nullptr;  // every row merges all n_parts
+  c.split = 0;
   c.o_parts = a->o_parts;
   c.lse_parts = a->lse_parts;
   c.o_out = static_cast<uint16_t *>(a->o_out);

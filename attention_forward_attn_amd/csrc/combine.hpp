@@ -6,8 +6,8 @@
 // LSE is -inf carry no weight and their O is never read, so a split that saw
 // no key may leave its partial output unwritten.
 //
-// One thread per 8 consecutive output columns of a row: the part loop reads
-// one 16-byte (bf16) or 32-byte (fp32) vector per part, four parts at a time.
+// One thread per 8 consecutive output columns of a row: each part gives it
+// one 16-byte (bf16) or 32-byte (fp32) vector.
 #pragma once
 
 #include "common.hpp"
@@ -32,8 +32,12 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float (&v)[8]
   }
 }
 
+// Parts are taken PB at a time: all their LSEs and partial outputs are
+// loaded before any is used, and the running (max, weight sum, accumulator)
+// is rescaled once per batch to the batch's new maximum.
 template <typename PT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  constexpr int PB = 8;
   const int cpr = p.d / 8;  // 8-column chunks per row
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= (int64_t)p.rows * cpr) return;
@@ -41,42 +45,41 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int r1 = row / p.n2, r2 = row - r1 * p.n2;
   const float *lp = p.lse_parts + r1 * p.lse_r1 + r2 * p.lse_r2;
   const PT *op = reinterpret_cast<const PT *>(p.o_parts) + r1 * p.o_r1 + r2 * p.o_r2 + ch * 8;
+  int n = p.n_parts;
+  if (p.kv_len != nullptr) {
+    const int L = p.kv_len[r1];
+    n = min(n, L > 0 ? (L - 1) / p.split + 1 : 1);
+  }
 
-  float mx = kNegInf;
-  for (int i = 0; i < p.n_parts; ++i) mx = fmaxf(mx, lp[i * p.lse_part_stride]);
-
-  uint16_t *out = p.o_out + r1 * p.out_r1 + r2 * p.out_r2 + ch * 8;
+  float mx = kNegInf, wsum = 0.0f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.0f;
-  if (mx != kNegInf) {
-    int i = 0;
-    for (; i + 4 <= p.n_parts; i += 4) {
-      float li[4], v[4][8];
+  for (int i = 0; i < n; i += PB) {
+    float li[PB], v[PB][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) li[u] = lp[(i + u) * p.lse_part_stride];
+    for (int u = 0; u < PB; ++u) li[u] = i + u < n ? lp[(i + u) * p.lse_part_stride] : kNegInf;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (li[u] != kNegInf) load8<PT>(op + (int64_t)(i + u) * p.o_part_stride, v[u]);
+    for (int u = 0; u < PB; ++u)
+      if (li[u] != kNegInf) load8<PT>(op + (int64_t)(i + u) * p.o_part_stride, v[u]);
+    float bm = li[0];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (li[u] == kNegInf) continue;
-        const float wgt = __expf(li[u] - mx);
-        wsum += wgt;
+    for (int u = 1; u < PB; ++u) bm = fmaxf(bm, li[u]);
+    if (bm == kNegInf) continue;
+    const float nm = fmaxf(mx, bm);
+    const float sc = mx == kNegInf ? 0.0f : __expf(mx - nm);
+    wsum *= sc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += wgt * v[u][e];
-      }
-    }
-    for (; i < p.n_parts; ++i) {
-      const float li = lp[i * p.lse_part_stride];
-      if (li == kNegInf) continue;
-      float v[8];
-      load8<PT>(op + (int64_t)i * p.o_part_stride, v);
-      const float wgt = __expf(li - mx);
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      if (li[u] == kNegInf) continue;
+      const float wgt = __expf(li[u] - nm);
       wsum += wgt;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wgt * v[e];
+      for (int e = 0; e < 8; ++e) acc[e] += wgt * v[u][e];
     }
+    mx = nm;
   }
+  uint16_t *out = p.o_out + r1 * p.out_r1 + r2 * p.out_r2 + ch * 8;
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
   u32x4 res;
 #pragma unroll

@@ -65,6 +65,10 @@ struct CombineParams {
   int64_t lse_part_stride, lse_r1, lse_r2;
   int64_t out_r1, out_r2;
   int64_t lse_out_r1, lse_out_r2;
+  // Decode: parts of row (r1, r2) are the splits of sequence r1 that hold
+  // keys, min(n_parts, max(1, ceil(kv_len[r1] / split))); NULL = all n_parts.
+  const int32_t *kv_len;
+  int32_t split;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

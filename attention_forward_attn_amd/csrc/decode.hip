@@ -9,8 +9,8 @@ int decode_block_rows(int d) { return (d == 64 || d == 128 || d == 256) ? 128 : 
 
 hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s) {
   switch (d) {
-    case 64: return launch_decode_split<64, 4, 1, 64, 2, 2>(p, s);
-    case 128: return launch_decode_split<128, 4, 1, 32, 2, 2>(p, s);
+    case 64: return launch_decode_split<64, 4, 1, 64, 2, 4>(p, s);
+    case 128: return launch_decode_split<128, 4, 1, 32, 2, 3>(p, s);
     default: return launch_decode_split<256, 4, 1, 32, 2, 1>(p, s);
   }
 }

@@ -1,4 +1,5 @@
-// Split-KV decode: one workgroup per (key split, kv head, head block, sequence).
+// Split-KV decode: one workgroup per unit (key split, sequence, kv head, head
+// block).
 //
 // A decode step has one query token per sequence, so a single sequence gives
 // an MMA only one row -- unless the query heads that share a kv head are
@@ -7,24 +8,86 @@
 // read once from HBM and used by all of them (the DSV4 status page's
 // "head-packed MQA/GQA", row D2, with MQA as kv head stride 0).  Each split
 // covers a fixed run of keys; its normalised partial output (bf16) and LSE
-// (fp32) are
-// merged afterwards by the combine kernel (the LSE merge of the STAGE_D.md
-// page).  With one query row the bottom-right causal mask admits every cached
-// key, so only the tail of a split is masked.
+// (fp32) are merged afterwards by the combine kernel (the LSE merge of the
+// STAGE_D.md page).  With one query row the bottom-right causal mask admits
+// every cached key, so only the tail of a split is masked.
+//
+// Work placement.  Sequence lengths live on the device, so the grid is sized
+// for max_kv_len and every workgroup first works out which unit it owns: the
+// units that hold keys are numbered split-major (split 0 of every sequence,
+// then split 1 of every sequence that reaches it, ...) and workgroup u takes
+// unit u; workgroups past the last unit exit at once.  Consecutive workgroups
+// are dispatched to consecutive XCDs, so this numbering hands every XCD the
+// same number of units, and the same number of full 512-key splits up to one
+// per split level -- with lengths spread over a range, numbering units per
+// sequence instead leaves some XCDs with twice the bytes of others.  Empty
+// splits never launch; the combine kernel reads only the splits a sequence
+// has.
 //
 // Decode streams K/V once, so the kernel is built to keep bytes in flight:
-// 8 waves = 4 head groups x 2 key groups (each wave takes 32 of the 64 keys of
-// every tile, with its own running max/sum/O), and an LDS ring of STAGES tiles
-// of which STAGES-1 are being loaded while one is consumed.  Every iteration
-// issues exactly one tile's loads (tiles past the end get an empty buffer
-// descriptor and load nothing), so the wait count is a constant.  At the end
-// the two key groups of each head group are merged in LDS by their running
-// maxima, exactly like two disjoint key sets.
+// an LDS ring of STAGES tiles of which STAGES-1 are being loaded while one is
+// consumed.  Every iteration issues exactly one tile's loads (tiles past the
+// end get an empty buffer descriptor and load nothing), so the wait count is a
+// constant.  With KG = 2 key groups, each wave takes half the keys of every
+// tile with its own running max/sum/O, and at the end the two key groups of
+// each head group are merged in LDS by their running maxima, exactly like two
+// disjoint key sets.
 #pragma once
 
 #include "tile.hpp"
 
 namespace attn {
+
+// Splits of sequence b that form a unit: one per started chunk of keys, and
+// split 0 even for an empty sequence (it carries the sink and the -inf LSE).
+// Lengths beyond max_kv_len are clamped to the splits the grid was sized for.
+__device__ __forceinline__ int decode_splits_of(const int32_t *kv_len, int split, int n_split, int b) {
+  const int L = kv_len[b];
+  const int n = L > 0 ? (L - 1) / split + 1 : 1;
+  return min(n, n_split);
+}
+
+// Unit u of the split-major numbering: (split, sequence, kv-group/head-block
+// index y).  Returns false past the last unit.  Every lane of the wave gets
+// the same answer.  The scan walks the split levels with one ballot per level
+// and per 64 sequences; it stops at u's level, so it is short for the early
+// (full) units and at most n_split levels long.
+__device__ bool decode_unit(const DecodeParams &p, int u, int lane, int &split, int &bi, int &y) {
+  const int ny = p.h_kv * p.n_hblk;
+  const int q = u / ny;
+  y = u - q * ny;
+  const int nb0 = lane < p.B ? decode_splits_of(p.kv_len, p.split, p.n_split, lane) : 0;
+  auto count_above = [&](int s) {  // sequences with more than s splits
+    int c = __popcll(__ballot(nb0 > s));
+    for (int b0 = 64; b0 < p.B; b0 += 64) {
+      const bool has = b0 + lane < p.B && decode_splits_of(p.kv_len, p.split, p.n_split, b0 + lane) > s;
+      c += __popcll(__ballot(has));
+    }
+    return c;
+  };
+  int r = q;  // rank of the unit within its split level
+  int s = 0;
+  for (;; ++s) {
+    if (s >= p.n_split) return false;
+    const int c = count_above(s);
+    if (r < c) break;
+    r -= c;
+  }
+  split = s;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int b = b0 + lane;
+    const bool has = b < p.B && (b0 == 0 ? nb0 : decode_splits_of(p.kv_len, p.split, p.n_split, b)) > s;
+    const uint64_t m = __ballot(has);
+    const int cnt = __popcll(m);
+    if (r < cnt) {
+      const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      bi = b0 + __builtin_ctzll(__ballot(has && pre == r));
+      return true;
+    }
+    r -= cnt;
+  }
+  return false;  // not reached: r is below the count of level s
+}
 
 // HG head groups of 32 heads x KG key groups of BN/KG keys = HG*KG waves.
 template <int D, int HG, int KG, int BN, int STAGES, int OCC>
@@ -45,9 +108,12 @@ void decode_split_kernel(DecodeParams p) {
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, hi = lane >> 5;
   const int hgrp = wave % HG, kgrp = wave / HG;
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / p.n_hblk, hb = blockIdx.y - g * p.n_hblk;
-  const int bi = blockIdx.z;
+  int split_, bi_, y_;
+  if (!decode_unit(p, blockIdx.x, lane, split_, bi_, y_)) return;
+  const int split = __builtin_amdgcn_readfirstlane(split_);
+  const int bi = __builtin_amdgcn_readfirstlane(bi_);
+  const int y = __builtin_amdgcn_readfirstlane(y_);
+  const int g = y / p.n_hblk, hb = y - g * p.n_hblk;
   const int L = p.kv_len[bi];
   const int kbeg = split * p.split;
   const int kend = min(kbeg + p.split, L);
@@ -56,11 +122,6 @@ void decode_split_kernel(DecodeParams p) {
   const bool row_ok = hig < p.ratio;
   const int head = g * p.ratio + min(hig, p.ratio - 1);
   const int64_t part = ((int64_t)bi * p.h_q + head) * p.n_split + split;
-
-  if (kbeg >= kend && split != 0) {  // nothing in this split: zero weight in the merge
-    if (row_ok && hi == 0 && kgrp == 0) p.lse_part[part] = kNegInf;
-    return;
-  }
 
   const int64_t start = p.kv_start[bi];
   const uint16_t *kbase = p.k + (start + kbeg) * p.k_st + g * p.k_sh;
@@ -177,7 +238,7 @@ void decode_split_kernel(DecodeParams p) {
 
 template <int D, int HG, int KG, int BN, int STAGES, int OCC>
 hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream) {
-  dim3 grid(p.n_split, p.h_kv * p.n_hblk, p.B);
+  dim3 grid((unsigned)((int64_t)p.n_split * p.B * p.h_kv * p.n_hblk));
   hipLaunchKernelGGL((decode_split_kernel<D, HG, KG, BN, STAGES, OCC>), grid, dim3(HG * KG * 64), 0, stream, p);
   return hipGetLastError();
 }

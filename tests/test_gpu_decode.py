@@ -78,6 +78,23 @@ def test_decode_head_stride_zero_matches_mqa():
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
 
 
+@pytest.mark.parametrize("B,h_q,h_kv,d,split", [(70, 16, 2, 128, 256), (133, 8, 1, 64, 128),
+                                                (65, 32, 1, 256, 512)])
+def test_decode_many_sequences(B, h_q, h_kv, d, split):
+    # more sequences than a wave has lanes, empty sequences, and a max_kv_len
+    # above every length (trailing splits hold no keys)
+    print(f"decode many sequences B={B} h_q={h_q} h_kv={h_kv} d={d} split={split}", flush=True)
+    rng = np.random.default_rng(B)
+    lens = rng.integers(0, 1300, size=B)
+    lens[::7] = 0
+    lens[1] = split
+    inp = make(B, h_q, h_kv, d, lens.tolist(), 24)
+    out, lse = run_decode(inp, 2048, split)
+    o_ref, l_ref = oracle.decode_ref(inp["q"], inp["k"], inp["v"], inp["kv_start"], inp["kv_len"],
+                                     1 / math.sqrt(d))
+    check(out, lse, o_ref, l_ref, f"B={B}")
+
+
 def test_decode_split_size_invariance():
     inp = make(4, 128, 1, 128, [1500, 3000, 64, 2049], 23)
     o1, l1 = run_decode(inp, 3000, 512)
