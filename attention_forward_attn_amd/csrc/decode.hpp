@@ -159,7 +159,7 @@ void decode_split_kernel(DecodeParams p) {
 
   for (int t = 0; t < n_tiles; ++t) {
     wait_vmcnt<(STAGES - 2) * 2 * TD::LOADS>();  // this wave's loads of tile t have landed
-    __syncthreads();                              // everyone's have; tile t-1's stage is free
+    barrier_nofence();                            // everyone's have; tile t-1's stage is free
     const int nxt = t + STAGES - 1;
     TD::dma(dl, smem + (nxt % STAGES) * (TD::STAGE_BYTES / 2), kbase, p.k_st, vbase, p.v_st, nxt * BN,
             n_keys, wave);

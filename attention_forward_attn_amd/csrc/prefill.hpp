@@ -21,6 +21,42 @@
 
 namespace attn {
 
+// Work unit of workgroup v: (batch x query head bh, query tile qt).
+// Workgroups are dealt round-robin to the 8 XCDs (v % 8).  When the kv heads
+// divide evenly, every query head of kv head bkv is placed on XCD bkv % 8, so
+// the query tiles and heads that read the same K/V share one L2.  The order
+// inside an XCD depends on the mask: with a plain causal mask (LONGEST_FIRST)
+// the later query tiles see the most keys, so units go out in levels of
+// decreasing qt and the short ones fill in behind the long ones; otherwise
+// all units are alike and one head's query tiles run together, which keeps
+// the K/V working set of an XCD to a few heads.
+template <bool LONGEST_FIRST>
+__device__ __forceinline__ void prefill_unit(const PrefillParams &p, int v, int &bh, int &qt) {
+  const int BH = p.b * p.h_q;
+  const int nq = p.n_qtiles;
+  if (((p.b * p.h_kv) & 7) == 0) {
+    const int xcd = v & 7, slot = v >> 3;  // slot inside the XCD's (BH / 8) x nq units
+    int j;                                 // head index inside the XCD
+    if (LONGEST_FIRST) {
+      const int level = slot / (BH >> 3);
+      j = slot - level * (BH >> 3);
+      qt = nq - 1 - level;
+    } else {
+      j = slot / nq;
+      qt = nq - 1 - (slot - j * nq);
+    }
+    const int bkv = xcd + 8 * (j / p.ratio);
+    bh = bkv * p.ratio + (j - (j / p.ratio) * p.ratio);
+  } else if (LONGEST_FIRST) {
+    const int level = v / BH;
+    bh = v - level * BH;
+    qt = nq - 1 - level;
+  } else {
+    bh = v / nq;
+    qt = nq - 1 - (v - bh * nq);
+  }
+}
+
 template <int D, int NW, int BN, bool CAUSAL, bool WINDOW, int OCC, int DS = D>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void prefill_kernel(PrefillParams p) {
@@ -35,15 +71,8 @@ void prefill_kernel(PrefillParams p) {
   const int w = wave / SPLIT;      // row block of this wave
   const int slice = wave % SPLIT;  // head-dim slice of this wave
 
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
-  // range of work units so that the query tiles sharing one head's K/V run on
-  // the same L2.  Inside a head, the longest (last) query tiles go first.
-  const int n_units = gridDim.x;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int per = n_units >> 3, rem = n_units & 7;
-  const int unit = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int bh = unit / p.n_qtiles;
-  const int qt = p.n_qtiles - 1 - (unit - bh * p.n_qtiles);
+  int bh, qt;
+  prefill_unit<CAUSAL && !WINDOW>(p, blockIdx.x, bh, qt);
   const int bi = bh / p.h_q, h = bh - bi * p.h_q;
   const int g = h / p.ratio;
   const int q0 = qt * BM;
@@ -202,6 +231,191 @@ void prefill_kernel(PrefillParams p) {
     if (p.lse != nullptr && hi == 0 && slice == 0)
       p.lse[bi * p.lse_sb + h * p.lse_sh + row] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   }
+}
+
+// Ping-pong prefill (SPLIT == 1 head dims): 8 waves in two groups of 4 that
+// share every staged K/V tile.  Waves w and w+4 run on the same SIMD, so the
+// two groups can take turns: while one group runs its MMAs (the value MMA of
+// the previous tile and the score MMA of the current one), the other runs the
+// softmax of its current tile on the vector ALU, and at every workgroup
+// barrier they swap.  Group 1 runs half an iteration behind group 0:
+//
+//   phase A_i:  group 0: P(i-1).V(i-1), S(i) = K(i).Q   group 1: softmax(i-1)
+//   phase B_i:  group 0: softmax(i)                     group 1: P(i-1).V(i-1), S(i)
+//
+// Row blocks are interleaved between the groups (group g owns blocks g, g+2,
+// g+4, g+6 of the 256-row query tile) so that both see nearly the same causal
+// and window extents.  A ring of STAGES LDS stages holds [K tile][V tile];
+// tile i is last read by group 1's value MMA in phase B_{i+1}, so the loads
+// of tile i+STAGES-2 go into the stage of tile i-2 once barrier A_i has
+// passed, and have a full iteration or more to land.  Every wave issues its
+// loads and its softmax in the phase where it runs no MMA, and the value
+// operands of a tile are read ahead across the barrier that opens the MMA
+// phase, so that phase is mostly MMA issue.
+template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_pp_kernel(PrefillParams p) {
+  using T = Tile<D, 8, BN>;
+  constexpr int BM = T::BM;
+  static_assert(T::SPLIT == 1 && BM == 256 && STAGES >= 3, "ping-pong shape");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * T::STAGE_BYTES / 2];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
+  const int grp = wave >> 2;
+  const int rb = 2 * (wave & 3) + grp;  // 32-row block of this wave inside the query tile
+
+  int bh, qt;
+  prefill_unit<CAUSAL && !WINDOW>(p, blockIdx.x, bh, qt);
+  const int bi = bh / p.h_q, h = bh - bi * p.h_q;
+  const int g = h / p.ratio;
+  const int q0 = qt * BM;
+  const int off = p.s_k - p.s_q;
+
+  const int i_last = min(p.s_q, q0 + BM) - 1;
+  int kend = p.s_k;
+  if (CAUSAL) kend = max(0, min(kend, i_last + off + 1));
+  int kbeg = 0;
+  if (WINDOW) kbeg = max(0, q0 + off - p.window + 1);
+  const int t_begin = kbeg / BN;
+  const int t_end = kbeg < kend ? (kend + BN - 1) / BN : t_begin;
+  const int nt = t_end - t_begin;
+  const int lim = min(p.s_k, t_end * BN);  // keys loaded: tiles at or past t_end stay empty
+
+  const int w_lo = q0 + rb * 32;
+  const int w_hi = min(w_lo + 31, p.s_q - 1);
+  const int row = w_lo + (lane & 31);
+  const bool row_ok = row < p.s_q;
+
+  const uint16_t *kbase = p.k + bi * p.k_sb + g * p.k_sh;
+  const uint16_t *vbase = p.v + bi * p.v_sb + g * p.v_sh;
+
+  typename T::Lane ln;
+  T::init_lane(ln, smem, p.k_ss, p.v_ss, wave, lane);
+#pragma unroll
+  for (int s = 0; s < STAGES - 2; ++s)
+    T::dma(ln, smem + s * (T::STAGE_BYTES / 2), kbase, p.k_ss, vbase, p.v_ss, (t_begin + s) * BN, lim, wave);
+
+  u32x4 qreg[T::NKK];
+  {
+    const uint16_t *qp = p.q + bi * p.q_sb + h * p.q_sh + (int64_t)min(row, p.s_q - 1) * p.q_ss + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < T::NKK; ++kk) qreg[kk] = *reinterpret_cast<const u32x4 *>(qp + kk * 16);
+  }
+
+  float m = kNegInf, l = 0.0f;
+  if (p.sinks != nullptr) {
+    m = p.sinks[h] * kLog2e;
+    l = hi == 0 ? 1.0f : 0.0f;
+  }
+  f32x16 o[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) o[db] = f32x16{};
+
+  auto active = [&](int t) {
+    const int j0 = t * BN;
+    bool a = w_lo < p.s_q;
+    if (CAUSAL) a = a && j0 <= w_hi + off;
+    if (WINDOW) a = a && j0 + BN - 1 >= w_lo + off - p.window + 1;
+    return a;
+  };
+  auto mask = [&](f32x16 (&s)[T::NKB], int t) {
+    const int j0 = t * BN;
+    bool need = j0 + BN > p.s_k;
+    if (CAUSAL) need = need || (j0 + BN - 1 > w_lo + off);
+    if (WINDOW) need = need || (j0 < w_hi + off - p.window + 1);
+    if (need) {
+      const int lim_hi = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
+      const int lim_lo = WINDOW ? row + off - p.window + 1 : 0;
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = j0 + T::key_of(kb, i, hi);
+          if (j > lim_hi || j < lim_lo) s[kb][i] = kNegInf;
+        }
+    }
+  };
+
+  f32x16 s[T::NKB];
+  u32x4 pk[T::NPV];
+  u32x2 vpre[2 * T::VG];  // value operands of unit 0, read ahead across the barrier
+  // MMA phase of iteration i: value MMA of tile i-1 (its first operands are
+  // already in flight) fused with the score MMA of tile i.  The wave raises
+  // its issue priority so that the other group's softmax fills the gaps
+  // between its MMAs rather than the other way round.
+  auto mma_phase = [&](int i) {
+    const bool pv = i > 0 && active(t_begin + i - 1);
+    const bool sc = i < nt && active(t_begin + i);
+    const uint32_t v_off = ((i + STAGES - 1) % STAGES) * T::STAGE_BYTES;
+    const uint32_t k_off = (i % STAGES) * T::STAGE_BYTES;
+    __builtin_amdgcn_s_setprio(1);
+    if (pv && sc) T::pv_scores(o, pk, s, qreg, vpre, ln, v_off, k_off);
+    else if (pv) T::values_from(o, pk, vpre, ln, v_off);
+    else if (sc) T::scores(s, qreg, ln, k_off);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Softmax of tile i, which ends by reading the first value operands of
+  // tile i for the next MMA phase.
+  auto softmax_phase = [&](int i) {
+    if (i >= 0 && active(t_begin + i)) {
+      mask(s, t_begin + i);
+      T::softmax_step(s, pk, o, m, l, p.c);
+      T::values_issue0(vpre, ln, (i % STAGES) * T::STAGE_BYTES);
+    }
+  };
+  // This wave's share of the loads of tile i+STAGES-2, into the stage of tile
+  // i-2 (free once barrier A_i has passed).  Each group issues it at the start
+  // of its softmax phase after A_i: group 1 in A_i, group 0 in B_i.  Before
+  // A_{i+1} a wave then has exactly one later tile in flight.
+  auto load_ahead = [&](int i) {
+    T::dma(ln, smem + ((i + STAGES - 2) % STAGES) * (T::STAGE_BYTES / 2), kbase, p.k_ss, vbase, p.v_ss,
+           (t_begin + i + STAGES - 2) * BN, lim, wave);
+  };
+
+  if (nt > 0) {
+    for (int i = 0; i <= nt; ++i) {
+      wait_vmcnt<(STAGES - 3) * 2 * T::LOADS>();  // this wave's loads of tile i have landed
+      barrier_nofence();                           // A_i: tile i published, tile i-2's stage free
+      if (grp == 0) {
+        mma_phase(i);
+      } else {
+        load_ahead(i);
+        if (i > 0) softmax_phase(i - 1);
+      }
+      barrier_nofence();  // B_i
+      if (grp == 0) {
+        load_ahead(i);
+        if (i < nt) softmax_phase(i);
+      } else {
+        mma_phase(i);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+
+  const float lt = sum_across_halves(l);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (row_ok) {
+    uint16_t *op = p.o + bi * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        u32x2 val;
+        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
+        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
+        *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
+      }
+    if (p.lse != nullptr && hi == 0)
+      p.lse[bi * p.lse_sb + h * p.lse_sh + row] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>
+hipError_t launch_prefill_pp(const PrefillParams &p, int n_units, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_pp_kernel<D, BN, CAUSAL, WINDOW, STAGES>), dim3(n_units), dim3(512), 0, stream, p);
+  return hipGetLastError();
 }
 
 // Host-side launcher of one instantiation.

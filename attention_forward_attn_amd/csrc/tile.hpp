@@ -61,6 +61,14 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup barrier without __syncthreads' memory fence.  The tile loops
+// publish LDS data only through direct-to-LDS loads, whose completion every
+// wave awaits itself (wait_vmcnt) before the barrier, and every LDS read of a
+// stage is consumed by an MMA (so it has completed) before the barrier that
+// frees the stage.  The fence would add a wait for all outstanding loads,
+// including the prefetch of later tiles.
+__device__ __forceinline__ void barrier_nofence() { __builtin_amdgcn_s_barrier(); }
+
 // 32-bit LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   const __attribute__((address_space(3))) char *q = (const __attribute__((address_space(3))) char *)p;
@@ -287,6 +295,25 @@ struct Tile {
     }
     score_steps<0, MMA>(s, qreg, a, b, c, ln, stage_off, hook);
   }
+  // The score MMAs in two halves, so that other work (the value MMA of the
+  // previous tile) can run while the first K operands are in flight:
+  // scores_issue reads the operands of k-steps 0 and 1 into a and b,
+  // scores_run later runs all k-steps from them.
+  struct KPre {
+    u32x4 a[NKB], b[NKB];
+  };
+  __device__ static __forceinline__ void scores_issue(KPre &pre, const Lane &ln, uint32_t stage_off) {
+    kreads<0>(pre.a, ln, stage_off);
+    if constexpr (NKK > 1) kreads<1>(pre.b, ln, stage_off);
+  }
+  __device__ static __forceinline__ void scores_run(f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK], KPre &pre,
+                                                    const Lane &ln, uint32_t stage_off) {
+    u32x4 c[NKB];
+    NoHook hook;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    score_steps<0, true>(s, qreg, pre.a, pre.b, c, ln, stage_off, hook);
+  }
 
   // O^T += V^T . P^T, one k-step of 16 keys at a time, with P packed bf16
   // (8 keys per lane).  The k-slot order of P (8*hi + j <-> key
@@ -337,6 +364,67 @@ struct Tile {
     u32x2 a[2 * VG], b[2 * VG];
     vreads<0>(a, ln, stage_off);
     value_steps<0>(o, pk, a, b, ln, stage_off, hook);
+  }
+  // values() with the reads of unit 0 already issued into vpre.
+  __device__ static __forceinline__ void values_from(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV],
+                                                     u32x2 (&vpre)[2 * VG], const Lane &ln, uint32_t stage_off) {
+    u32x2 b[2 * VG];
+    NoVHook hook;
+    value_steps<0>(o, pk, vpre, b, ln, stage_off, hook);
+  }
+
+  // Value MMA of one tile interleaved with the score MMA of the next, for the
+  // ping-pong prefill: value unit u (4 MMAs over one 16-key step) alternates
+  // with score k-steps 2u and 2u+1, and every operand group is read one group
+  // ahead, so each LDS read has the MMAs of two groups to land while at most
+  // 12 reads are in flight.  The reads of value unit 0 (vpre) are issued by
+  // the caller before the workgroup barrier that opens the phase.
+  static constexpr bool PV_S_FUSED = (VUNITS * 2 == NKK) && (VG == NDB);
+  __device__ static __forceinline__ void values_issue0(u32x2 (&vpre)[2 * VG], const Lane &ln, uint32_t v_off) {
+    vreads<0>(vpre, ln, v_off);
+  }
+  template <int U>
+  __device__ static __forceinline__ void pv_s_step(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV], f32x16 (&s)[NKB],
+                                                   const u32x4 (&qreg)[NKK], u32x2 (&vcur)[2 * VG],
+                                                   u32x2 (&vnxt)[2 * VG], u32x4 (&kcur)[2][NKB],
+                                                   u32x4 (&knxt)[2][NKB], const Lane &ln, uint32_t v_off,
+                                                   uint32_t k_off) {
+    constexpr int KR = 2 * NKB;  // reads of one pair of score k-steps
+    lds_wait<KR>(vcur);          // value unit U landed (the k pair U behind it may not have)
+#pragma unroll
+    for (int i = 0; i < VG; ++i) {
+      const u32x4 a = {vcur[2 * i][0], vcur[2 * i][1], vcur[2 * i + 1][0], vcur[2 * i + 1][1]};
+      o[i] = mfma32(a, pk[U], o[i]);
+    }
+    if constexpr (U + 1 < VUNITS) {
+      vreads<U + 1>(vnxt, ln, v_off);
+      lds_wait<2 * VG>(kcur[0]);
+      tie8(kcur[1], NKB);
+    } else {
+      lds_wait<0>(kcur[0]);
+      tie8(kcur[1], NKB);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(kcur[0][kb], qreg[2 * U], s[kb]);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(kcur[1][kb], qreg[2 * U + 1], s[kb]);
+    if constexpr (U + 1 < VUNITS) {
+      kreads<2 * U + 2>(knxt[0], ln, k_off);
+      kreads<2 * U + 3>(knxt[1], ln, k_off);
+      pv_s_step<U + 1>(o, pk, s, qreg, vnxt, vcur, knxt, kcur, ln, v_off, k_off);
+    }
+  }
+  __device__ static __forceinline__ void pv_scores(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV], f32x16 (&s)[NKB],
+                                                   const u32x4 (&qreg)[NKK], u32x2 (&vpre)[2 * VG],
+                                                   const Lane &ln, uint32_t v_off, uint32_t k_off) {
+    static_assert(PV_S_FUSED, "fused value/score schedule needs NKK == 2 * value units and one head-dim group");
+    u32x2 vb[2 * VG];
+    u32x4 ka[2][NKB], kb2[2][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    kreads<0>(ka[0], ln, k_off);
+    kreads<1>(ka[1], ln, k_off);
+    pv_s_step<0>(o, pk, s, qreg, vpre, vb, ka, kb2, ln, v_off, k_off);
   }
 
   // Key index (relative to the tile start) held by accumulator register i of block kb.
