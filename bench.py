@@ -13,7 +13,9 @@ not read K/V out of the 256 MB last-level cache.
 `value` is the prefill throughput in TFLOP/s counted as 4*d per visible
 (query, key) pair (causal-adjusted); the decode throughput in GB/s (algorithmic
 bytes: K and V of every cached token plus Q, O and LSE) is reported beside it.
-Kernel times come from HIP events recorded on the stream the kernels run on.
+Kernel times come from HIP events recorded on the stream the kernels run on:
+the K timed steps run as K prefill launches and then K decode passes, each
+block between two events (see timed()).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
 """
@@ -159,24 +161,31 @@ def cpu_baseline_prefill(w, budget_s: float = 12.0):
 
 
 def timed(cases, steps: int, warmup: int):
-    """Run warmup + steps; return (per-case mean ms, wall ms per step)."""
+    """Run warmup + steps; return (per-case mean ms per launch, wall ms per step).
+
+    The timed region runs the K steps case by case: K launches of the first
+    case back to back, then K of the next, each block between two HIP events
+    on the launch stream (torch's current stream), so a per-launch average
+    carries no event overhead of its own.  Every launch takes the next input
+    set of its case's rotation, as a step would.  The region is bracketed by
+    torch.cuda.synchronize() on both sides.
+    """
     import torch
 
     for i in range(warmup):
         for c in cases:
             c.run(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(cases) + 1)] for _ in range(steps)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(cases) + 1)]
     t0 = time.perf_counter()
-    for i in range(steps):
-        evs[i][0].record()
-        for j, c in enumerate(cases):
+    evs[0].record()
+    for j, c in enumerate(cases):
+        for i in range(steps):
             c.run(warmup + i)
-            evs[i][j + 1].record()
+        evs[j + 1].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    per = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
-           for j in range(len(cases))]
+    per = [evs[j].elapsed_time(evs[j + 1]) / steps for j in range(len(cases))]
     return per, wall_ms
 
 
