@@ -190,7 +190,7 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
   const int ratio = a->h_q / a->h_kv;
   const int64_t n_split = a->max_kv_len > 0 ? (a->max_kv_len + a->split_size - 1) / a->split_size : 1;
   const int64_t n_hblk = (ratio + bm - 1) / bm;
-  if (n_split * a->B * a->h_kv * n_hblk > INT32_MAX)
+  if (attn::decode_grid_size(n_split, a->B, a->h_kv, n_hblk) > INT32_MAX)
     return fail(ATTN_ERR_SHAPE, "decode grid too large: splits x B x kv heads x head blocks must fit in int32");
 
   const int64_t parts = (int64_t)a->B * a->h_q * n_split;

@@ -53,6 +53,13 @@ struct DecodeParams {
   float c;
 };
 
+// Workgroups the split-KV decode launches for these sizes (its unit numbering
+// needs the slots in whole groups of 8): every (split, sequence, kv head) slot,
+// rounded up to a multiple of 8, times the head blocks.
+__host__ __device__ inline int64_t decode_grid_size(int64_t n_split, int64_t B, int64_t h_kv, int64_t n_hblk) {
+  return (n_split * B * h_kv + 7) / 8 * 8 * n_hblk;
+}
+
 // Device-side parameters of the LSE-merge kernel.  Rows are addressed as
 // (r1, r2) with r2 < n2, so both flat rows (n2 = 1) and [B][h] rows work.
 struct CombineParams {

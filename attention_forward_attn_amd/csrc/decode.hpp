@@ -1,5 +1,5 @@
 // Split-KV decode: one workgroup per unit (key split, sequence, kv head, head
-// block).
+// block of HG*32 query heads).
 //
 // A decode step has one query token per sequence, so a single sequence gives
 // an MMA only one row -- unless the query heads that share a kv head are
@@ -47,15 +47,19 @@ __device__ __forceinline__ int decode_splits_of(const int32_t *kv_len, int split
   return min(n, n_split);
 }
 
-// Unit u of the split-major numbering: (split, sequence, kv-group/head-block
-// index y).  Returns false past the last unit.  Every lane of the wave gets
-// the same answer.  The scan walks the split levels with one ballot per level
-// and per 64 sequences; it stops at u's level, so it is short for the early
-// (full) units and at most n_split levels long.
-__device__ bool decode_unit(const DecodeParams &p, int u, int lane, int &split, int &bi, int &y) {
-  const int ny = p.h_kv * p.n_hblk;
-  const int q = u / ny;
-  y = u - q * ny;
+// Unit u: (split, sequence bi, kv head g, head block hb).  The (split,
+// sequence, kv head) triples that hold keys are numbered split-major (q); the
+// head blocks of one triple go to the same XCD (u % 8), one after another in
+// dispatch order, so the K/V they share is fetched into one L2 once:
+//   u = ((q / 8) * n_hblk + hb) * 8 + q % 8.
+// Returns false past the last unit.  Every lane of the wave gets the same
+// answer.  The scan walks the split levels with one ballot per level and per
+// 64 sequences; it stops at u's level, so it is short for the early (full)
+// units and at most n_split levels long.
+__device__ bool decode_unit(const DecodeParams &p, int u, int lane, int &split, int &bi, int &g, int &hb) {
+  const int r8 = u >> 3;
+  hb = r8 % p.n_hblk;
+  const int q = (r8 / p.n_hblk) * 8 + (u & 7);
   const int nb0 = lane < p.B ? decode_splits_of(p.kv_len, p.split, p.n_split, lane) : 0;
   auto count_above = [&](int s) {  // sequences with more than s splits
     int c = __popcll(__ballot(nb0 > s));
@@ -69,11 +73,13 @@ __device__ bool decode_unit(const DecodeParams &p, int u, int lane, int &split, 
   int s = 0;
   for (;; ++s) {
     if (s >= p.n_split) return false;
-    const int c = count_above(s);
+    const int c = count_above(s) * p.h_kv;
     if (r < c) break;
     r -= c;
   }
   split = s;
+  g = r % p.h_kv;
+  r /= p.h_kv;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int b = b0 + lane;
     const bool has = b < p.B && (b0 == 0 ? nb0 : decode_splits_of(p.kv_len, p.split, p.n_split, b)) > s;
@@ -105,15 +111,16 @@ void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_BYTES / 2];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
   const int hgrp = wave % HG, kgrp = wave / HG;
 
-  int split_, bi_, y_;
-  if (!decode_unit(p, blockIdx.x, lane, split_, bi_, y_)) return;
+  int split_, bi_, g_, hb_;
+  if (!decode_unit(p, blockIdx.x, lane, split_, bi_, g_, hb_)) return;
   const int split = __builtin_amdgcn_readfirstlane(split_);
   const int bi = __builtin_amdgcn_readfirstlane(bi_);
-  const int y = __builtin_amdgcn_readfirstlane(y_);
-  const int g = y / p.n_hblk, hb = y - g * p.n_hblk;
+  const int g = __builtin_amdgcn_readfirstlane(g_);
+  const int hb = __builtin_amdgcn_readfirstlane(hb_);
   const int L = p.kv_len[bi];
   const int kbeg = split * p.split;
   const int kend = min(kbeg + p.split, L);
@@ -238,7 +245,7 @@ void decode_split_kernel(DecodeParams p) {
 
 template <int D, int HG, int KG, int BN, int STAGES, int OCC>
 hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream) {
-  dim3 grid((unsigned)((int64_t)p.n_split * p.B * p.h_kv * p.n_hblk));
+  dim3 grid((unsigned)decode_grid_size(p.n_split, p.B, p.h_kv, p.n_hblk));
   hipLaunchKernelGGL((decode_split_kernel<D, HG, KG, BN, STAGES, OCC>), grid, dim3(HG * KG * 64), 0, stream, p);
   return hipGetLastError();
 }

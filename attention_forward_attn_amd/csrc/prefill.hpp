@@ -67,7 +67,8 @@ void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[(2 * T::STAGE_BYTES + XBYTES) / 2];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
   const int w = wave / SPLIT;      // row block of this wave
   const int slice = wave % SPLIT;  // head-dim slice of this wave
 
@@ -350,9 +351,16 @@ void prefill_pp_kernel(PrefillParams p) {
     const uint32_t v_off = ((i + STAGES - 1) % STAGES) * T::STAGE_BYTES;
     const uint32_t k_off = (i % STAGES) * T::STAGE_BYTES;
     __builtin_amdgcn_s_setprio(1);
-    if (pv && sc) T::pv_scores(o, pk, s, qreg, vpre, ln, v_off, k_off);
-    else if (pv) T::values_from(o, pk, vpre, ln, v_off);
-    else if (sc) T::scores(s, qreg, ln, k_off);
+    if constexpr (T::PV_S_FUSED) {
+      if (pv && sc) T::pv_scores(o, pk, s, qreg, vpre, ln, v_off, k_off);
+      else if (pv) T::values_from(o, pk, vpre, ln, v_off);
+      else if (sc) T::scores(s, qreg, ln, k_off);
+    } else {
+      typename T::KPre pre;
+      if (sc) T::scores_issue(pre, ln, k_off);
+      if (pv) T::values_from(o, pk, vpre, ln, v_off);
+      if (sc) T::scores_run(s, qreg, pre, ln, k_off);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   // Softmax of tile i, which ends by reading the first value operands of
