@@ -290,5 +290,5 @@ attn_status attn_combine(const attn_combine_args *a, void *stream) {
 }  // extern "C"
 
 namespace attn {
-int prefill_block_rows(int d) { return d == 128 ? 256 : (d == 64 || d == 256) ? 128 : (d == 512 ? 64 : 0); }
+int prefill_block_rows(int d) { return (d == 128 || d == 256) ? 256 : d == 64 ? 128 : (d == 512 ? 64 : 0); }
 }  // namespace attn

@@ -355,11 +355,9 @@ void prefill_pp_kernel(PrefillParams p) {
       if (pv && sc) T::pv_scores(o, pk, s, qreg, vpre, ln, v_off, k_off);
       else if (pv) T::values_from(o, pk, vpre, ln, v_off);
       else if (sc) T::scores(s, qreg, ln, k_off);
-    } else {
-      typename T::KPre pre;
-      if (sc) T::scores_issue(pre, ln, k_off);
-      if (pv) T::values_from(o, pk, vpre, ln, v_off);
-      if (sc) T::scores_run(s, qreg, pre, ln, k_off);
+    } else {  // registers are short (d = 256): no operands read ahead
+      if (pv) T::values(o, pk, ln, v_off);
+      if (sc) T::scores(s, qreg, ln, k_off);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -369,7 +367,7 @@ void prefill_pp_kernel(PrefillParams p) {
     if (i >= 0 && active(t_begin + i)) {
       mask(s, t_begin + i);
       T::softmax_step(s, pk, o, m, l, p.c);
-      T::values_issue0(vpre, ln, (i % STAGES) * T::STAGE_BYTES);
+      if constexpr (T::PV_S_FUSED) T::values_issue0(vpre, ln, (i % STAGES) * T::STAGE_BYTES);
     }
   };
   // This wave's share of the loads of tile i+STAGES-2, into the stage of tile

@@ -6,9 +6,9 @@ namespace attn {
 
 hipError_t prefill_d256(const PrefillParams &p, int mask, int n_units, hipStream_t s) {
   switch (mask) {
-    case kMaskNone: return launch_prefill<256, 4, 32, false, false, 1>(p, n_units, s);
-    case kMaskCausal: return launch_prefill<256, 4, 32, true, false, 1>(p, n_units, s);
-    default: return launch_prefill<256, 4, 32, true, true, 1>(p, n_units, s);
+    case kMaskNone: return launch_prefill_pp<256, 32, false, false, 4>(p, n_units, s);
+    case kMaskCausal: return launch_prefill_pp<256, 32, true, false, 4>(p, n_units, s);
+    default: return launch_prefill_pp<256, 32, true, true, 4>(p, n_units, s);
   }
 }
 

@@ -158,10 +158,16 @@ struct Tile {
 
   // Per-lane constants: global byte offsets of this lane's DMA chunks inside a
   // tile, and LDS byte addresses (stage 0) of its MMA operands.
+  // Both swizzles only touch the low 4 bits of a chunk index, so chunks 16
+  // apart stay 256 bytes apart: k-step kk+8 and head-dim block db+4 reuse the
+  // address of kk and db with an immediate offset of 256 bytes, and a lane
+  // keeps at most 8 + 4 LDS addresses.
+  static constexpr int NKL = NKK < 8 ? NKK : 8;
+  static constexpr int NVL = NDB < 4 ? NDB : 4;
   struct Lane {
     uint32_t kg[LOADS], vg[LOADS];  // global byte offsets (tile-relative)
-    uint32_t kl[NKK];               // LDS address of the K operand of k-step kk, key block 0
-    uint32_t vl[NDB];               // LDS address of the V^T operand of head-dim block db, k-step 0
+    uint32_t kl[NKL];               // LDS address of the K operand of k-step kk (mod 8), key block 0
+    uint32_t vl[NVL];               // LDS address of the V^T operand of head-dim block db (mod 4), k-step 0
   };
 
   // DMA offsets: wave w of the NW loading waves, writing a BN x D tile.
@@ -182,14 +188,15 @@ struct Tile {
   __device__ static __forceinline__ void init_mma(Lane &ln, uint32_t kbase, uint32_t vbase, int lane,
                                                   int slice = 0) {
     const int lr = lane & 31, hi = lane >> 5;
+    static_assert(NKK <= NKL || (DS / 8) % 16 == 0, "slices must start on a 16-chunk boundary");
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
+    for (int kk = 0; kk < NKL; ++kk)
       ln.kl[kk] = kbase + lr * D * 2 + (((slice * (DS / 8) + 2 * kk + hi) ^ kswz(lr)) * 16);
     const int grp = lane >> 4, s = lane & 15;
     const int krow = 4 * (grp >> 1) + (s >> 2);     // key row inside a 16-key step
     const int dcol = 16 * (grp & 1) + 4 * (s & 3);  // head-dim column inside a 32-block
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NVL; ++db) {
       const int col = slice * DS + db * 32 + dcol;
       ln.vl[db] = vbase + krow * D * 2 + (((col >> 3) ^ vswz(krow)) * 16) + (col & 7) * 2;
     }
@@ -240,11 +247,12 @@ struct Tile {
   // of k-step kk+1 are in flight while the MMAs of step kk run.
   template <int KK>
   __device__ static __forceinline__ void kreads(u32x4 (&a)[NKB], const Lane &ln, uint32_t stage_off) {
-    const uint32_t ad = ln.kl[KK] + stage_off;
-    a[0] = ds_read_b128<0>(ad);
-    if constexpr (NKB > 1) a[1] = ds_read_b128<1 * 32 * D * 2>(ad);
-    if constexpr (NKB > 2) a[2] = ds_read_b128<2 * 32 * D * 2>(ad);
-    if constexpr (NKB > 3) a[3] = ds_read_b128<3 * 32 * D * 2>(ad);
+    const uint32_t ad = ln.kl[KK % NKL] + stage_off;
+    constexpr int KO = (KK / NKL) * 256;
+    a[0] = ds_read_b128<KO>(ad);
+    if constexpr (NKB > 1) a[1] = ds_read_b128<KO + 1 * 32 * D * 2>(ad);
+    if constexpr (NKB > 2) a[2] = ds_read_b128<KO + 2 * 32 * D * 2>(ad);
+    if constexpr (NKB > 3) a[3] = ds_read_b128<KO + 3 * 32 * D * 2>(ad);
     static_assert(NKB <= 4, "at most 128 keys per tile");
   }
   struct NoHook {
@@ -321,18 +329,23 @@ struct Tile {
   // and 16T + 8 + 4*hi + {0..3}.  Work goes in units of (k-step, group of up
   // to 4 head-dim blocks), 8 transpose reads each, and the reads of unit U+1
   // are in flight while the MMAs of unit U run.
-  static constexpr int VG = NDB < 4 ? NDB : 4;  // head-dim blocks per unit
+  // head-dim blocks per unit: 4, or 2 at wide head dims where registers are short
+  static constexpr int VG = NDB < 4 ? NDB : (NDB >= 8 ? 2 : 4);
   static constexpr int VUNITS = NPV * (NDB / VG);
   template <int U>
   __device__ static __forceinline__ void vreads(u32x2 (&v)[2 * VG], const Lane &ln, uint32_t stage_off) {
     constexpr int T_ = U / (NDB / VG), G = U % (NDB / VG);
     constexpr int OFF_LO = T_ * 16 * D * 2;
     constexpr int OFF_HI = OFF_LO + 8 * D * 2;
-#pragma unroll
-    for (int i = 0; i < VG; ++i) {
-      v[2 * i] = ds_read_tr16<OFF_LO>(ln.vl[G * VG + i] + stage_off);
-      v[2 * i + 1] = ds_read_tr16<OFF_HI>(ln.vl[G * VG + i] + stage_off);
-    }
+    vread_blocks<OFF_LO, OFF_HI, G * VG, 0>(v, ln, stage_off);
+  }
+  template <int OFF_LO, int OFF_HI, int DB0, int I>
+  __device__ static __forceinline__ void vread_blocks(u32x2 (&v)[2 * VG], const Lane &ln, uint32_t stage_off) {
+    constexpr int DB = DB0 + I;
+    constexpr int XO = (DB / NVL) * 256;
+    v[2 * I] = ds_read_tr16<OFF_LO + XO>(ln.vl[DB % NVL] + stage_off);
+    v[2 * I + 1] = ds_read_tr16<OFF_HI + XO>(ln.vl[DB % NVL] + stage_off);
+    if constexpr (I + 1 < VG) vread_blocks<OFF_LO, OFF_HI, DB0, I + 1>(v, ln, stage_off);
   }
   // After the MMAs of the last unit of k-step T are issued, hook.vstep<T>() runs.
   template <int U, typename Hook>
