@@ -352,7 +352,10 @@ void prefill_pp_kernel(PrefillParams p) {
     const uint32_t k_off = (i % STAGES) * T::STAGE_BYTES;
     __builtin_amdgcn_s_setprio(1);
     if constexpr (T::PV_S_FUSED) {
-      if (pv && sc) T::pv_scores(o, pk, s, qreg, vpre, ln, v_off, k_off);
+      if (pv && sc) {
+        if constexpr (T::PV_S_FINE) T::pv_scores_fine(o, pk, s, qreg, vpre, ln, v_off, k_off);
+        else T::pv_scores(o, pk, s, qreg, vpre, ln, v_off, k_off);
+      }
       else if (pv) T::values_from(o, pk, vpre, ln, v_off);
       else if (sc) T::scores(s, qreg, ln, k_off);
     } else {  // registers are short (d = 256): no operands read ahead

@@ -440,6 +440,79 @@ struct Tile {
     pv_s_step<0>(o, pk, s, qreg, vpre, vb, ka, kb2, ln, v_off, k_off);
   }
 
+  // Finer version of the same schedule: 2*NKK groups of two MMAs alternate a
+  // value half-unit (two head-dim blocks of one 16-key step) with one score
+  // k-step, and the operands of group g+3 are read before group g waits, so
+  // every LDS read has the MMAs of three groups to land (at most 12 reads in
+  // flight).  Groups 0 and 2 (value unit 0) come from vpre, read before the
+  // barrier; the reads are issued in the order 0, 2, 1, 3, 4, 5, ...
+  static constexpr bool PV_S_FINE = PV_S_FUSED && NDB == 4 && NKK == 8;
+  static constexpr int fine_n(int g) { return (g & 1) ? NKB : 4; }  // reads of group g
+  static constexpr int fine_pos(int g) { return g == 1 ? 2 : g == 2 ? 1 : g; }  // issue position
+  // reads issued after group g's, once group g+3 (if any) has been issued
+  static constexpr int fine_after(int g) {
+    int c = 0;
+    const int last = g + 3 < 2 * NKK ? g + 3 : 2 * NKK - 1;
+    for (int k = 0; k <= last; ++k)
+      if (fine_pos(k) > fine_pos(g)) c += fine_n(k);
+    return c;
+  }
+  struct FineBufs {
+    u32x2 pv[3][4];
+    u32x4 sk[3][NKB];
+  };
+  template <int G>
+  __device__ static __forceinline__ void fine_issue(FineBufs &fb, u32x2 (&vpre)[8], const Lane &ln,
+                                                    uint32_t v_off, uint32_t k_off) {
+    if constexpr (G & 1) {
+      kreads<G / 2>(fb.sk[(G / 2) % 3], ln, k_off);
+    } else {
+      constexpr int H = G / 2, T_ = H / 2, B0 = 2 * (H & 1);
+      static_assert(H >= 2, "value half-units 0 and 1 come from vpre");
+      constexpr int OFF_LO = T_ * 16 * D * 2, OFF_HI = OFF_LO + 8 * D * 2;
+      u32x2 (&v)[4] = fb.pv[(H - 2) % 3];
+      v[0] = ds_read_tr16<OFF_LO>(ln.vl[B0] + v_off);
+      v[1] = ds_read_tr16<OFF_HI>(ln.vl[B0] + v_off);
+      v[2] = ds_read_tr16<OFF_LO>(ln.vl[B0 + 1] + v_off);
+      v[3] = ds_read_tr16<OFF_HI>(ln.vl[B0 + 1] + v_off);
+    }
+  }
+  template <int G>
+  __device__ static __forceinline__ void fine_step(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV], f32x16 (&s)[NKB],
+                                                   const u32x4 (&qreg)[NKK], u32x2 (&vpre)[8], FineBufs &fb,
+                                                   const Lane &ln, uint32_t v_off, uint32_t k_off) {
+    if constexpr (G + 3 < 2 * NKK) fine_issue<G + 3>(fb, vpre, ln, v_off, k_off);
+    constexpr int W = fine_after(G);
+    if constexpr (G & 1) {
+      u32x4 (&k)[NKB] = fb.sk[(G / 2) % 3];
+      lds_wait<W>(k);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(k[kb], qreg[G / 2], s[kb]);
+    } else {
+      constexpr int H = G / 2, T_ = H / 2, B0 = 2 * (H & 1);
+      u32x2 *v = H < 2 ? vpre + 4 * H : fb.pv[(H - 2 + 3) % 3];
+      asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(W));
+      tie8(v, 4);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 a = {v[2 * j][0], v[2 * j][1], v[2 * j + 1][0], v[2 * j + 1][1]};
+        o[B0 + j] = mfma32(a, pk[T_], o[B0 + j]);
+      }
+    }
+    if constexpr (G + 1 < 2 * NKK) fine_step<G + 1>(o, pk, s, qreg, vpre, fb, ln, v_off, k_off);
+  }
+  __device__ static __forceinline__ void pv_scores_fine(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV],
+                                                        f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK],
+                                                        u32x2 (&vpre)[8], const Lane &ln, uint32_t v_off,
+                                                        uint32_t k_off) {
+    static_assert(PV_S_FINE, "fine schedule shape");
+    FineBufs fb;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    fine_issue<1>(fb, vpre, ln, v_off, k_off);  // groups 0 and 2 are in vpre
+    fine_step<0>(o, pk, s, qreg, vpre, fb, ln, v_off, k_off);
+  }
+
   // Key index (relative to the tile start) held by accumulator register i of block kb.
   __device__ static __forceinline__ int key_of(int kb, int i, int hi) {
     return kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
