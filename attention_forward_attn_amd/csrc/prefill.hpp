@@ -8,12 +8,13 @@
 // A sink (status page row D5c) enters as the initial state of the running
 // softmax: max = sigma * log2(e) and sum = 1, with nothing added to O.
 //
-// Head dim 512 (the STAGE_D.md page's hd=512 case): the two waves of a pair
-// own the same 32 query rows and split the head dim into two 256-wide halves.
-// Each wave computes the partial scores over its half of Q and K; the pair
-// swaps the partials through LDS and adds them, so the score is summed in
-// logit space (S = S_0 + S_1) before any softmax; both waves then run the
-// same softmax and each multiplies P by its own 256 columns of V.
+// Head dim 512 (the STAGE_D.md page's hd=512 case): SPLIT consecutive waves
+// own the same 32 query rows and split the head dim into SPLIT slices (two
+// 256-wide halves as on the page, or four 128-wide quarters).  Each wave
+// computes the partial scores over its slice of Q and K; the group swaps the
+// partials through LDS and adds them, so the score is summed in logit space
+// (S = S_0 + S_1 + ...) before any softmax; every wave then runs the same
+// softmax and multiplies P by its own slice of V's columns.
 //
 #pragma once
 
@@ -24,7 +25,8 @@ namespace attn {
 // Work unit of workgroup v: (batch x query head bh, query tile qt).
 // Workgroups are dealt round-robin to the 8 XCDs (v % 8).  When the kv heads
 // divide evenly, every query head of kv head bkv is placed on XCD bkv % 8, so
-// the query tiles and heads that read the same K/V share one L2.  The order
+// the query tiles and heads that read the same K/V share one L2; with fewer
+// than 8 kv heads, each gets its own group of 8 / (b * h_kv) XCDs.  The order
 // inside an XCD depends on the mask: with a plain causal mask (LONGEST_FIRST)
 // the later query tiles see the most keys, so units go out in levels of
 // decreasing qt and the short ones fill in behind the long ones; otherwise
@@ -47,6 +49,15 @@ __device__ __forceinline__ void prefill_unit(const PrefillParams &p, int v, int 
     }
     const int bkv = xcd + 8 * (j / p.ratio);
     bh = bkv * p.ratio + (j - (j / p.ratio) * p.ratio);
+  } else if ((8 % (p.b * p.h_kv)) == 0 && ((int64_t)BH * nq) % 8 == 0) {
+    // fewer than 8 kv heads: each gets 8 / (b * h_kv) XCDs of its own
+    const int G = 8 / (p.b * p.h_kv);
+    const int xcd = v & 7, slot = v >> 3;
+    const int bkv = xcd / G;
+    const int j = slot * G + (xcd - bkv * G);  // unit inside the kv head: ratio x nq of them
+    const int lvl = j / p.ratio;
+    bh = bkv * p.ratio + (j - lvl * p.ratio);
+    qt = LONGEST_FIRST ? nq - 1 - lvl : lvl;
   } else if (LONGEST_FIRST) {
     const int level = v / BH;
     bh = v - level * BH;
@@ -166,7 +177,7 @@ void prefill_kernel(PrefillParams p) {
       }
     }
   } else {
-    // Head dim split over wave pairs (no cross-tile pipelining): two LDS
+    // Head dim split over SPLIT waves (no cross-tile pipelining): two LDS
     // stages of [K tile][V tile].
     typename T::Lane ln;
     T::init_lane(ln, smem, p.k_ss, p.v_ss, wave, lane, slice);
@@ -180,8 +191,8 @@ void prefill_kernel(PrefillParams p) {
                p.s_k, wave);
       const uint32_t stage_off = cur * T::STAGE_BYTES;
       const bool act = active(t);
-      // Both waves of a pair take part in the exchange (and its barrier); the
-      // pair's activity is decided together, inactive pairs skip the MMAs.
+      // All waves of a group take part in the exchange (and its barrier); the
+      // group's activity is decided together, inactive groups skip the MMAs.
       f32x16 s[T::NKB];
       if (act) T::scores(s, qreg, ln, stage_off);
       f32x4 *xb = reinterpret_cast<f32x4 *>(reinterpret_cast<char *>(smem) + 2 * T::STAGE_BYTES);
@@ -196,16 +207,20 @@ void prefill_kernel(PrefillParams p) {
       }
       __syncthreads();
       if (act) {
-        const int partner = wave ^ 1;
+        // S = S_0 + S_1 (+ S_2 + S_3), summed in slice order by every wave of
+        // the group, so all of them see bit-identical scores.
+        const int w0 = wave - slice;
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 v = xb[(partner * T::NKB * 4 + kb * 4 + q4) * 64 + lane];
-            s[kb][4 * q4] += v[0];
-            s[kb][4 * q4 + 1] += v[1];
-            s[kb][4 * q4 + 2] += v[2];
-            s[kb][4 * q4 + 3] += v[3];
+            f32x4 v = xb[(w0 * T::NKB * 4 + kb * 4 + q4) * 64 + lane];
+#pragma unroll
+            for (int j = 1; j < SPLIT; ++j) v += xb[((w0 + j) * T::NKB * 4 + kb * 4 + q4) * 64 + lane];
+            s[kb][4 * q4] = v[0];
+            s[kb][4 * q4 + 1] = v[1];
+            s[kb][4 * q4 + 2] = v[2];
+            s[kb][4 * q4 + 3] = v[3];
           }
         mask(s, t);
         u32x4 pk[T::NPV];
