@@ -69,6 +69,21 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 // including the prefetch of later tiles.
 __device__ __forceinline__ void barrier_nofence() { __builtin_amdgcn_s_barrier(); }
 
+// Eight independent 2^x (v_exp_f32, the instruction behind fast_exp2) issued
+// back to back.  Left to itself the compiler pairs every exp with the FMA
+// that feeds it, so a single wave stalls on each pair; here all eight
+// arguments are computed first.  The trailing s_nop gives the wait state a
+// vector instruction needs before reading a transcendental result (one is
+// required, two are given), which the compiler cannot see through the asm
+// statement.
+__device__ __forceinline__ void exp2_x8(float (&e)[8], const float (&t)[8]) {
+  asm volatile(
+      "v_exp_f32 %0, %8\n v_exp_f32 %1, %9\n v_exp_f32 %2, %10\n v_exp_f32 %3, %11\n"
+      "v_exp_f32 %4, %12\n v_exp_f32 %5, %13\n v_exp_f32 %6, %14\n v_exp_f32 %7, %15\n s_nop 1"
+      : "=&v"(e[0]), "=&v"(e[1]), "=&v"(e[2]), "=&v"(e[3]), "=&v"(e[4]), "=&v"(e[5]), "=&v"(e[6]), "=&v"(e[7])
+      : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(t[4]), "v"(t[5]), "v"(t[6]), "v"(t[7]));
+}
+
 // 32-bit LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   const __attribute__((address_space(3))) char *q = (const __attribute__((address_space(3))) char *)p;
@@ -546,9 +561,10 @@ struct Tile {
   __device__ static __forceinline__ void softmax_exp(const f32x16 (&s)[NKB], u32x4 (&pk)[NPV], float &rs,
                                                      float c, float base) {
     constexpr int kb = T_ >> 1, r0 = (T_ & 1) * 8;
-    float e[8];
+    float t[8], e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(s[kb][r0 + j], c, -base));
+    for (int j = 0; j < 8; ++j) t[j] = fmaf(s[kb][r0 + j], c, -base);
+    exp2_x8(e, t);
     u32x4 x;
 #pragma unroll
     for (int q = 0; q < 4; ++q) x[q] = pack_bf16x2(e[2 * q], e[2 * q + 1]);
