@@ -107,7 +107,8 @@ attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
       omax > (int64_t(1) << 40))
     return fail(ATTN_ERR_SHAPE, "tensor extent exceeds 2^40 elements");
 
-  const int bm = attn::prefill_block_rows(a->d);
+  const int mask = a->window > 0 ? attn::kMaskCausalWindow : (a->causal ? attn::kMaskCausal : attn::kMaskNone);
+  const int bm = attn::prefill_block_rows(a->d, mask);
   const int64_t n_qtiles = (a->s_q + bm - 1) / bm;
   const int64_t n_units = n_qtiles * a->b * a->h_q;
   if (n_units > kMaxIndex) return fail(ATTN_ERR_SHAPE, "too many work units (%lld)", (long long)n_units);
@@ -130,7 +131,6 @@ attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
   p.n_qtiles = (int32_t)n_qtiles;
   p.c = a->scale * attn::kLog2e;
 
-  const int mask = a->window > 0 ? attn::kMaskCausalWindow : (a->causal ? attn::kMaskCausal : attn::kMaskNone);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (a->d) {
@@ -290,5 +290,16 @@ attn_status attn_combine(const attn_combine_args *a, void *stream) {
 }  // extern "C"
 
 namespace attn {
-int prefill_block_rows(int d) { return (d == 128 || d == 256) ? 256 : d == 64 ? 128 : (d == 512 ? 64 : 0); }
+// d = 128 and 256 run the 8-wave ping-pong kernel on 256 rows, except that a
+// sliding window at d = 128 keeps the 4-wave kernel on 128 rows: with the
+// window's two masked edges, the smaller tile wastes less of each tile range.
+int prefill_block_rows(int d, int mask) {
+  switch (d) {
+    case 64: return 128;
+    case 128: return mask == kMaskCausalWindow ? 128 : 256;
+    case 256: return 256;
+    case 512: return 64;
+    default: return 0;
+  }
+}
 }  // namespace attn

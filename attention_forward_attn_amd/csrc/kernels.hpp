@@ -8,8 +8,8 @@ namespace attn {
 // Mask kinds of the prefill kernel.
 enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskCausalWindow = 2 };
 
-// Query rows per prefill workgroup for head dim d (0 if unsupported).
-int prefill_block_rows(int d);
+// Query rows per prefill workgroup for head dim d and mask kind (0 if unsupported).
+int prefill_block_rows(int d, int mask);
 // Enqueue the prefill kernel for head dim d; n_units = b * h_q * n_qtiles.
 hipError_t prefill_d64(const PrefillParams &p, int mask, int n_units, hipStream_t s);
 hipError_t prefill_d128(const PrefillParams &p, int mask, int n_units, hipStream_t s);

@@ -8,7 +8,7 @@ hipError_t prefill_d128(const PrefillParams &p, int mask, int n_units, hipStream
   switch (mask) {
     case kMaskNone: return launch_prefill_pp<128, 64, false, false, 4>(p, n_units, s);
     case kMaskCausal: return launch_prefill_pp<128, 64, true, false, 4>(p, n_units, s);
-    default: return launch_prefill_pp<128, 64, true, true, 4>(p, n_units, s);
+    default: return launch_prefill<128, 4, 64, true, true, 2>(p, n_units, s);
   }
 }
 
