@@ -74,6 +74,33 @@ def test_prefill_small(case):
     check(out, lse, o_ref, l_ref, str(case))
 
 
+EDGE_LENGTHS = [1, 17, 63, 64, 65, 255, 257, 1000]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("s", EDGE_LENGTHS)
+def test_prefill_edge_lengths(s, d, causal):
+    # lengths around the 64-key tiles and the 128/256-row query tiles
+    out, lse, o_ref, l_ref = run_case(1, 2, 1, s, s, d, causal=causal, seed=s + d)
+    check(out, lse, o_ref, l_ref, f"s={s} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 4, 8, 16, 32])
+def test_prefill_gqa_ratios(ratio):
+    out, lse, o_ref, l_ref = run_case(1, 32, 32 // ratio, 300, 300, 128, causal=True, seed=ratio)
+    check(out, lse, o_ref, l_ref, f"ratio {ratio}")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("window", [1, 1024, 5000])
+def test_prefill_window_sizes(window, d):
+    # a one-key window, one shorter than the sequence, one longer than it
+    out, lse, o_ref, l_ref = run_case(1, 2, 2, 1100, 1100, d, causal=True, window=window, sink=True,
+                                      seed=window + d)
+    check(out, lse, o_ref, l_ref, f"window {window} d={d}")
+
+
 @pytest.mark.parametrize("d", [64, 128, 256, 512])
 def test_prefill_strided_bshd(d):
     out, lse, o_ref, l_ref = run_case(2, 4, 2, 200, 200, d, causal=True, layout="bshd")
@@ -169,8 +196,10 @@ def test_prefill_full_size_sampled(name):
     picks = set()
     for bi in {0, w.b - 1}:
         for h in {0, w.h_q - 1, int(rng.integers(w.h_q))}:
-            for i in {0, 1, 63, 64, 127, 128, w.s_q // 2, w.s_q - 2, w.s_q - 1, int(rng.integers(w.s_q))}:
-                picks.add((bi, h, i))
+            for i in {0, 1, 63, 64, 127, 128, 255, 256, w.s_q // 2, w.s_q - 2, w.s_q - 1,
+                      int(rng.integers(w.s_q))}:
+                if i < w.s_q:
+                    picks.add((bi, h, i))
     picks = sorted(picks)
     o_ref, l_ref = oracle_rows(inp["q"], inp["k"], inp["v"], scale, w.causal, w.window,
                                inp["sinks"], picks)
