@@ -356,6 +356,20 @@ void prefill_pp_kernel(PrefillParams p) {
   f32x16 s[T::NKB];
   u32x4 pk[T::NPV];
   u32x2 vpre[2 * T::VG];  // value operands of unit 0, read ahead across the barrier
+  // This wave's share of the loads of tile i+STAGES-2, into the stage of tile
+  // i-2 (free once barrier A_i has passed).  Each group issues it once per
+  // iteration, group 0 after A_i and group 1 after B_i: with the fine schedule
+  // right after the last MMAs of its MMA phase, whose issue slots then sit
+  // idle until the barrier (measured 3 % faster than at the start of the
+  // softmax phase, and than between the first MMA groups, where the loads
+  // hold up the MMA issue); otherwise at the start of the softmax phase of the
+  // same half-iteration.  Before A_{i+1} a wave has exactly one later tile in
+  // flight.
+  auto load_ahead = [&](int i) {
+    T::dma(ln, smem + ((i + STAGES - 2) % STAGES) * (T::STAGE_BYTES / 2), kbase, p.k_ss, vbase, p.v_ss,
+           (t_begin + i + STAGES - 2) * BN, lim, wave);
+  };
+  constexpr bool DMA_IN_MMA = T::PV_S_FINE;
   // MMA phase of iteration i: value MMA of tile i-1 (its first operands are
   // already in flight) fused with the score MMA of tile i.  The wave raises
   // its issue priority so that the other group's softmax fills the gaps
@@ -368,11 +382,18 @@ void prefill_pp_kernel(PrefillParams p) {
     __builtin_amdgcn_s_setprio(1);
     if constexpr (T::PV_S_FUSED) {
       if (pv && sc) {
-        if constexpr (T::PV_S_FINE) T::pv_scores_fine(o, pk, s, qreg, vpre, ln, v_off, k_off);
-        else T::pv_scores(o, pk, s, qreg, vpre, ln, v_off, k_off);
+        if constexpr (T::PV_S_FINE)
+          T::pv_scores_fine(o, pk, s, qreg, vpre, ln, v_off, k_off,
+                            typename T::template DmaHook<15, 15>{
+                                ln, smem + ((i + STAGES - 2) % STAGES) * (T::STAGE_BYTES / 2), kbase, vbase,
+                                p.k_ss, p.v_ss, (t_begin + i + STAGES - 2) * BN, lim, wave});
+        else
+          T::pv_scores(o, pk, s, qreg, vpre, ln, v_off, k_off);
+      } else {
+        if (DMA_IN_MMA) load_ahead(i);
+        if (pv) T::values_from(o, pk, vpre, ln, v_off);
+        else if (sc) T::scores(s, qreg, ln, k_off);
       }
-      else if (pv) T::values_from(o, pk, vpre, ln, v_off);
-      else if (sc) T::scores(s, qreg, ln, k_off);
     } else {  // registers are short (d = 256): no operands read ahead
       if (pv) T::values(o, pk, ln, v_off);
       if (sc) T::scores(s, qreg, ln, k_off);
@@ -388,14 +409,6 @@ void prefill_pp_kernel(PrefillParams p) {
       if constexpr (T::PV_S_FUSED) T::values_issue0(vpre, ln, (i % STAGES) * T::STAGE_BYTES);
     }
   };
-  // This wave's share of the loads of tile i+STAGES-2, into the stage of tile
-  // i-2 (free once barrier A_i has passed).  Each group issues it at the start
-  // of its softmax phase after A_i: group 1 in A_i, group 0 in B_i.  Before
-  // A_{i+1} a wave then has exactly one later tile in flight.
-  auto load_ahead = [&](int i) {
-    T::dma(ln, smem + ((i + STAGES - 2) % STAGES) * (T::STAGE_BYTES / 2), kbase, p.k_ss, vbase, p.v_ss,
-           (t_begin + i + STAGES - 2) * BN, lim, wave);
-  };
 
   if (nt > 0) {
     for (int i = 0; i <= nt; ++i) {
@@ -404,12 +417,12 @@ void prefill_pp_kernel(PrefillParams p) {
       if (grp == 0) {
         mma_phase(i);
       } else {
-        load_ahead(i);
+        if (!DMA_IN_MMA) load_ahead(i);
         if (i > 0) softmax_phase(i - 1);
       }
       barrier_nofence();  // B_i
       if (grp == 0) {
-        load_ahead(i);
+        if (!DMA_IN_MMA) load_ahead(i);
         if (i < nt) softmax_phase(i);
       } else {
         mma_phase(i);

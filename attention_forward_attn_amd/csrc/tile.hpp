@@ -231,8 +231,8 @@ struct Tile {
   // so its loads touch no memory and only write zeros to LDS.  Byte offsets
   // inside a tile must fit in 32 bits (row strides below 2^24 elements,
   // checked by the host).
-  template <bool IS_V>
-  __device__ static __forceinline__ void dma1(const Lane &ln, uint16_t *dst, const uint16_t *base,
+  // (is_v selects the V lane offsets; a constant at every call.)
+  __device__ static __forceinline__ void dma1(const Lane &ln, bool is_v, uint16_t *dst, const uint16_t *base,
                                               int64_t rs, int j0, int nkeys, int w) {
     const int rows = min(nkeys - j0, BN);
     const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * rs * 2 + D * 2) : 0u;
@@ -240,23 +240,38 @@ struct Tile {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (u * NW + w) * 512), 16,
-                                               IS_V ? ln.vg[u] : ln.kg[u], 0, 0, 0);
+                                               is_v ? ln.vg[u] : ln.kg[u], 0, 0, 0);
   }
   __device__ static __forceinline__ void dma_k(const Lane &ln, uint16_t *dst, const uint16_t *base,
                                                int64_t rs, int j0, int nkeys, int w) {
-    dma1<false>(ln, dst, base, rs, j0, nkeys, w);
+    dma1(ln, false, dst, base, rs, j0, nkeys, w);
   }
   __device__ static __forceinline__ void dma_v(const Lane &ln, uint16_t *dst, const uint16_t *base,
                                                int64_t rs, int j0, int nkeys, int w) {
-    dma1<true>(ln, dst, base, rs, j0, nkeys, w);
+    dma1(ln, true, dst, base, rs, j0, nkeys, w);
   }
   // K and V tiles of one key range into a stage laid out as [K tile][V tile].
   __device__ static __forceinline__ void dma(const Lane &ln, uint16_t *stage, const uint16_t *kbase,
                                              int64_t k_rs, const uint16_t *vbase, int64_t v_rs,
                                              int j0, int nkeys, int w) {
-    dma1<false>(ln, stage, kbase, k_rs, j0, nkeys, w);
-    dma1<true>(ln, stage + TILE_ELEMS, vbase, v_rs, j0, nkeys, w);
+    dma1(ln, false, stage, kbase, k_rs, j0, nkeys, w);
+    dma1(ln, true, stage + TILE_ELEMS, vbase, v_rs, j0, nkeys, w);
   }
+  // The same loads, issued from inside an MMA schedule: step<G>() issues the
+  // K share after MMA group GK and the V share after group GV.
+  template <int GK, int GV>
+  struct DmaHook {
+    const Lane &ln;
+    uint16_t *stage;
+    const uint16_t *kbase, *vbase;
+    int64_t k_rs, v_rs;
+    int j0, nkeys, w;
+    template <int G>
+    __device__ __forceinline__ void step() {
+      if constexpr (G == GK) dma_k(ln, stage, kbase, k_rs, j0, nkeys, w);
+      if constexpr (G == GV) dma_v(ln, stage + TILE_ELEMS, vbase, v_rs, j0, nkeys, w);
+    }
+  };
 
   // S^T block accumulators of this wave for the staged tile.  The K operands
   // of k-step kk+1 are in flight while the MMAs of step kk run.
@@ -492,10 +507,10 @@ struct Tile {
       v[3] = ds_read_tr16<OFF_HI>(ln.vl[B0 + 1] + v_off);
     }
   }
-  template <int G>
+  template <int G, typename Hook>
   __device__ static __forceinline__ void fine_step(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV], f32x16 (&s)[NKB],
                                                    const u32x4 (&qreg)[NKK], u32x2 (&vpre)[8], FineBufs &fb,
-                                                   const Lane &ln, uint32_t v_off, uint32_t k_off) {
+                                                   const Lane &ln, uint32_t v_off, uint32_t k_off, Hook &hook) {
     if constexpr (G + 3 < 2 * NKK) fine_issue<G + 3>(fb, vpre, ln, v_off, k_off);
     constexpr int W = fine_after(G);
     if constexpr (G & 1) {
@@ -514,18 +529,21 @@ struct Tile {
         o[B0 + j] = mfma32(a, pk[T_], o[B0 + j]);
       }
     }
-    if constexpr (G + 1 < 2 * NKK) fine_step<G + 1>(o, pk, s, qreg, vpre, fb, ln, v_off, k_off);
+    hook.template step<G>();
+    if constexpr (G + 1 < 2 * NKK) fine_step<G + 1>(o, pk, s, qreg, vpre, fb, ln, v_off, k_off, hook);
   }
+  // hook.step<G>() runs after the MMAs of group G are issued.
+  template <typename Hook = NoHook>
   __device__ static __forceinline__ void pv_scores_fine(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV],
                                                         f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK],
                                                         u32x2 (&vpre)[8], const Lane &ln, uint32_t v_off,
-                                                        uint32_t k_off) {
+                                                        uint32_t k_off, Hook &&hook = Hook{}) {
     static_assert(PV_S_FINE, "fine schedule shape");
     FineBufs fb;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
     fine_issue<1>(fb, vpre, ln, v_off, k_off);  // groups 0 and 2 are in vpre
-    fine_step<0>(o, pk, s, qreg, vpre, fb, ln, v_off, k_off);
+    fine_step<0>(o, pk, s, qreg, vpre, fb, ln, v_off, k_off, hook);
   }
 
   // Key index (relative to the tile start) held by accumulator register i of block kb.

@@ -264,8 +264,8 @@ def bench_one(name: str, steps: int, warmup: int, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None, help="bench one named workload alone")
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
