@@ -3,8 +3,9 @@
 // Per row, with M = max_p lse_p and w_p = exp(lse_p - M):
 //   O = sum_p w_p O_p / sum_p w_p,   LSE = M + ln sum_p w_p
 // (the STAGE_D.md page's "O rescale (kt>0)" workaround merge).  Parts whose
-// LSE is -inf carry no weight and their O is never read, so a split that saw
-// no key may leave its partial output unwritten.
+// LSE is -inf carry no weight: their O is loaded but never used, so a split
+// that saw no key may leave its partial output unwritten (any bit pattern,
+// NaN included).
 //
 // One thread per 8 consecutive output columns of a row: each part gives it
 // one 16-byte (bf16) or 32-byte (fp32) vector.
@@ -14,30 +15,36 @@
 
 namespace attn {
 
+// Raw 8-column vector of one part (fp32 or bf16) and its widening to fp32.
 template <typename PT>
-__device__ __forceinline__ void load8(const PT *p, float (&v)[8]);
+struct Vec8;
 template <>
-__device__ __forceinline__ void load8<float>(const float *p, float (&v)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
-  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
-}
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float (&v)[8]) {
-  const u32x4 a = *reinterpret_cast<const u32x4 *>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(a[i] << 16);
-    v[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+struct Vec8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = *reinterpret_cast<const f32x4 *>(p);
+    b = *reinterpret_cast<const f32x4 *>(p + 4);
   }
-}
+  __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+template <>
+struct Vec8<uint16_t> {
+  u32x4 a;
+  __device__ __forceinline__ void load(const uint16_t *p) { a = *reinterpret_cast<const u32x4 *>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    return (e & 1) ? __uint_as_float(a[e >> 1] & 0xffff0000u) : __uint_as_float(a[e >> 1] << 16);
+  }
+};
 
-// Parts are taken PB at a time: all their LSEs and partial outputs are
-// loaded before any is used, and the running (max, weight sum, accumulator)
-// is rescaled once per batch to the batch's new maximum.
+// Parts are taken PB at a time.  The partial vectors of a batch are loaded
+// together with their LSEs (not after them: a part's LSE only decides whether
+// its vector is used), so a batch costs one memory round trip; the running
+// (max, weight sum, accumulator) is rescaled once per batch to the batch's
+// new maximum.  bf16 parts come 16 to a batch (every split of a 8192-key
+// sequence at 512 keys per split in one trip), fp32 parts 8.
 template <typename PT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  constexpr int PB = 8;
+  constexpr int PB = sizeof(PT) == 2 ? 16 : 8;
   const int cpr = p.d / 8;  // 8-column chunks per row
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= (int64_t)p.rows * cpr) return;
@@ -54,12 +61,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   float mx = kNegInf, wsum = 0.0f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < n; i += PB) {
-    float li[PB], v[PB][8];
+    float li[PB];
+    Vec8<PT> v[PB];
 #pragma unroll
-    for (int u = 0; u < PB; ++u) li[u] = i + u < n ? lp[(i + u) * p.lse_part_stride] : kNegInf;
-#pragma unroll
-    for (int u = 0; u < PB; ++u)
-      if (li[u] != kNegInf) load8<PT>(op + (int64_t)(i + u) * p.o_part_stride, v[u]);
+    for (int u = 0; u < PB; ++u) {
+      li[u] = kNegInf;
+      if (i + u < n) {
+        li[u] = lp[(i + u) * p.lse_part_stride];
+        v[u].load(op + (int64_t)(i + u) * p.o_part_stride);
+      }
+    }
     float bm = li[0];
 #pragma unroll
     for (int u = 1; u < PB; ++u) bm = fmaxf(bm, li[u]);
@@ -71,11 +82,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     for (int e = 0; e < 8; ++e) acc[e] *= sc;
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      if (li[u] == kNegInf) continue;
+      if (li[u] == kNegInf) continue;  // such a part's vector may be unwritten: never read it
       const float wgt = __expf(li[u] - nm);
       wsum += wgt;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wgt * v[u][e];
+      for (int e = 0; e < 8; ++e) acc[e] += wgt * v[u].get(e);
     }
     mx = nm;
   }

@@ -41,10 +41,12 @@ namespace attn {
 // Splits of sequence b that form a unit: one per started chunk of keys, and
 // split 0 even for an empty sequence (it carries the sink and the -inf LSE).
 // Lengths beyond max_kv_len are clamped to the splits the grid was sized for.
-__device__ __forceinline__ int decode_splits_of(const int32_t *kv_len, int split, int n_split, int b) {
-  const int L = kv_len[b];
+__device__ __forceinline__ int decode_splits_len(int L, int split, int n_split) {
   const int n = L > 0 ? (L - 1) / split + 1 : 1;
   return min(n, n_split);
+}
+__device__ __forceinline__ int decode_splits_of(const int32_t *kv_len, int split, int n_split, int b) {
+  return decode_splits_len(kv_len[b], split, n_split);
 }
 
 // Unit u: (split, sequence bi, kv head g, head block hb).  The (split,
@@ -55,12 +57,14 @@ __device__ __forceinline__ int decode_splits_of(const int32_t *kv_len, int split
 // Returns false past the last unit.  Every lane of the wave gets the same
 // answer.  The scan walks the split levels with one ballot per level and per
 // 64 sequences; it stops at u's level, so it is short for the early (full)
-// units and at most n_split levels long.
-__device__ bool decode_unit(const DecodeParams &p, int u, int lane, int &split, int &bi, int &g, int &hb) {
+// units and at most n_split levels long.  len0 is kv_len[lane] (lanes below
+// B), loaded by the caller.
+__device__ bool decode_unit(const DecodeParams &p, int u, int lane, int len0, int &split, int &bi, int &g,
+                            int &hb) {
   const int r8 = u >> 3;
   hb = r8 % p.n_hblk;
   const int q = (r8 / p.n_hblk) * 8 + (u & 7);
-  const int nb0 = lane < p.B ? decode_splits_of(p.kv_len, p.split, p.n_split, lane) : 0;
+  const int nb0 = lane < p.B ? decode_splits_len(len0, p.split, p.n_split) : 0;
   auto count_above = [&](int s) {  // sequences with more than s splits
     int c = __popcll(__ballot(nb0 > s));
     for (int b0 = 64; b0 < p.B; b0 += 64) {
@@ -115,13 +119,17 @@ void decode_split_kernel(DecodeParams p) {
   const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
   const int hgrp = wave % HG, kgrp = wave / HG;
 
+  // Lengths and starts of the first 64 sequences are loaded once, side by
+  // side, so the unit scan and this unit's key range wait for one load.
+  const int len0 = lane < p.B ? p.kv_len[lane] : 0;
+  const int64_t start0 = lane < p.B ? p.kv_start[lane] : 0;
   int split_, bi_, g_, hb_;
-  if (!decode_unit(p, blockIdx.x, lane, split_, bi_, g_, hb_)) return;
+  if (!decode_unit(p, blockIdx.x, lane, len0, split_, bi_, g_, hb_)) return;
   const int split = __builtin_amdgcn_readfirstlane(split_);
   const int bi = __builtin_amdgcn_readfirstlane(bi_);
   const int g = __builtin_amdgcn_readfirstlane(g_);
   const int hb = __builtin_amdgcn_readfirstlane(hb_);
-  const int L = p.kv_len[bi];
+  const int L = bi < 64 ? __builtin_amdgcn_readlane(len0, bi) : p.kv_len[bi];
   const int kbeg = split * p.split;
   const int kend = min(kbeg + p.split, L);
 
@@ -130,7 +138,10 @@ void decode_split_kernel(DecodeParams p) {
   const int head = g * p.ratio + min(hig, p.ratio - 1);
   const int64_t part = ((int64_t)bi * p.h_q + head) * p.n_split + split;
 
-  const int64_t start = p.kv_start[bi];
+  const int64_t start =
+      bi < 64 ? (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(start0 >> 32), bi) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)start0, bi))
+              : p.kv_start[bi];
   const uint16_t *kbase = p.k + (start + kbeg) * p.k_st + g * p.k_sh;
   const uint16_t *vbase = p.v + (start + kbeg) * p.v_st + g * p.v_sh;
   const int n_keys = max(kend - kbeg, 0);
@@ -226,9 +237,42 @@ void decode_split_kernel(DecodeParams p) {
 
   const float lt = sum_across_halves(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (row_ok) {
-    // normalised partial output, bf16 (its rounding is far below the final
-    // bf16 rounding of O after the merge)
+  if (row_ok && hi == 0) p.lse_part[part] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  // Normalised partial output, bf16 (its rounding is far below the final bf16
+  // rounding of O after the merge).  A lane holds pieces of one head's row,
+  // so a store straight from the accumulators would touch 32 rows 8 bytes at
+  // a time; the tile goes through the (now idle) K/V ring instead, with 16-byte
+  // chunks XOR-swizzled by row, and every store then writes whole rows.
+  if constexpr (KG == 1) {
+    constexpr int NC = D / 8;              // 16-byte chunks per row
+    constexpr int SW = NC < 16 ? NC : 16;  // swizzle span
+    constexpr int RPI = 64 / NC;           // rows per store instruction
+    static_assert(BM * D * 2 <= RING_BYTES, "partial tile must fit in the ring");
+    __syncthreads();  // every wave is done with the last stage
+    char *xw = reinterpret_cast<char *>(smem) + hgrp * 32 * D * 2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        u32x2 val;
+        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
+        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
+        const int chunk = db * 4 + gi;
+        *reinterpret_cast<u32x2 *>(xw + lr * D * 2 + (chunk ^ (lr % SW)) * 16 + 8 * hi) = val;
+      }
+    __syncthreads();
+    const int c = lane % NC;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / NC;
+      const u32x4 val = *reinterpret_cast<const u32x4 *>(xw + r * D * 2 + (c ^ (r % SW)) * 16);
+      const int hr = hb * BM + hgrp * 32 + r;  // head inside the kv group
+      if (hr < p.ratio) {
+        const int64_t pr = ((int64_t)bi * p.h_q + g * p.ratio + hr) * p.n_split + split;
+        *reinterpret_cast<u32x4 *>(p.o_part + pr * D + c * 8) = val;
+      }
+    }
+  } else if (row_ok) {
     uint16_t *op = p.o_part + part * D + 4 * hi;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -239,7 +283,6 @@ void decode_split_kernel(DecodeParams p) {
         val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
         *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
       }
-    if (hi == 0) p.lse_part[part] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   }
 }
 
