@@ -253,21 +253,24 @@ void prefill_kernel(PrefillParams p) {
 // share every staged K/V tile.  Waves w and w+4 run on the same SIMD, so the
 // two groups can take turns: while one group runs its MMAs (the value MMA of
 // the previous tile and the score MMA of the current one), the other runs the
-// softmax of its current tile on the vector ALU, and at every workgroup
-// barrier they swap.  Group 1 runs half an iteration behind group 0:
+// softmax of its current tile on the vector ALU.  Group 1 runs half an
+// iteration behind group 0; one workgroup barrier A_i per iteration:
 //
-//   phase A_i:  group 0: P(i-1).V(i-1), S(i) = K(i).Q   group 1: softmax(i-1)
-//   phase B_i:  group 0: softmax(i)                     group 1: P(i-1).V(i-1), S(i)
+//   after A_i:  group 0: P(i-1).V(i-1), S(i) = K(i).Q   group 1: softmax(i-1)
+//      then:    group 0: softmax(i)                     group 1: P(i-1).V(i-1), S(i)
 //
-// Row blocks are interleaved between the groups (group g owns blocks g, g+2,
-// g+4, g+6 of the 256-row query tile) so that both see nearly the same causal
-// and window extents.  A ring of STAGES LDS stages holds [K tile][V tile];
-// tile i is last read by group 1's value MMA in phase B_{i+1}, so the loads
-// of tile i+STAGES-2 go into the stage of tile i-2 once barrier A_i has
-// passed, and have a full iteration or more to land.  Every wave issues its
-// loads and its softmax in the phase where it runs no MMA, and the value
-// operands of a tile are read ahead across the barrier that opens the MMA
-// phase, so that phase is mostly MMA issue.
+// Each group goes from its first half to its second without a barrier: the
+// halves keep their order because each half of one group is about as long
+// as the other group's half that it overlaps, and no LDS access depends on
+// the switch (below).  Row blocks are interleaved between the groups (group g
+// owns blocks g, g+2, g+4, g+6 of the 256-row query tile) so that both see
+// nearly the same causal and window extents.  A ring of STAGES LDS stages
+// holds [K tile][V tile]; between A_i and A_{i+1} the waves read only the
+// stages of tiles i-1 and i, and write (by DMA) only the stage of tile i-2,
+// which takes tile i+STAGES-2 and whose last reads were consumed by MMAs
+// before A_i.  Every wave's loads of tile i+1 are waited for before A_{i+1},
+// so they have a full iteration or more to land.  The value operands of a tile are read ahead at
+// the end of the softmax, so the MMA phase is mostly MMA issue.
 template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_pp_kernel(PrefillParams p) {
@@ -357,14 +360,12 @@ void prefill_pp_kernel(PrefillParams p) {
   u32x4 pk[T::NPV];
   u32x2 vpre[2 * T::VG];  // value operands of unit 0, read ahead across the barrier
   // This wave's share of the loads of tile i+STAGES-2, into the stage of tile
-  // i-2 (free once barrier A_i has passed).  Each group issues it once per
-  // iteration, group 0 after A_i and group 1 after B_i: with the fine schedule
-  // right after the last MMAs of its MMA phase, whose issue slots then sit
-  // idle until the barrier (measured 3 % faster than at the start of the
-  // softmax phase, and than between the first MMA groups, where the loads
-  // hold up the MMA issue); otherwise at the start of the softmax phase of the
-  // same half-iteration.  Before A_{i+1} a wave has exactly one later tile in
-  // flight.
+  // i-2 (free once barrier A_i has passed), issued once per iteration: with
+  // the fine schedule right after the last MMAs of the wave's MMA phase
+  // (measured 3 % faster than at the start of the softmax phase, and than
+  // between the first MMA groups, where the loads hold up the MMA issue);
+  // otherwise at the start of the wave's softmax phase.  Before A_{i+1} a
+  // wave has exactly one later tile in flight.
   auto load_ahead = [&](int i) {
     T::dma(ln, smem + ((i + STAGES - 2) % STAGES) * (T::STAGE_BYTES / 2), kbase, p.k_ss, vbase, p.v_ss,
            (t_begin + i + STAGES - 2) * BN, lim, wave);
@@ -416,15 +417,11 @@ void prefill_pp_kernel(PrefillParams p) {
       barrier_nofence();                           // A_i: tile i published, tile i-2's stage free
       if (grp == 0) {
         mma_phase(i);
-      } else {
-        if (!DMA_IN_MMA) load_ahead(i);
-        if (i > 0) softmax_phase(i - 1);
-      }
-      barrier_nofence();  // B_i
-      if (grp == 0) {
         if (!DMA_IN_MMA) load_ahead(i);
         if (i < nt) softmax_phase(i);
       } else {
+        if (!DMA_IN_MMA) load_ahead(i);
+        if (i > 0) softmax_phase(i - 1);
         mma_phase(i);
       }
     }
