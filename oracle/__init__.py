@@ -8,6 +8,8 @@ from .attention import (  # noqa: F401
     NEG_INF,
     attention_flops,
     attention_ref,
+    gather_pages,
+    decode_paged_ref,
     decode_ref,
     decode_split_ref,
     merge_ref,

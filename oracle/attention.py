@@ -29,6 +29,8 @@ What it computes, and where the pages define it:
   Mathematically Impossible", which limits it to disjoint token sets).
 * ``decode_ref`` / ``decode_split_ref`` -- single-token decode over a packed
   per-sequence KV cache, unsplit and split into fixed-size key chunks.
+* ``decode_paged_ref`` -- the same decode over a paged KV cache addressed
+  through a block table (reading of the layout stated in its docstring).
 
 Readings taken where the pages are silent or garbled (each is stated again
 where it is used):
@@ -308,6 +310,52 @@ def decode_split_ref(q, k, v, kv_start, kv_len, scale: float, split: int, sinks=
         pl = np.concatenate([pl, np.broadcast_to(sig[None, None, :], (1, B, h_q))], axis=0)
     o, l = merge_ref(po, pl)
     return o, l, po, pl
+
+
+def gather_pages(cache, block_table_row, n_tokens: int, page_size: int) -> np.ndarray:
+    """Tokens 0..n_tokens-1 of one sequence out of a paged cache, in order.
+
+    cache is [n_pages, page_size, h_kv, d]; token t lives in page
+    block_table_row[t // page_size] at slot t % page_size.  Only the pages
+    that hold one of the n_tokens tokens are touched.  Returns [n_tokens, h_kv, d].
+    """
+    cache = _as_f64(cache)
+    table = np.asarray(block_table_row, dtype=np.int64).reshape(-1)
+    out = np.zeros((n_tokens,) + cache.shape[2:])
+    for t0 in range(0, n_tokens, page_size):
+        n = min(page_size, n_tokens - t0)
+        out[t0:t0 + n] = cache[int(table[t0 // page_size]), :n]
+    return out
+
+
+def decode_paged_ref(q, k_cache, v_cache, block_table, kv_len, page_size: int, scale: float,
+                     sinks=None):
+    """Single-token decode over a paged KV cache (block table), fp64.
+
+    The pages name a paged KV cache as a separate kernel variant ("paged vs
+    dense", hard rules of the optimize-fa4-blackwell skill page) and as part
+    of the cache infrastructure (DSV4 status page, "KV cache infra" row) but
+    fix no layout.  Reading used: the cache is a pool of fixed-size pages
+    [n_pages, page_size, h_kv, d]; row b of block_table lists the pages of
+    sequence b in token order, so token t of the sequence is slot
+    t % page_size of page block_table[b][t // page_size].  The attention is
+    then exactly decode_ref over the gathered keys and values.
+    Returns O [B,h_q,d], LSE [B,h_q].
+    """
+    q = _as_f64(q)
+    lens = np.asarray(kv_len, dtype=np.int64).reshape(-1)
+    B, h_q, d = q.shape
+    out = np.zeros((B, h_q, d))
+    lse = np.zeros((B, h_q))
+    table = np.asarray(block_table)
+    for bi in range(B):
+        n = int(lens[bi])
+        kb = np.transpose(gather_pages(k_cache, table[bi], n, page_size), (1, 0, 2))[None]
+        vb = np.transpose(gather_pages(v_cache, table[bi], n, page_size), (1, 0, 2))[None]
+        o, l = attention_ref(q[bi][None, :, None, :], kb, vb, scale, sinks=sinks)
+        out[bi] = o[0, :, 0]
+        lse[bi] = l[0, :, 0]
+    return out, lse
 
 
 def attention_flops(b: int, h_q: int, s_q: int, s_k: int, d: int, causal: bool,

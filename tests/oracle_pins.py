@@ -12,6 +12,7 @@ disagrees with:
   window limits, GQA = MHA on repeated heads, hard attention through a
   permutation, empty rows, the flop count,
 * a textbook routine: torch's CPU fp64 ``scaled_dot_product_attention``,
+* the paged-cache decode against the brute force on the keys it scattered,
 * the streaming recurrence and the split/merge reformulation, and the
   negative result that merging head-dim halves is NOT attention.
 
@@ -367,6 +368,47 @@ def pin_decode_matches_brute(orc):
             _close(l[bi], bl[0, :, 0], 1e-12, "decode LSE")
 
 
+def pin_paged_decode_matches_brute(orc):
+    """Decode through a block table equals the brute force on each sequence's own keys.
+
+    The keys and values are drawn per sequence, then scattered to randomly
+    chosen physical pages of a pool whose other slots hold NaN, so reading a
+    wrong page or slot shows up as NaN or as a wrong value.
+    """
+    rng = _rng(25)
+    B, h_q, h_kv, d = 3, 4, 2, 4
+    lens = [7, 1, 12]
+    sig = np.array([0.5, -1.0, 2.0, 0.0])
+    for P in (1, 3, 4, 16):
+        n_pages = sum(-(-L // P) for L in lens) + 5
+        kc = np.full((n_pages, P, h_kv, d), np.nan)
+        vc = np.full((n_pages, P, h_kv, d), np.nan)
+        perm = rng.permutation(n_pages)
+        table = np.full((B, max(-(-L // P) for L in lens)), -1, dtype=np.int64)
+        q = rng.standard_normal((B, h_q, d))
+        keys, vals, used = [], [], 0
+        for bi, L in enumerate(lens):
+            kb = rng.standard_normal((L, h_kv, d))
+            vb = rng.standard_normal((L, h_kv, d))
+            keys.append(kb)
+            vals.append(vb)
+            for pg in range(-(-L // P)):
+                phys = int(perm[used])
+                used += 1
+                table[bi, pg] = phys
+                n = min(P, L - pg * P)
+                kc[phys, :n] = kb[pg * P:pg * P + n]
+                vc[phys, :n] = vb[pg * P:pg * P + n]
+        for sinks in (None, sig):
+            o, l = orc.decode_paged_ref(q, kc, vc, table, np.array(lens), P, 0.45, sinks=sinks)
+            for bi in range(B):
+                kb = np.transpose(keys[bi], (1, 0, 2))[None]
+                vb = np.transpose(vals[bi], (1, 0, 2))[None]
+                bo, bl = brute_force(q[bi][None, :, None, :], kb, vb, 0.45, False, 0, sinks)
+                _close(o[bi], bo[0, :, 0], 1e-12, f"paged decode O (page size {P})")
+                _close(l[bi], bl[0, :, 0], 1e-12, f"paged decode LSE (page size {P})")
+
+
 def pin_split_merge_equals_unsplit(orc):
     """Split-KV partials merged by LSE equal the unsplit decode (disjoint key sets)."""
     q, k, v, starts, lens = _decode_case(23)
@@ -434,6 +476,7 @@ PINS = [
     pin_textbook_sdpa,
     pin_online_equals_plain,
     pin_decode_matches_brute,
+    pin_paged_decode_matches_brute,
     pin_split_merge_equals_unsplit,
     pin_head_dim_halves_do_not_merge,
     pin_flop_count,

@@ -48,6 +48,12 @@ MUTATIONS = [
     ("split drops a key", "j1 = min(int(lens[bi]), j0 + split)", "j1 = min(int(lens[bi]), j0 + split - 1)"),
     ("decode window of sequence shifted", "kb = np.transpose(k[s0:s0 + n], (1, 0, 2))[None]",
      "kb = np.transpose(k[s0 + 1:s0 + n + 1], (1, 0, 2))[None]"),
+    ("paged: next page read", "out[t0:t0 + n] = cache[int(table[t0 // page_size]), :n]",
+     "out[t0:t0 + n] = cache[int(table[t0 // page_size + 1]), :n]"),
+    ("paged: slot offset", "out[t0:t0 + n] = cache[int(table[t0 // page_size]), :n]",
+     "out[t0:t0 + n] = cache[int(table[t0 // page_size]), 1:n + 1]"),
+    ("paged: page index by slot", "out[t0:t0 + n] = cache[int(table[t0 // page_size]), :n]",
+     "out[t0:t0 + n] = cache[int(table[t0 % page_size]), :n]"),
     ("flops count 2d per pair", "return 4 * d * pairs * b * h_q", "return 2 * d * pairs * b * h_q"),
 ]
 
