@@ -61,6 +61,24 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class DecodePagedArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("kv_len", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("sinks", ctypes.c_void_p),
+        ("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32), ("split_size", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+        ("bt_stride", ctypes.c_int64),
+        ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("k_ps", ctypes.c_int64), ("k_ts", ctypes.c_int64), ("k_sh", ctypes.c_int64),
+        ("v_ps", ctypes.c_int64), ("v_ts", ctypes.c_int64), ("v_sh", ctypes.c_int64),
+        ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("lse_sb", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+    ]
+
+
 class CombineArgs(ctypes.Structure):
     _fields_ = [
         ("o_parts", ctypes.c_void_p), ("lse_parts", ctypes.c_void_p),
@@ -90,6 +108,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_void_p]
     lib.attn_fwd_decode.restype = ctypes.c_int
+    lib.attn_fwd_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p]
+    lib.attn_fwd_decode_paged.restype = ctypes.c_int
     lib.attn_combine.argtypes = [ctypes.POINTER(CombineArgs), ctypes.c_void_p]
     lib.attn_combine.restype = ctypes.c_int
     lib.attn_fwd_decode_workspace_size.argtypes = [ctypes.c_int32] * 5
@@ -242,6 +263,63 @@ def decode(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = 
     a.scale = scale
     _check(lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def decode_paged(q, k_cache, v_cache, block_table, kv_len, max_kv_len: int, *, scale: float | None = None,
+                 sinks=None, split_size: int = 512, workspace=None, out=None, lse=None,
+                 return_lse: bool = True, stream=None):
+    """Single-token decode over a paged KV cache (block table), split-KV + LSE merge.
+
+    q: bf16 [B, h_q, d]; k_cache, v_cache: bf16 [n_pages, page_size, h_kv, d]
+    (any page, token and head strides with a unit head-dim stride);
+    block_table: int32 [B, max_pages] (row b lists the pages of sequence b in
+    token order); kv_len: int32 [B]; max_kv_len: host upper bound on kv_len.
+    Returns (O bf16 [B, h_q, d], LSE fp32 [B, h_q] or None).
+    """
+    import torch
+
+    lib = load_library()
+    _require_cuda_bf16("q", q, 3)
+    _require_cuda_bf16("k_cache", k_cache, 4)
+    _require_cuda_bf16("v_cache", v_cache, 4)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [B, max_pages] with unit column stride")
+    if kv_len.dtype != torch.int32:
+        raise ValueError("kv_len must be int32")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    B, h_q, d = q.shape
+    n_pages, page_size, h_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = int(lib.attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, h_q), dtype=torch.float32, device=q.device)
+    if lse is not None and lse.stride(-1) != 1:
+        raise ValueError("lse must have unit stride along the heads")
+    a = DecodePagedArgs()
+    a.q, a.k, a.v = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+    a.block_table, a.kv_len = block_table.data_ptr(), kv_len.data_ptr()
+    a.o = out.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.B, a.h_q, a.h_kv, a.d = B, h_q, h_kv, d
+    a.max_kv_len, a.split_size = int(max_kv_len), int(split_size)
+    a.page_size, a.n_pages = int(page_size), int(n_pages)
+    a.bt_stride = block_table.stride(0)
+    a.q_sb, a.q_sh = q.stride(0), q.stride(1)
+    a.k_ps, a.k_ts, a.k_sh = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    a.v_ps, a.v_ts, a.v_sh = v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)
+    a.o_sb, a.o_sh = out.stride(0), out.stride(1)
+    a.lse_sb = lse.stride(0) if lse is not None else 0
+    a.scale = scale
+    _check(lib.attn_fwd_decode_paged(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 

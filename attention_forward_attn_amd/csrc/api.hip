@@ -49,6 +49,66 @@ attn_status hip_fail(hipError_t e, const char *what) {
   return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Shared tail of the dense and paged decode entry points (arguments already
+// validated; p carries the K/V addressing): grid check, workspace layout, the
+// split kernel and the combine kernel.
+attn_status run_decode(attn::DecodeParams &p, const int32_t *kv_len, const float *sinks, void *o, float *lse,
+                       int32_t B, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_kv_len, int32_t split_size,
+                       int64_t q_sb, int64_t q_sh, int64_t o_sb, int64_t o_sh, int64_t lse_sb, float scale,
+                       bool paged, void *workspace, void *stream) {
+  const int bm = attn::decode_block_rows(d);
+  const int ratio = h_q / h_kv;
+  const int64_t n_split = max_kv_len > 0 ? (max_kv_len + split_size - 1) / split_size : 1;
+  const int64_t n_hblk = (ratio + bm - 1) / bm;
+  if (attn::decode_grid_size(n_split, B, h_kv, n_hblk) > INT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "decode grid too large: splits x B x kv heads x head blocks must fit in int32");
+
+  const int64_t parts = (int64_t)B * h_q * n_split;
+  const int64_t o_bytes = parts * d * 2;
+  uint16_t *o_part = static_cast<uint16_t *>(workspace);
+  float *lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + (o_bytes + 255) / 256 * 256);
+
+  p.kv_len = kv_len;
+  p.sinks = sinks;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.q_sb = q_sb; p.q_sh = q_sh;
+  p.B = B; p.h_q = h_q; p.h_kv = h_kv; p.ratio = ratio;
+  p.n_split = (int32_t)n_split;
+  p.split = split_size;
+  p.n_hblk = (int32_t)n_hblk;
+  p.c = scale * attn::kLog2e;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = paged ? attn::decode_split_paged(d, p, s) : attn::decode_split(d, p, s);
+  if (e != hipSuccess) return hip_fail(e, "decode split launch");
+
+  attn::CombineParams c;
+  c.o_parts = o_part;
+  c.lse_parts = lse_part;
+  c.o_out = static_cast<uint16_t *>(o);
+  c.lse_out = lse;
+  c.n_parts = (int32_t)n_split;
+  c.rows = B * h_q;
+  c.n2 = h_q;
+  c.d = d;
+  c.o_part_stride = d;
+  c.o_r1 = (int64_t)h_q * n_split * d;
+  c.o_r2 = n_split * d;
+  c.lse_part_stride = 1;
+  c.lse_r1 = (int64_t)h_q * n_split;
+  c.lse_r2 = n_split;
+  c.out_r1 = o_sb;
+  c.out_r2 = o_sh;
+  c.lse_out_r1 = lse_sb;
+  c.lse_out_r2 = 1;
+  c.kv_len = kv_len;
+  c.split = split_size;
+  e = attn::combine_bf16(c, s);
+  if (e != hipSuccess) return hip_fail(e, "decode combine launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,64 +246,73 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
                 workspace ? "" : ", NULL");
   if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
 
-  const int bm = attn::decode_block_rows(a->d);
-  const int ratio = a->h_q / a->h_kv;
-  const int64_t n_split = a->max_kv_len > 0 ? (a->max_kv_len + a->split_size - 1) / a->split_size : 1;
-  const int64_t n_hblk = (ratio + bm - 1) / bm;
-  if (attn::decode_grid_size(n_split, a->B, a->h_kv, n_hblk) > INT32_MAX)
-    return fail(ATTN_ERR_SHAPE, "decode grid too large: splits x B x kv heads x head blocks must fit in int32");
-
-  const int64_t parts = (int64_t)a->B * a->h_q * n_split;
-  const int64_t o_bytes = parts * a->d * 2;
-  uint16_t *o_part = static_cast<uint16_t *>(workspace);
-  float *lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + (o_bytes + 255) / 256 * 256);
-
-  attn::DecodeParams p;
+  attn::DecodeParams p{};
   p.q = static_cast<const uint16_t *>(a->q);
   p.k = static_cast<const uint16_t *>(a->k);
   p.v = static_cast<const uint16_t *>(a->v);
   p.kv_start = a->kv_start;
-  p.kv_len = a->kv_len;
-  p.sinks = a->sinks;
-  p.o_part = o_part;
-  p.lse_part = lse_part;
-  p.q_sb = a->q_sb; p.q_sh = a->q_sh;
   p.k_st = a->k_st; p.k_sh = a->k_sh;
   p.v_st = a->v_st; p.v_sh = a->v_sh;
-  p.B = a->B; p.h_q = a->h_q; p.h_kv = a->h_kv; p.ratio = ratio;
-  p.n_split = (int32_t)n_split;
-  p.split = a->split_size;
-  p.n_hblk = (int32_t)n_hblk;
-  p.c = a->scale * attn::kLog2e;
+  return run_decode(p, a->kv_len, a->sinks, a->o, a->lse, a->B, a->h_q, a->h_kv, a->d, a->max_kv_len,
+                    a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, false, workspace,
+                    stream);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = attn::decode_split(a->d, p, s);
-  if (e != hipSuccess) return hip_fail(e, "decode split launch");
+attn_status attn_fwd_decode_paged(const attn_decode_paged_args *a, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
+  if (a->B < 1 || a->h_q < 1 || a->h_kv < 1)
+    return fail(ATTN_ERR_SHAPE, "need B, h_q, h_kv >= 1");
+  if (a->h_q % a->h_kv != 0)
+    return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
+  if (a->d != 64 && a->d != 128 && a->d != 256)
+    return fail(ATTN_ERR_SHAPE, "decode d must be 64, 128 or 256 (got %d)", a->d);
+  if (a->max_kv_len < 0) return fail(ATTN_ERR_SHAPE, "max_kv_len must be >= 0");
+  if (a->split_size < 64 || a->split_size % 64 != 0)
+    return fail(ATTN_ERR_SHAPE, "split_size must be a positive multiple of 64 (got %d)", a->split_size);
+  const int ps = a->page_size;
+  if (ps < 16 || (ps & (ps - 1)) != 0 || ps > a->split_size || a->split_size / ps > 64)
+    return fail(ATTN_ERR_SHAPE,
+                "page_size must be a power of two in [16, split_size] with at most 64 pages per split (got %d)", ps);
+  if (a->n_pages < 1) return fail(ATTN_ERR_SHAPE, "n_pages must be >= 1");
+  const int64_t max_pages = ((int64_t)a->max_kv_len + ps - 1) / ps;
+  if (a->bt_stride < max_pages)
+    return fail(ATTN_ERR_STRIDE, "bt_stride (%lld) must be >= ceil(max_kv_len / page_size) = %lld",
+                (long long)a->bt_stride, (long long)max_pages);
+  if (!(std::isfinite(a->scale) && a->scale > 0.0f))
+    return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+  if (!a->q || !a->k || !a->v || !a->o || !a->block_table || !a->kv_len)
+    return fail(ATTN_ERR_NULL, "q, k, v, o, block_table and kv_len must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(ATTN_ERR_ALIGN, "q, k, v, o must be 16-byte aligned");
+  if (!aligned4(a->block_table) || !aligned4(a->kv_len) || (a->lse && !aligned4(a->lse)) ||
+      (a->sinks && !aligned4(a->sinks)))
+    return fail(ATTN_ERR_ALIGN, "block_table, kv_len, lse and sinks must be 4-byte aligned");
+  const int64_t st[] = {a->q_sb, a->q_sh, a->k_ps, a->k_ts, a->k_sh, a->v_ps, a->v_ts, a->v_sh, a->o_sb, a->o_sh};
+  for (int64_t s : st)
+    if (!bf16_stride_ok(s)) return fail(ATTN_ERR_STRIDE, "bf16 strides must be non-negative multiples of 8 elements");
+  if (a->lse && a->lse_sb < 0) return fail(ATTN_ERR_STRIDE, "lse_sb must be >= 0");
+  if (a->k_ts >= kMaxRowStride || a->v_ts >= kMaxRowStride)
+    return fail(ATTN_ERR_STRIDE, "k/v token strides must be below 2^24 elements");
+  const size_t need = attn_fwd_decode_workspace_size(a->B, a->h_q, a->d, a->max_kv_len, a->split_size);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
 
-  attn::CombineParams c;
-  c.o_parts = o_part;
-  c.lse_parts = lse_part;
-  c.o_out = static_cast<uint16_t *>(a->o);
-  c.lse_out = a->lse;
-  c.n_parts = (int32_t)n_split;
-  c.rows = a->B * a->h_q;
-  c.n2 = a->h_q;
-  c.d = a->d;
-  c.o_part_stride = a->d;
-  c.o_r1 = (int64_t)a->h_q * n_split * a->d;
-  c.o_r2 = n_split * a->d;
-  c.lse_part_stride = 1;
-  c.lse_r1 = (int64_t)a->h_q * n_split;
-  c.lse_r2 = n_split;
-  c.out_r1 = a->o_sb;
-  c.out_r2 = a->o_sh;
-  c.lse_out_r1 = a->lse_sb;
-  c.lse_out_r2 = 1;
-  c.kv_len = a->kv_len;
-  c.split = a->split_size;
-  e = attn::combine_bf16(c, s);
-  if (e != hipSuccess) return hip_fail(e, "decode combine launch");
-  return ok();
+  attn::DecodeParams p{};
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k = static_cast<const uint16_t *>(a->k);
+  p.v = static_cast<const uint16_t *>(a->v);
+  p.block_table = a->block_table;
+  p.bt_stride = a->bt_stride;
+  p.k_ps = a->k_ps; p.k_st = a->k_ts; p.k_sh = a->k_sh;
+  p.v_ps = a->v_ps; p.v_st = a->v_ts; p.v_sh = a->v_sh;
+  p.page_shift = __builtin_ctz((unsigned)ps);
+  p.n_pages = a->n_pages;
+  return run_decode(p, a->kv_len, a->sinks, a->o, a->lse, a->B, a->h_q, a->h_kv, a->d, a->max_kv_len,
+                    a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, true, workspace,
+                    stream);
 }
 
 attn_status attn_combine(const attn_combine_args *a, void *stream) {

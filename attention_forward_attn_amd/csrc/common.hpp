@@ -50,6 +50,13 @@ struct DecodeParams {
   int32_t B, h_q, h_kv, ratio;
   int32_t n_split, split;
   int32_t n_hblk;  // head blocks per kv group: ceil(ratio / BM)
+  // Paged cache only: token j of sequence b is row j % 2^page_shift of page
+  // block_table[b * bt_stride + j >> page_shift], at k + page * k_ps + row * k_st
+  // (+ g * k_sh); kv_start is unused.
+  const int32_t *block_table;
+  int64_t bt_stride;
+  int64_t k_ps, v_ps;
+  int32_t page_shift, n_pages;
   float c;
 };
 

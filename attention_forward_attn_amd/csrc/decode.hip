@@ -15,6 +15,14 @@ hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s) {
   }
 }
 
+hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_decode_split<64, 4, 1, 64, 2, 4, true>(p, s);
+    case 128: return launch_decode_split<128, 4, 1, 32, 2, 3, true>(p, s);
+    default: return launch_decode_split<256, 4, 1, 32, 2, 1, true>(p, s);
+  }
+}
+
 hipError_t combine(const CombineParams &p, hipStream_t s) { return launch_combine<float>(p, s); }
 hipError_t combine_bf16(const CombineParams &p, hipStream_t s) { return launch_combine<uint16_t>(p, s); }
 

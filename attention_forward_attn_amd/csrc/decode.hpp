@@ -100,7 +100,9 @@ __device__ bool decode_unit(const DecodeParams &p, int u, int lane, int len0, in
 }
 
 // HG head groups of 32 heads x KG key groups of BN/KG keys = HG*KG waves.
-template <int D, int HG, int KG, int BN, int STAGES, int OCC>
+// PAGED: K/V are read through the block table (one descriptor per DMA load,
+// see Tile::dma1_paged) instead of from a per-sequence contiguous range.
+template <int D, int HG, int KG, int BN, int STAGES, int OCC, bool PAGED = false>
 __global__ __launch_bounds__(HG * KG * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_split_kernel(DecodeParams p) {
   constexpr int NW = HG * KG;
@@ -122,7 +124,7 @@ void decode_split_kernel(DecodeParams p) {
   // Lengths and starts of the first 64 sequences are loaded once, side by
   // side, so the unit scan and this unit's key range wait for one load.
   const int len0 = lane < p.B ? p.kv_len[lane] : 0;
-  const int64_t start0 = lane < p.B ? p.kv_start[lane] : 0;
+  const int64_t start0 = !PAGED && lane < p.B ? p.kv_start[lane] : 0;
   int split_, bi_, g_, hb_;
   if (!decode_unit(p, blockIdx.x, lane, len0, split_, bi_, g_, hb_)) return;
   const int split = __builtin_amdgcn_readfirstlane(split_);
@@ -139,25 +141,40 @@ void decode_split_kernel(DecodeParams p) {
   const int64_t part = ((int64_t)bi * p.h_q + head) * p.n_split + split;
 
   const int64_t start =
-      bi < 64 ? (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(start0 >> 32), bi) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((int)start0, bi))
-              : p.kv_start[bi];
-  const uint16_t *kbase = p.k + (start + kbeg) * p.k_st + g * p.k_sh;
-  const uint16_t *vbase = p.v + (start + kbeg) * p.v_st + g * p.v_sh;
+      PAGED ? 0
+      : bi < 64 ? (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(start0 >> 32), bi) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)start0, bi))
+                : p.kv_start[bi];
+  // Dense: the split's first key.  Paged: the kv head's base; the pages of
+  // this split (at most 64) are read once into lane-wise registers.
+  const uint16_t *kbase = p.k + (PAGED ? 0 : (start + kbeg) * p.k_st) + g * p.k_sh;
+  const uint16_t *vbase = p.v + (PAGED ? 0 : (start + kbeg) * p.v_st) + g * p.v_sh;
   const int n_keys = max(kend - kbeg, 0);
+  int pg = 0;
+  if constexpr (PAGED) {
+    const int n_pg = (n_keys + (1 << p.page_shift) - 1) >> p.page_shift;
+    if (lane < n_pg) pg = p.block_table[(int64_t)bi * p.bt_stride + (kbeg >> p.page_shift) + lane];
+  }
   const int n_tiles = (n_keys + BN - 1) / BN;
   const bool wave_ok = hb * BM + hgrp * 32 < p.ratio;
 
   typename TD::Lane dl;
-  TD::init_dma(dl, p.k_st, p.v_st, wave, lane);
+  if constexpr (PAGED) TD::init_dma_paged(dl, p.k_st, p.v_st, wave, lane);
+  else TD::init_dma(dl, p.k_st, p.v_st, wave, lane);
+  auto load_tile = [&](uint16_t *stage, int t) {
+    if constexpr (PAGED)
+      TD::dma_paged(dl, stage, kbase, p.k_st, p.k_ps, vbase, p.v_st, p.v_ps, pg, p.page_shift, p.n_pages, t * BN,
+                    n_keys, wave);
+    else
+      TD::dma(dl, stage, kbase, p.k_st, vbase, p.v_st, t * BN, n_keys, wave);
+  };
   typename TC::Lane ml;
   const uint32_t base = lds_offset(smem);
   TC::init_mma(ml, base + kgrp * (BN / KG) * D * 2, base + TD::TILE_BYTES + kgrp * (BN / KG) * D * 2, lane);
 
   // Prologue: tiles 0 .. STAGES-2 in flight.
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    TD::dma(dl, smem + s * (TD::STAGE_BYTES / 2), kbase, p.k_st, vbase, p.v_st, s * BN, n_keys, wave);
+  for (int s = 0; s < STAGES - 1; ++s) load_tile(smem + s * (TD::STAGE_BYTES / 2), s);
 
   u32x4 qreg[TC::NKK];
   {
@@ -179,8 +196,7 @@ void decode_split_kernel(DecodeParams p) {
     wait_vmcnt<(STAGES - 2) * 2 * TD::LOADS>();  // this wave's loads of tile t have landed
     barrier_nofence();                            // everyone's have; tile t-1's stage is free
     const int nxt = t + STAGES - 1;
-    TD::dma(dl, smem + (nxt % STAGES) * (TD::STAGE_BYTES / 2), kbase, p.k_st, vbase, p.v_st, nxt * BN,
-            n_keys, wave);
+    load_tile(smem + (nxt % STAGES) * (TD::STAGE_BYTES / 2), nxt);
     const uint32_t stage_off = (t % STAGES) * TD::STAGE_BYTES;
     const int j0 = t * BN + kgrp * (BN / KG);  // first key of this wave's part of the tile
     if (wave_ok && j0 < n_keys) {
@@ -286,10 +302,11 @@ void decode_split_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int HG, int KG, int BN, int STAGES, int OCC>
+template <int D, int HG, int KG, int BN, int STAGES, int OCC, bool PAGED = false>
 hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream) {
   dim3 grid((unsigned)decode_grid_size(p.n_split, p.B, p.h_kv, p.n_hblk));
-  hipLaunchKernelGGL((decode_split_kernel<D, HG, KG, BN, STAGES, OCC>), grid, dim3(HG * KG * 64), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, HG, KG, BN, STAGES, OCC, PAGED>), grid, dim3(HG * KG * 64), 0, stream,
+                     p);
   return hipGetLastError();
 }
 

@@ -19,6 +19,8 @@ hipError_t prefill_d512(const PrefillParams &p, int mask, int n_units, hipStream
 // Query heads per decode workgroup (0 if unsupported).
 int decode_block_rows(int d);
 hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s);
+// The same over a paged cache (p.block_table, p.page_shift, p.k_ps, p.v_ps set).
+hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s);
 
 // LSE merge of fp32 partials (public entry point) / of bf16 partials (decode).
 hipError_t combine(const CombineParams &p, hipStream_t s);

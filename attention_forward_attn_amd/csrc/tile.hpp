@@ -257,6 +257,48 @@ struct Tile {
     dma1(ln, false, stage, kbase, k_rs, j0, nkeys, w);
     dma1(ln, true, stage + TILE_ELEMS, vbase, v_rs, j0, nkeys, w);
   }
+  // Paged caches: a load's 64/CH consecutive tile rows always sit in one page
+  // (pages hold at least 16 rows), so each load gets its own descriptor and
+  // the lane offsets are taken from the load's first row.
+  __device__ static __forceinline__ void init_dma_paged(Lane &ln, int64_t k_rs, int64_t v_rs, int w, int lane) {
+    static_assert(LOADS_EXACT * 64 * NW * 8 == TILE_ELEMS && 64 % CH == 0, "whole loads of whole rows");
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int pch = (u * NW + w) * 64 + lane;
+      const int r = pch / CH, rl = lane / CH;  // row in the tile, row in the load
+      ln.kg[u] = (uint32_t)(rl * k_rs * 2) + (uint32_t)(((pch % CH) ^ kswz(r)) * 16);
+      ln.vg[u] = (uint32_t)(rl * v_rs * 2) + (uint32_t)(((pch % CH) ^ vswz(r)) * 16);
+    }
+  }
+  // This wave's loads of the tile whose first key is jt (keys counted from the
+  // start of a run of pages): key j of the run is row j % 2^shift of page
+  // readlane(pg, j >> shift) at `head` + page * page_rs + row * rs.  Rows at or
+  // past nkeys, and pages outside [0, n_pages), read as zero without touching
+  // memory.  jt and w must be wave-uniform.
+  __device__ static __forceinline__ void dma1_paged(const Lane &ln, bool is_v, uint16_t *dst, const uint16_t *head,
+                                                    int64_t rs, int64_t page_rs, int pg, int shift, int n_pages,
+                                                    int jt, int nkeys, int w) {
+    constexpr int RPL = 64 / CH;  // rows per load
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int key = jt + (u * NW + w) * RPL;
+      const int nv = min(nkeys - key, RPL);
+      const int page = __builtin_amdgcn_readlane(pg, min(key >> shift, 63));
+      const bool ok = nv > 0 && (uint32_t)page < (uint32_t)n_pages;
+      const uint16_t *base = head + (int64_t)page * page_rs + (int64_t)(key & ((1 << shift) - 1)) * rs;
+      const uint32_t bytes = ok ? (uint32_t)((nv - 1) * rs * 2 + D * 2) : 0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(ok ? base : head, bytes),
+                                               (lds_void *)(dst + (u * NW + w) * 512), 16,
+                                               is_v ? ln.vg[u] : ln.kg[u], 0, 0, 0);
+    }
+  }
+  __device__ static __forceinline__ void dma_paged(const Lane &ln, uint16_t *stage, const uint16_t *khead,
+                                                   int64_t k_rs, int64_t k_page_rs, const uint16_t *vhead,
+                                                   int64_t v_rs, int64_t v_page_rs, int pg, int shift,
+                                                   int n_pages, int jt, int nkeys, int w) {
+    dma1_paged(ln, false, stage, khead, k_rs, k_page_rs, pg, shift, n_pages, jt, nkeys, w);
+    dma1_paged(ln, true, stage + TILE_ELEMS, vhead, v_rs, v_page_rs, pg, shift, n_pages, jt, nkeys, w);
+  }
   // The same loads, issued from inside an MMA schedule: step<G>() issues the
   // K share after MMA group GK and the V share after group GV.
   template <int GK, int GV>

@@ -9,7 +9,10 @@ lengths first (decode only), then Q, K, V, then sink logits.  Values are fp32
 N(0, 1) rounded to bf16 with round-to-nearest-even; sinks stay fp32 N(0, 1).
 Prefill tensors are [b, h, s, d] contiguous; the decode KV cache is packed
 token-major, [sum_b L_b, h_kv, d], contiguous per sequence, with ``kv_start``
-the exclusive prefix sum of the lengths.
+the exclusive prefix sum of the lengths.  A paged cache holds the same draw
+in pages of ``page_size`` tokens, [n_pages, page_size, h_kv, d]; the pages of
+all sequences (plus ``spare`` unused ones) are placed in a random order drawn
+from a second generator (seed + 7919), so the values match the packed draw.
 """
 
 from __future__ import annotations
@@ -41,6 +44,7 @@ class Workload:
     len_lo: int = 0
     len_hi: int = 0
     split: int = 512
+    page_size: int = 0  # paged KV cache (0 = contiguous per sequence)
     notes: dict = field(default_factory=dict, compare=False)
 
 
@@ -74,6 +78,9 @@ WORKLOADS = {
            len_lo=1024, len_hi=8192),
         _w("mqa_decode_B64_hq128_d256", "decode", BASE_SEED + 3, 256, 128, 1, b=64,
            len_lo=1024, len_hi=8192),
+        # the same draw held in a paged cache of 64-token pages
+        _w("mqa_decode_paged_B64_hq128_d128_p64", "decode", BASE_SEED + 3, 128, 128, 1, b=64,
+           len_lo=1024, len_hi=8192, page_size=64),
         # family 4: large head dims, long context
         _w("long_b1_h8_s16384_d256_causal", "prefill", BASE_SEED + 4, 256, 8, 8, b=1,
            s_q=16384, s_k=16384, causal=True),
@@ -123,4 +130,40 @@ def workload_inputs(w: Workload):
     """Inputs of a named workload (see WORKLOADS)."""
     if w.kind == "prefill":
         return prefill_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed, w.sinks)
+    if w.page_size:
+        return paged_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.page_size, w.seed, w.sinks)
     return decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed, w.sinks)
+
+
+def paged_decode_inputs(B: int, h_q: int, h_kv: int, d: int, len_lo: int, len_hi: int, page_size: int,
+                        seed: int, with_sinks: bool = False, spare: int = 0, poison: bool = False):
+    """The draw of decode_inputs laid out in a paged cache.
+
+    Returns decode_inputs' dict plus k_cache, v_cache (bf16 [n_pages,
+    page_size, h_kv, d]), block_table (int32 [B, ceil(len_hi / page_size)];
+    entries past a sequence's pages are -1) and page_size.  Slots that hold no token are
+    zero, or NaN with poison=True (so that reading one shows).
+    """
+    inp = decode_inputs(B, h_q, h_kv, d, len_lo, len_hi, seed, with_sinks)
+    lens = [int(x) for x in inp["kv_len"]]
+    starts = [int(x) for x in inp["kv_start"]]
+    n_used = sum(-(-L // page_size) for L in lens)
+    n_pages = max(1, n_used + spare)
+    perm = torch.randperm(n_pages, generator=torch.Generator("cpu").manual_seed(seed + 7919))
+    fill = float("nan") if poison else 0.0
+    kc = torch.full((n_pages, page_size, h_kv, d), fill, dtype=torch.bfloat16)
+    vc = torch.full((n_pages, page_size, h_kv, d), fill, dtype=torch.bfloat16)
+    max_pages = max(1, -(-len_hi // page_size))  # the table is sized for the longest possible sequence
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    used = 0
+    for b, (s0, L) in enumerate(zip(starts, lens)):
+        for pg in range(-(-L // page_size)):
+            phys = int(perm[used])
+            used += 1
+            table[b, pg] = phys
+            n = min(page_size, L - pg * page_size)
+            kc[phys, :n] = inp["k"][s0 + pg * page_size:s0 + pg * page_size + n]
+            vc[phys, :n] = inp["v"][s0 + pg * page_size:s0 + pg * page_size + n]
+    inp.update(k_cache=kc, v_cache=vc, block_table=table, page_size=page_size)
+    return inp
+

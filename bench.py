@@ -243,6 +243,43 @@ def roofline_decode(nbytes: int, ms: float, traffic=None):
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
 
 
+class PagedDecodeCase(DecodeCase):
+    """The decode workload held in a paged cache (block table of page_size-token pages)."""
+
+    def __init__(self, w, n_sets: int, dev):
+        import torch
+
+        import attention_forward_attn_amd as afa
+        from attention_forward_attn_amd.inputs import paged_decode_inputs
+
+        self.w = w
+        base = paged_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.page_size, w.seed, w.sinks)
+        self.total = int(base["kv_len"].sum())
+        self.max_len = int(base["kv_len"].max())
+        self.kv_len = base["kv_len"].to(dev)
+        self.table = base["block_table"].to(dev)
+        self.sets = [{"q": base["q"].to(dev), "k": base["k_cache"].to(dev), "v": base["v_cache"].to(dev)}]
+        gen = torch.Generator(device=dev).manual_seed(w.seed + 1)
+        for _ in range(1, n_sets):
+            self.sets.append({n: torch.randn(t.shape, generator=gen, device=dev).to(torch.bfloat16)
+                              for n, t in self.sets[0].items()})
+        self.sinks = base["sinks"].to(dev) if base["sinks"] is not None else None
+        self.scale = 1.0 / math.sqrt(w.d)
+        self.ws = torch.empty(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
+                              dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.b, w.h_q, w.d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.b, w.h_q), dtype=torch.float32, device=dev)
+        self.bytes = decode_bytes(w, self.total)
+
+    def run(self, i: int):
+        import attention_forward_attn_amd as afa
+
+        s = self.sets[i % len(self.sets)]
+        afa.decode_paged(s["q"], s["k"], s["v"], self.table, self.kv_len, self.max_len,
+                         scale=self.scale, sinks=self.sinks, split_size=self.w.split, workspace=self.ws,
+                         out=self.out, lse=self.lse)
+
+
 def bench_one(name: str, steps: int, warmup: int, dev):
     """One JSON line for one named workload (prefill or decode) alone."""
     from attention_forward_attn_amd.inputs import WORKLOADS
@@ -254,7 +291,7 @@ def bench_one(name: str, steps: int, warmup: int, dev):
         r = roofline_prefill(c.flops, ms)
         return {"workload": name, "kind": "prefill", "ms": round(ms, 4), "TFLOP/s": r["achieved"],
                 "frac_of_peak": r["frac"], "gflop": round(c.flops / 1e9, 2)}
-    c = DecodeCase(w, 4 if w.d <= 128 else 2, dev)
+    c = (PagedDecodeCase if w.page_size else DecodeCase)(w, 4 if w.d <= 128 else 2, dev)
     (ms,), wall = timed([c], steps, warmup)
     r = roofline_decode(c.bytes, ms)
     return {"workload": name, "kind": "decode", "ms": round(ms, 4), "GB/s": r["achieved"],

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 1
+#define ATTN_FWD_ABI_VERSION 2
 
 typedef enum {
   ATTN_OK = 0,
@@ -149,12 +149,57 @@ typedef struct {
 } attn_decode_args;
 
 /*
+ * Decode over a paged KV cache: the same operation, split kernel and combine
+ * as attn_fwd_decode; only the addressing of K and V differs.  The pages name
+ * paged and dense caches as separate kernel variants (optimize-fa4-blackwell
+ * skill page, hard rules) and a paged cache among the serving infrastructure
+ * (DSV4 status page, "KV cache infra" row) without fixing a layout; the one
+ * taken here is a pool of pages of page_size tokens, with row bi of a block
+ * table listing the pages of sequence bi in token order.  Token tok of
+ * sequence bi, kv head g is at
+ *     k + block_table[bi*bt_stride + tok/page_size]*k_ps + (tok % page_size)*k_ts + g*k_sh
+ * (v: v_ps, v_ts, v_sh).
+ *
+ * block_table: DEVICE int32; row bi must list ceil(kv_len[bi]/page_size) page
+ *       indices in [0, n_pages); entries past those are not read.  A page index
+ *       outside [0, n_pages) is never dereferenced: its tokens read as zeros
+ *       (a wrong result, not a fault).
+ * page_size: a power of two in [16, split_size] with split_size/page_size <= 64;
+ *       bt_stride >= ceil(max_kv_len/page_size).
+ * Other fields, the workspace (attn_fwd_decode_workspace_size with the same
+ * sizes), its ownership and the supported sizes are those of attn_fwd_decode.
+ */
+typedef struct {
+  const void *q;
+  const void *k;
+  const void *v;
+  const int32_t *block_table;
+  const int32_t *kv_len;
+  void *o;
+  float *lse;
+  const float *sinks;
+  int32_t B, h_q, h_kv, d;
+  int32_t max_kv_len;
+  int32_t split_size;
+  int32_t page_size;
+  int32_t n_pages;
+  int64_t bt_stride;
+  int64_t q_sb, q_sh;
+  int64_t k_ps, k_ts, k_sh;
+  int64_t v_ps, v_ts, v_sh;
+  int64_t o_sb, o_sh;
+  int64_t lse_sb;
+  float scale;
+} attn_decode_paged_args;
+
+/*
  * Merge n_parts partial attention results computed over DISJOINT key sets
  * (STAGE_D.md page, "O rescale (kt>0)" workaround): per row, with
  * M = max_p lse_p and w_p = exp(lse_p - M),
  *     O = sum_p w_p O_p / sum_p w_p,   LSE = M + ln sum_p w_p.
- * A part with lse = -inf has zero weight and its O is not read; a row whose
- * parts are all -inf gets O = 0, LSE = -inf.  It must not be used to merge
+ * A part with lse = -inf has zero weight: its O is loaded (so o_parts must be
+ * allocated for every part) but never used, and may hold any bits, NaN
+ * included; a row whose parts are all -inf gets O = 0, LSE = -inf.  It must not be used to merge
  * partial dot products over the same keys (head-dim sub-tiles add in logit
  * space; STAGE_D.md page, section 2).
  *
@@ -184,6 +229,8 @@ size_t attn_fwd_decode_workspace_size(int32_t B, int32_t h_q, int32_t d, int32_t
 attn_status attn_fwd_prefill(const attn_prefill_args *args, void *stream);
 attn_status attn_fwd_decode(const attn_decode_args *args, void *workspace, size_t workspace_bytes,
                             void *stream);
+attn_status attn_fwd_decode_paged(const attn_decode_paged_args *args, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 attn_status attn_combine(const attn_combine_args *args, void *stream);
 
 /* Static, human-readable name of a status code. */

@@ -12,7 +12,7 @@ import re
 import pytest
 
 import attention_forward_attn_amd as afa
-from attention_forward_attn_amd._binding import CombineArgs, DecodeArgs, PrefillArgs
+from attention_forward_attn_amd._binding import CombineArgs, DecodeArgs, DecodePagedArgs, PrefillArgs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("attn_fwd_prefill", "attn_fwd_decode", "attn_combine",
+    for want in ("attn_fwd_prefill", "attn_fwd_decode", "attn_fwd_decode_paged", "attn_combine",
                  "attn_fwd_decode_workspace_size", "attn_status_str", "attn_last_error",
                  "attn_abi_version"):
         assert want in names
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     lib = afa.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
 
 
 def test_status_strings():
@@ -153,6 +153,62 @@ def test_decode_rejects(name, over, code):
     a = good_decode(**over)
     st = lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None)
     assert st == code, (st, lib.attn_last_error())
+
+
+def good_paged(**over):
+    a = DecodePagedArgs()
+    a.q = a.k = a.v = a.o = FAKE
+    a.block_table = a.kv_len = FAKE
+    a.lse = None
+    a.sinks = None
+    a.B, a.h_q, a.h_kv, a.d = 4, 128, 1, 128
+    a.max_kv_len, a.split_size = 8192, 512
+    a.page_size, a.n_pages = 64, 1000
+    a.bt_stride = 128
+    a.q_sb, a.q_sh = 128 * 128, 128
+    a.k_ps, a.k_ts, a.k_sh = 64 * 128, 128, 0
+    a.v_ps, a.v_ts, a.v_sh = 64 * 128, 128, 0
+    a.o_sb, a.o_sh = 128 * 128, 128
+    a.lse_sb = 128
+    a.scale = 0.088
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+PAGED_BAD = [
+    ("null block table", dict(block_table=None), 1),
+    ("null kv_len", dict(kv_len=None), 1),
+    ("d=512", dict(d=512), 2),
+    ("ratio", dict(h_q=6, h_kv=4), 2),
+    ("page 8", dict(page_size=8), 2),
+    ("page 48", dict(page_size=48), 2),
+    ("page above split", dict(page_size=1024), 2),
+    ("65 pages per split", dict(split_size=1024 + 64, page_size=16), 2),
+    ("no pages", dict(n_pages=0), 2),
+    ("table too narrow", dict(bt_stride=127), 3),
+    ("odd page stride", dict(k_ps=12), 3),
+    ("huge token stride", dict(v_ts=1 << 24), 3),
+    ("misaligned v", dict(v=FAKE + 8), 4),
+    ("misaligned block table", dict(block_table=FAKE + 2), 4),
+]
+
+
+@pytest.mark.parametrize("name,over,code", PAGED_BAD, ids=[c[0] for c in PAGED_BAD])
+def test_decode_paged_rejects(name, over, code):
+    lib = afa.load_library()
+    a = good_paged(**over)
+    st = lib.attn_fwd_decode_paged(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert st == code, (st, lib.attn_last_error())
+
+
+def test_decode_paged_workspace_checks():
+    lib = afa.load_library()
+    a = good_paged()
+    need = lib.attn_fwd_decode_workspace_size(4, 128, 128, 8192, 512)
+    assert lib.attn_fwd_decode_paged(ctypes.byref(a), None, need, None) == 6
+    assert lib.attn_fwd_decode_paged(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
+    assert lib.attn_fwd_decode_paged(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4
 
 
 def test_decode_workspace_checks():

@@ -8,7 +8,7 @@ import torch
 
 import attention_forward_attn_amd as afa
 import oracle
-from attention_forward_attn_amd.inputs import WORKLOADS, decode_inputs
+from attention_forward_attn_amd.inputs import WORKLOADS, decode_inputs, paged_decode_inputs
 from parity_util import check
 
 pytestmark = pytest.mark.gpu
@@ -119,7 +119,8 @@ def test_combine_matches_merge(n, rows, d):
     gen = torch.Generator().manual_seed(n * 100 + rows)
     o_parts = torch.randn(n, rows, d, generator=gen)
     lse_parts = torch.randn(n, rows, generator=gen) * 3
-    lse_parts[0, 0] = float("-inf")          # one empty part
+    lse_parts[0, 0] = float("-inf")          # one empty part: its vector is loaded, never used
+    o_parts[0, 0] = float("nan")
     if rows > 2:
         lse_parts[:, 1] = float("-inf")      # one empty row
         o_parts[:, 1] = float("nan")         # never read
@@ -127,3 +128,83 @@ def test_combine_matches_merge(n, rows, d):
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.merge_ref(np.nan_to_num(o_parts.double().numpy()), lse_parts.double().numpy())
     check(out, lse, o_ref, l_ref, "combine")
+
+
+# --- paged KV cache -------------------------------------------------------
+
+def run_paged(inp, max_len, split=512, sinks=None, table=None):
+    q = inp["q"].to(DEV)
+    kc, vc = inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    bt = (inp["block_table"] if table is None else table).to(DEV)
+    kl = inp["kv_len"].to(DEV)
+    d = q.shape[-1]
+    ws = torch.full((afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split),),
+                    255, dtype=torch.uint8, device=DEV)  # NaN-poisoned partials
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+    sd = None if sinks is None else sinks.to(DEV)
+    afa.decode_paged(q, kc, vc, bt, kl, max_len, sinks=sd, split_size=split, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+PAGED = [
+    # B, h_q, h_kv, d, len_lo, len_hi, page_size, split
+    (4, 128, 1, 128, 1, 1500, 16, 512),
+    (3, 128, 1, 256, 1, 1100, 64, 512),
+    (5, 16, 4, 64, 1, 700, 32, 128),
+    (4, 8, 8, 128, 0, 300, 256, 256),      # empty sequences possible
+    (3, 256, 2, 128, 100, 1030, 128, 1024),
+    (2, 32, 1, 128, 200, 2100, 16, 1024),  # 64 pages per split
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=[str(c) for c in PAGED])
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_decode_paged_small(case, with_sink):
+    B, h_q, h_kv, d, lo, hi, page, split = case
+    print(f"paged decode case {case} sink={with_sink}", flush=True)
+    inp = paged_decode_inputs(B, h_q, h_kv, d, lo, hi, page, 31, with_sink, spare=3, poison=True)
+    out, lse = run_paged(inp, hi, split, inp["sinks"])
+    o_ref, l_ref = oracle.decode_paged_ref(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
+                                           inp["kv_len"], page, 1 / math.sqrt(d), sinks=inp["sinks"])
+    check(out, lse, o_ref, l_ref, str(case))
+
+
+@pytest.mark.parametrize("d,page", [(64, 16), (128, 64), (256, 32)])
+def test_decode_paged_equals_dense_bitwise(d, page):
+    """The same keys read through a block table give bit-identical results."""
+    inp = paged_decode_inputs(6, 32, 2, d, 1, 1800, page, 32, True, spare=2, poison=True)
+    out_p, lse_p = run_paged(inp, 1800, 512, inp["sinks"])
+    out_d, lse_d = run_decode(inp, 1800, 512, inp["sinks"])
+    assert torch.equal(out_p, out_d) and torch.equal(lse_p, lse_d)
+
+
+def test_decode_paged_bad_page_reads_zero():
+    """A page index outside [0, n_pages) is not dereferenced: its tokens read as zeros."""
+    inp = paged_decode_inputs(3, 16, 1, 128, 300, 600, 64, 33, poison=True)
+    n_pages = inp["k_cache"].shape[0]
+    table = inp["block_table"].clone()
+    table[0, 1] = n_pages       # one past the pool
+    table[2, 0] = -5
+    out, lse = run_paged(inp, 600, 256, table=table)
+    # expected: the same pages pointed at an all-zero page appended to the pool
+    zero = torch.zeros((1,) + tuple(inp["k_cache"].shape[1:]), dtype=torch.bfloat16)
+    kc = torch.cat([inp["k_cache"], zero])
+    vc = torch.cat([inp["v_cache"], zero])
+    t2 = table.clone()
+    t2[0, 1] = n_pages
+    t2[2, 0] = n_pages
+    o_ref, l_ref = oracle.decode_paged_ref(inp["q"], kc, vc, t2, inp["kv_len"], 64, 1 / math.sqrt(128))
+    check(out, lse, o_ref, l_ref, "bad page")
+
+
+def test_decode_paged_full_size():
+    w = WORKLOADS["mqa_decode_paged_B64_hq128_d128_p64"]
+    print(f"full-size paged decode {w.name}", flush=True)
+    inp = paged_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.page_size, w.seed)
+    out, lse = run_paged(inp, w.len_hi, w.split)
+    o_ref, l_ref = oracle.decode_ref(inp["q"], inp["k"], inp["v"], inp["kv_start"], inp["kv_len"],
+                                     1 / math.sqrt(w.d))
+    check(out, lse, o_ref, l_ref, w.name)
+
