@@ -150,10 +150,10 @@ typedef struct {
 
 /*
  * Decode over a paged KV cache: the same operation, split kernel and combine
- * as attn_fwd_decode; only the addressing of K and V differs.  The pages name
- * paged and dense caches as separate kernel variants (optimize-fa4-blackwell
- * skill page, hard rules) and a paged cache among the serving infrastructure
- * (DSV4 status page, "KV cache infra" row) without fixing a layout; the one
+ * as attn_fwd_decode; only the addressing of K and V differs.  The pages ask
+ * for paged and dense caches to get kernels of their own (optimize-fa4-blackwell
+ * skill page, hard rules) and list a paged cache in the serving infrastructure
+ * (DSV4 status page, KV cache infrastructure row) without fixing a layout; the one
  * taken here is a pool of pages of page_size tokens, with row bi of a block
  * table listing the pages of sequence bi in token order.  Token tok of
  * sequence bi, kv head g is at

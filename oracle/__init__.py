@@ -8,7 +8,9 @@ from .attention import (  # noqa: F401
     NEG_INF,
     attention_flops,
     attention_ref,
+    fp8_e4m3_value,
     gather_pages,
+    decode_fp8_ref,
     decode_paged_ref,
     decode_ref,
     decode_split_ref,

@@ -31,6 +31,9 @@ What it computes, and where the pages define it:
   per-sequence KV cache, unsplit and split into fixed-size key chunks.
 * ``decode_paged_ref`` -- the same decode over a paged KV cache addressed
   through a block table (reading of the layout stated in its docstring).
+* ``decode_fp8_ref`` -- the same decode over an FP8 (E4M3) KV cache with a
+  per-kv-head scale for K and for V (``fp8_e4m3_value`` decodes the codes from
+  the format's definition).
 
 Readings taken where the pages are silent or garbled (each is stated again
 where it is used):
@@ -332,10 +335,10 @@ def decode_paged_ref(q, k_cache, v_cache, block_table, kv_len, page_size: int, s
                      sinks=None):
     """Single-token decode over a paged KV cache (block table), fp64.
 
-    The pages name a paged KV cache as a separate kernel variant ("paged vs
-    dense", hard rules of the optimize-fa4-blackwell skill page) and as part
-    of the cache infrastructure (DSV4 status page, "KV cache infra" row) but
-    fix no layout.  Reading used: the cache is a pool of fixed-size pages
+    The pages ask for paged and dense caches to get kernels of their own
+    (hard rules of the optimize-fa4-blackwell skill page) and list a paged
+    cache in the serving infrastructure (DSV4 status page, the KV cache
+    infrastructure row), but fix no layout.  Reading used: the cache is a pool of fixed-size pages
     [n_pages, page_size, h_kv, d]; row b of block_table lists the pages of
     sequence b in token order, so token t of the sequence is slot
     t % page_size of page block_table[b][t // page_size].  The attention is
@@ -356,6 +359,38 @@ def decode_paged_ref(q, k_cache, v_cache, block_table, kv_len, page_size: int, s
         out[bi] = o[0, :, 0]
         lse[bi] = l[0, :, 0]
     return out, lse
+
+
+def fp8_e4m3_value(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 ("e4m3fn") codes, float64.
+
+    The format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; an
+    all-zero exponent is subnormal (m/8 * 2^-6); exponent 15 with mantissa 7
+    is NaN; there are no infinities, so the largest finite value is 448.
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def decode_fp8_ref(q, k_codes, v_codes, k_scale, v_scale, kv_start, kv_len, scale: float, sinks=None):
+    """Decode over an FP8 KV cache: keys and values are E4M3 codes times a per-kv-head scale.
+
+    The pages plan a KV cache in fewer bits that is widened again in on-chip
+    memory for a deeper load pipeline (DSV4 status page, priority 7); they fix
+    neither the format nor the scaling.  Reading used: 8-bit E4M3 codes [T, h_kv, d] with one fp32
+    scale per kv head for K and one for V, K = code value * k_scale[g],
+    V = code value * v_scale[g]; the attention is then exactly decode_ref on
+    those values.  Returns O [B,h_q,d], LSE [B,h_q].
+    """
+    ks = _as_f64(k_scale).reshape(-1)
+    vs = _as_f64(v_scale).reshape(-1)
+    k = fp8_e4m3_value(np.asarray(k_codes)) * ks[None, :, None]
+    v = fp8_e4m3_value(np.asarray(v_codes)) * vs[None, :, None]
+    return decode_ref(q, k, v, kv_start, kv_len, scale, sinks=sinks)
 
 
 def attention_flops(b: int, h_q: int, s_q: int, s_k: int, d: int, causal: bool,

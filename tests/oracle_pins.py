@@ -13,6 +13,8 @@ disagrees with:
   permutation, empty rows, the flop count,
 * a textbook routine: torch's CPU fp64 ``scaled_dot_product_attention``,
 * the paged-cache decode against the brute force on the keys it scattered,
+* the FP8 E4M3 decoder against torch's float8_e4m3fn type on all 256 codes,
+  and the FP8 decode against the brute force on torch-dequantized values,
 * the streaming recurrence and the split/merge reformulation, and the
   negative result that merging head-dim halves is NOT attention.
 
@@ -409,6 +411,45 @@ def pin_paged_decode_matches_brute(orc):
                 _close(l[bi], bl[0, :, 0], 1e-12, f"paged decode LSE (page size {P})")
 
 
+def pin_fp8_codes_match_library(orc):
+    """All 256 E4M3 codes decode to torch's float8_e4m3fn values (NaN where torch gives NaN)."""
+    import torch
+
+    codes = np.arange(256)
+    want = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.fp8_e4m3_value(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want)), "NaN codes differ"
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok]), "E4M3 values differ"
+
+
+def pin_fp8_decode_matches_brute(orc):
+    """FP8 decode equals the brute force on values dequantized through torch's float8 type."""
+    import torch
+
+    rng = _rng(26)
+    B, h_q, h_kv, d = 3, 4, 2, 4
+    lens = np.array([5, 1, 9])
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    T = int(lens.sum())
+    q = rng.standard_normal((B, h_q, d))
+    kc = torch.from_numpy(np.clip(rng.standard_normal((T, h_kv, d)) * 3, -448, 448)).to(torch.float8_e4m3fn)
+    vc = torch.from_numpy(np.clip(rng.standard_normal((T, h_kv, d)) * 3, -448, 448)).to(torch.float8_e4m3fn)
+    ks, vs = np.array([0.75, 1.5]), np.array([2.0, 0.25])
+    kd = kc.to(torch.float64).numpy() * ks[None, :, None]
+    vd = vc.to(torch.float64).numpy() * vs[None, :, None]
+    sig = np.array([0.5, -1.0, 2.0, 0.0])
+    for sinks in (None, sig):
+        o, l = orc.decode_fp8_ref(q, kc.view(torch.uint8).numpy(), vc.view(torch.uint8).numpy(), ks, vs,
+                                  starts, lens, 0.45, sinks=sinks)
+        for bi in range(B):
+            kb = np.transpose(kd[starts[bi]:starts[bi] + lens[bi]], (1, 0, 2))[None]
+            vb = np.transpose(vd[starts[bi]:starts[bi] + lens[bi]], (1, 0, 2))[None]
+            bo, bl = brute_force(q[bi][None, :, None, :], kb, vb, 0.45, False, 0, sinks)
+            _close(o[bi], bo[0, :, 0], 1e-12, "fp8 decode O")
+            _close(l[bi], bl[0, :, 0], 1e-12, "fp8 decode LSE")
+
+
 def pin_split_merge_equals_unsplit(orc):
     """Split-KV partials merged by LSE equal the unsplit decode (disjoint key sets)."""
     q, k, v, starts, lens = _decode_case(23)
@@ -477,6 +518,8 @@ PINS = [
     pin_online_equals_plain,
     pin_decode_matches_brute,
     pin_paged_decode_matches_brute,
+    pin_fp8_codes_match_library,
+    pin_fp8_decode_matches_brute,
     pin_split_merge_equals_unsplit,
     pin_head_dim_halves_do_not_merge,
     pin_flop_count,

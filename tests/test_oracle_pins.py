@@ -54,6 +54,12 @@ MUTATIONS = [
      "out[t0:t0 + n] = cache[int(table[t0 // page_size]), 1:n + 1]"),
     ("paged: page index by slot", "out[t0:t0 + n] = cache[int(table[t0 // page_size]), :n]",
      "out[t0:t0 + n] = cache[int(table[t0 % page_size]), :n]"),
+    ("fp8: exponent bias 8", "(1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)",
+     "(1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 8.0)"),
+    ("fp8: subnormals as normals", "np.where(e == 0, m / 8.0 * 2.0 ** -6,", "np.where(e < 0, m / 8.0 * 2.0 ** -6,"),
+    ("fp8: sign dropped", "sign = np.where((c >> 7) & 1, -1.0, 1.0)", "sign = np.where((c >> 7) & 1, 1.0, 1.0)"),
+    ("fp8: scales swapped", "k = fp8_e4m3_value(np.asarray(k_codes)) * ks[None, :, None]",
+     "k = fp8_e4m3_value(np.asarray(k_codes)) * vs[None, :, None]"),
     ("flops count 2d per pair", "return 4 * d * pairs * b * h_q", "return 2 * d * pairs * b * h_q"),
 ]
 
