@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     combine,
     decode,
+    decode_fp8,
     decode_paged,
     decode_workspace_size,
     load_library,

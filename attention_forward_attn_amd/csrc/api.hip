@@ -50,12 +50,13 @@ attn_status hip_fail(hipError_t e, const char *what) {
 }
 
 // Shared tail of the dense and paged decode entry points (arguments already
-// validated; p carries the K/V addressing): grid check, workspace layout, the
-// split kernel and the combine kernel.
+// validated; p carries the K/V addressing; kind 0 = contiguous bf16 cache,
+// 1 = paged, 2 = FP8): grid check, workspace layout, the split kernel and the
+// combine kernel.
 attn_status run_decode(attn::DecodeParams &p, const int32_t *kv_len, const float *sinks, void *o, float *lse,
                        int32_t B, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_kv_len, int32_t split_size,
                        int64_t q_sb, int64_t q_sh, int64_t o_sb, int64_t o_sh, int64_t lse_sb, float scale,
-                       bool paged, void *workspace, void *stream) {
+                       int kind, void *workspace, void *stream) {
   const int bm = attn::decode_block_rows(d);
   const int ratio = h_q / h_kv;
   const int64_t n_split = max_kv_len > 0 ? (max_kv_len + split_size - 1) / split_size : 1;
@@ -80,7 +81,9 @@ attn_status run_decode(attn::DecodeParams &p, const int32_t *kv_len, const float
   p.c = scale * attn::kLog2e;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = paged ? attn::decode_split_paged(d, p, s) : attn::decode_split(d, p, s);
+  hipError_t e = kind == 1   ? attn::decode_split_paged(d, p, s)
+                 : kind == 2 ? attn::decode_split_fp8(d, p, s)
+                             : attn::decode_split(d, p, s);
   if (e != hipSuccess) return hip_fail(e, "decode split launch");
 
   attn::CombineParams c;
@@ -254,7 +257,56 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
   p.k_st = a->k_st; p.k_sh = a->k_sh;
   p.v_st = a->v_st; p.v_sh = a->v_sh;
   return run_decode(p, a->kv_len, a->sinks, a->o, a->lse, a->B, a->h_q, a->h_kv, a->d, a->max_kv_len,
-                    a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, false, workspace,
+                    a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, 0, workspace,
+                    stream);
+}
+
+attn_status attn_fwd_decode_fp8(const attn_decode_fp8_args *a, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
+  if (a->B < 1 || a->h_q < 1 || a->h_kv < 1)
+    return fail(ATTN_ERR_SHAPE, "need B, h_q, h_kv >= 1");
+  if (a->h_q % a->h_kv != 0)
+    return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
+  if (a->d != 128) return fail(ATTN_ERR_SHAPE, "FP8 decode supports d = 128 (got %d)", a->d);
+  if (a->max_kv_len < 0) return fail(ATTN_ERR_SHAPE, "max_kv_len must be >= 0");
+  if (a->split_size < 64 || a->split_size % 64 != 0)
+    return fail(ATTN_ERR_SHAPE, "split_size must be a positive multiple of 64 (got %d)", a->split_size);
+  if (!(std::isfinite(a->scale) && a->scale > 0.0f))
+    return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+  if (!a->q || !a->k || !a->v || !a->o || !a->kv_start || !a->kv_len || !a->k_scale || !a->v_scale)
+    return fail(ATTN_ERR_NULL, "q, k, v, o, kv_start, kv_len, k_scale and v_scale must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(ATTN_ERR_ALIGN, "q, k, v, o must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(a->kv_start) & 7u) || !aligned4(a->kv_len) || !aligned4(a->k_scale) ||
+      !aligned4(a->v_scale) || (a->lse && !aligned4(a->lse)) || (a->sinks && !aligned4(a->sinks)))
+    return fail(ATTN_ERR_ALIGN, "kv_start must be 8-byte and kv_len, scales, lse, sinks 4-byte aligned");
+  const int64_t st[] = {a->q_sb, a->q_sh, a->o_sb, a->o_sh};
+  for (int64_t s : st)
+    if (!bf16_stride_ok(s)) return fail(ATTN_ERR_STRIDE, "bf16 strides must be non-negative multiples of 8 elements");
+  const int64_t cst[] = {a->k_st, a->k_sh, a->v_st, a->v_sh};
+  for (int64_t s : cst)
+    if (s < 0 || s % 16 != 0) return fail(ATTN_ERR_STRIDE, "FP8 cache strides must be non-negative multiples of 16 bytes");
+  if (a->lse && a->lse_sb < 0) return fail(ATTN_ERR_STRIDE, "lse_sb must be >= 0");
+  if (a->k_st >= kMaxRowStride || a->v_st >= kMaxRowStride)
+    return fail(ATTN_ERR_STRIDE, "k/v token strides must be below 2^24 bytes");
+  const size_t need = attn_fwd_decode_workspace_size(a->B, a->h_q, a->d, a->max_kv_len, a->split_size);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+  attn::DecodeParams p{};
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k = reinterpret_cast<const uint16_t *>(a->k);  // byte addressing inside the kernel
+  p.v = reinterpret_cast<const uint16_t *>(a->v);
+  p.kv_start = a->kv_start;
+  p.k_st = a->k_st; p.k_sh = a->k_sh;
+  p.v_st = a->v_st; p.v_sh = a->v_sh;
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  return run_decode(p, a->kv_len, a->sinks, a->o, a->lse, a->B, a->h_q, a->h_kv, a->d, a->max_kv_len,
+                    a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, 2, workspace,
                     stream);
 }
 
@@ -311,7 +363,7 @@ attn_status attn_fwd_decode_paged(const attn_decode_paged_args *a, void *workspa
   p.page_shift = __builtin_ctz((unsigned)ps);
   p.n_pages = a->n_pages;
   return run_decode(p, a->kv_len, a->sinks, a->o, a->lse, a->B, a->h_q, a->h_kv, a->d, a->max_kv_len,
-                    a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, true, workspace,
+                    a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, 1, workspace,
                     stream);
 }
 

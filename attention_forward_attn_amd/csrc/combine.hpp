@@ -36,28 +36,16 @@ struct Vec8<uint16_t> {
   }
 };
 
+// Merge of one 8-column chunk of one row over n parts (LSE at lp[i*ls], vector
+// at op[i*os]); writes 8 bf16 to out and, if lse_out is not NULL, the LSE.
 // Parts are taken PB at a time.  The partial vectors of a batch are loaded
 // together with their LSEs (not after them: a part's LSE only decides whether
 // its vector is used), so a batch costs one memory round trip; the running
 // (max, weight sum, accumulator) is rescaled once per batch to the batch's
-// new maximum.  bf16 parts come 16 to a batch (every split of a 8192-key
-// sequence at 512 keys per split in one trip), fp32 parts 8.
-template <typename PT>
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  constexpr int PB = sizeof(PT) == 2 ? 16 : 8;
-  const int cpr = p.d / 8;  // 8-column chunks per row
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (int64_t)p.rows * cpr) return;
-  const int row = (int)(gid / cpr), ch = (int)(gid - (int64_t)row * cpr);
-  const int r1 = row / p.n2, r2 = row - r1 * p.n2;
-  const float *lp = p.lse_parts + r1 * p.lse_r1 + r2 * p.lse_r2;
-  const PT *op = reinterpret_cast<const PT *>(p.o_parts) + r1 * p.o_r1 + r2 * p.o_r2 + ch * 8;
-  int n = p.n_parts;
-  if (p.kv_len != nullptr) {
-    const int L = p.kv_len[r1];
-    n = min(n, L > 0 ? (L - 1) / p.split + 1 : 1);
-  }
-
+// new maximum.
+template <typename PT, int PB>
+__device__ __forceinline__ void merge_chunk(const float *lp, int64_t ls, const PT *op, int64_t os, int n,
+                                            uint16_t *out, float *lse_out) {
   float mx = kNegInf, wsum = 0.0f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < n; i += PB) {
@@ -67,8 +55,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     for (int u = 0; u < PB; ++u) {
       li[u] = kNegInf;
       if (i + u < n) {
-        li[u] = lp[(i + u) * p.lse_part_stride];
-        v[u].load(op + (int64_t)(i + u) * p.o_part_stride);
+        li[u] = lp[(i + u) * ls];
+        v[u].load(op + (int64_t)(i + u) * os);
       }
     }
     float bm = li[0];
@@ -82,7 +70,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     for (int e = 0; e < 8; ++e) acc[e] *= sc;
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      if (li[u] == kNegInf) continue;  // such a part's vector may be unwritten: never read it
+      if (li[u] == kNegInf) continue;  // such a part's vector may be unwritten: never use it
       const float wgt = __expf(li[u] - nm);
       wsum += wgt;
 #pragma unroll
@@ -90,14 +78,34 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
     mx = nm;
   }
-  uint16_t *out = p.o_out + r1 * p.out_r1 + r2 * p.out_r2 + ch * 8;
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
   u32x4 res;
 #pragma unroll
   for (int q = 0; q < 4; ++q) res[q] = pack_bf16x2(acc[2 * q] * inv, acc[2 * q + 1] * inv);
   *reinterpret_cast<u32x4 *>(out) = res;
-  if (p.lse_out != nullptr && ch == 0)
-    p.lse_out[r1 * p.lse_out_r1 + r2 * p.lse_out_r2] = wsum > 0.0f ? mx + __logf(wsum) : kNegInf;
+  if (lse_out != nullptr) *lse_out = wsum > 0.0f ? mx + __logf(wsum) : kNegInf;
+}
+
+// bf16 parts come 16 to a batch (every split of an 8192-key sequence at 512
+// keys per split in one trip), fp32 parts 8.
+template <typename PT>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  constexpr int PB = sizeof(PT) == 2 ? 16 : 8;
+  const int cpr = p.d / 8;  // 8-column chunks per row
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)p.rows * cpr) return;
+  const int row = (int)(gid / cpr), ch = (int)(gid - (int64_t)row * cpr);
+  const int r1 = row / p.n2, r2 = row - r1 * p.n2;
+  int n = p.n_parts;
+  if (p.kv_len != nullptr) {
+    const int L = p.kv_len[r1];
+    n = min(n, L > 0 ? (L - 1) / p.split + 1 : 1);
+  }
+  merge_chunk<PT, PB>(p.lse_parts + r1 * p.lse_r1 + r2 * p.lse_r2, p.lse_part_stride,
+                      reinterpret_cast<const PT *>(p.o_parts) + r1 * p.o_r1 + r2 * p.o_r2 + ch * 8,
+                      p.o_part_stride, n, p.o_out + r1 * p.out_r1 + r2 * p.out_r2 + ch * 8,
+                      p.lse_out != nullptr && ch == 0 ? p.lse_out + r1 * p.lse_out_r1 + r2 * p.lse_out_r2
+                                                      : nullptr);
 }
 
 template <typename PT>

@@ -57,6 +57,8 @@ struct DecodeParams {
   int64_t bt_stride;
   int64_t k_ps, v_ps;
   int32_t page_shift, n_pages;
+  // FP8 cache only: E4M3 codes times these per-kv-head scales.
+  const float *k_scale, *v_scale;
   float c;
 };
 

@@ -23,6 +23,11 @@ hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s) {
   }
 }
 
+hipError_t decode_split_fp8(int d, const DecodeParams &p, hipStream_t s) {
+  if (d != 128) return hipErrorInvalidValue;
+  return launch_decode_split<128, 4, 1, 32, 2, 3, false, true>(p, s);
+}
+
 hipError_t combine(const CombineParams &p, hipStream_t s) { return launch_combine<float>(p, s); }
 hipError_t combine_bf16(const CombineParams &p, hipStream_t s) { return launch_combine<uint16_t>(p, s); }
 

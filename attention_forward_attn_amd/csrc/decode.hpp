@@ -34,6 +34,7 @@
 // disjoint key sets.
 #pragma once
 
+#include "fp8.hpp"
 #include "tile.hpp"
 
 namespace attn {
@@ -102,18 +103,23 @@ __device__ bool decode_unit(const DecodeParams &p, int u, int lane, int len0, in
 // HG head groups of 32 heads x KG key groups of BN/KG keys = HG*KG waves.
 // PAGED: K/V are read through the block table (one descriptor per DMA load,
 // see Tile::dma1_paged) instead of from a per-sequence contiguous range.
-template <int D, int HG, int KG, int BN, int STAGES, int OCC, bool PAGED = false>
+// FP8: K/V are E4M3 codes with a per-kv-head scale (see fp8.hpp).
+template <int D, int HG, int KG, int BN, int STAGES, int OCC, bool PAGED = false, bool FP8 = false>
 __global__ __launch_bounds__(HG * KG * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_split_kernel(DecodeParams p) {
   constexpr int NW = HG * KG;
   using TD = Tile<D, NW, BN>;       // DMA geometry: all waves load one BN-key tile
   using TC = Tile<D, NW, BN / KG>;  // MMA view: each wave computes on BN/KG keys of it
+  using F8 = Fp8Tile<FP8 ? D : 128, NW, FP8 ? BN : 32>;
   constexpr int BM = 32 * HG;       // query heads per workgroup
   constexpr int NDB = TC::NDB;
   constexpr int MERGE_BYTES = KG > 1 ? HG * (NDB * 4 + 1) * 64 * 16 : 0;
-  constexpr int RING_BYTES = STAGES * TD::STAGE_BYTES;
-  constexpr int SMEM_BYTES = RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES;
+  constexpr int RING_BYTES = STAGES * (FP8 ? F8::STAGE_BYTES : TD::STAGE_BYTES);
+  constexpr int STORE_BYTES = BM * D * 2;  // partial tile staged for the whole-row stores
+  constexpr int SMEM_BYTES = RING_BYTES > MERGE_BYTES ? (RING_BYTES > STORE_BYTES ? RING_BYTES : STORE_BYTES)
+                                                      : MERGE_BYTES;
   static_assert(STAGES >= 2 && (KG == 1 || KG == 2) && (BN / KG) % 32 == 0, "decode shape");
+  static_assert(!FP8 || (KG == 1 && !PAGED), "FP8 decode: one key group, contiguous cache");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_BYTES / 2];
 
   const int tid = threadIdx.x;
@@ -149,6 +155,9 @@ void decode_split_kernel(DecodeParams p) {
   // this split (at most 64) are read once into lane-wise registers.
   const uint16_t *kbase = p.k + (PAGED ? 0 : (start + kbeg) * p.k_st) + g * p.k_sh;
   const uint16_t *vbase = p.v + (PAGED ? 0 : (start + kbeg) * p.v_st) + g * p.v_sh;
+  // FP8: the cache is addressed in bytes (strides count bytes).
+  const uint8_t *kbase8 = reinterpret_cast<const uint8_t *>(p.k) + (start + kbeg) * p.k_st + g * p.k_sh;
+  const uint8_t *vbase8 = reinterpret_cast<const uint8_t *>(p.v) + (start + kbeg) * p.v_st + g * p.v_sh;
   const int n_keys = max(kend - kbeg, 0);
   int pg = 0;
   if constexpr (PAGED) {
@@ -159,10 +168,13 @@ void decode_split_kernel(DecodeParams p) {
   const bool wave_ok = hb * BM + hgrp * 32 < p.ratio;
 
   typename TD::Lane dl;
+  typename F8::Lane fl;
   if constexpr (PAGED) TD::init_dma_paged(dl, p.k_st, p.v_st, wave, lane);
   else TD::init_dma(dl, p.k_st, p.v_st, wave, lane);
   auto load_tile = [&](uint16_t *stage, int t) {
-    if constexpr (PAGED)
+    if constexpr (FP8)
+      F8::dma(fl, reinterpret_cast<uint8_t *>(stage), kbase8, p.k_st, vbase8, p.v_st, t * BN, n_keys, wave);
+    else if constexpr (PAGED)
       TD::dma_paged(dl, stage, kbase, p.k_st, p.k_ps, vbase, p.v_st, p.v_ps, pg, p.page_shift, p.n_pages, t * BN,
                     n_keys, wave);
     else
@@ -170,11 +182,17 @@ void decode_split_kernel(DecodeParams p) {
   };
   typename TC::Lane ml;
   const uint32_t base = lds_offset(smem);
-  TC::init_mma(ml, base + kgrp * (BN / KG) * D * 2, base + TD::TILE_BYTES + kgrp * (BN / KG) * D * 2, lane);
+  if constexpr (FP8) {
+    F8::init(fl, p.k_st, p.v_st, wave, lane, base, base + F8::TILE_BYTES);
+  } else {
+    TC::init_mma(ml, base + kgrp * (BN / KG) * D * 2, base + TD::TILE_BYTES + kgrp * (BN / KG) * D * 2, lane);
+  }
 
+  constexpr int STG = FP8 ? F8::STAGE_BYTES : TD::STAGE_BYTES;  // bytes per ring stage
+  constexpr int NLD = FP8 ? F8::LOADS : TD::LOADS;              // loads per wave per K or V tile
   // Prologue: tiles 0 .. STAGES-2 in flight.
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) load_tile(smem + s * (TD::STAGE_BYTES / 2), s);
+  for (int s = 0; s < STAGES - 1; ++s) load_tile(smem + s * (STG / 2), s);
 
   u32x4 qreg[TC::NKK];
   {
@@ -191,17 +209,20 @@ void decode_split_kernel(DecodeParams p) {
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  // FP8: the K scale multiplies every logit, so it joins the exp2 factor.
+  const float c = FP8 ? p.c * p.k_scale[g] : p.c;
 
   for (int t = 0; t < n_tiles; ++t) {
-    wait_vmcnt<(STAGES - 2) * 2 * TD::LOADS>();  // this wave's loads of tile t have landed
-    barrier_nofence();                            // everyone's have; tile t-1's stage is free
+    wait_vmcnt<(STAGES - 2) * 2 * NLD>();  // this wave's loads of tile t have landed
+    barrier_nofence();                      // everyone's have; tile t-1's stage is free
     const int nxt = t + STAGES - 1;
-    load_tile(smem + (nxt % STAGES) * (TD::STAGE_BYTES / 2), nxt);
-    const uint32_t stage_off = (t % STAGES) * TD::STAGE_BYTES;
+    load_tile(smem + (nxt % STAGES) * (STG / 2), nxt);
+    const uint32_t stage_off = (t % STAGES) * STG;
     const int j0 = t * BN + kgrp * (BN / KG);  // first key of this wave's part of the tile
     if (wave_ok && j0 < n_keys) {
       f32x16 s[TC::NKB];
-      TC::scores(s, qreg, ml, stage_off);
+      if constexpr (FP8) F8::scores(s, qreg, fl, stage_off);
+      else TC::scores(s, qreg, ml, stage_off);
       if (j0 + BN / KG > n_keys) {
 #pragma unroll
         for (int kb = 0; kb < TC::NKB; ++kb)
@@ -210,8 +231,9 @@ void decode_split_kernel(DecodeParams p) {
             if (j0 + TC::key_of(kb, i, hi) >= n_keys) s[kb][i] = kNegInf;
       }
       u32x4 pk[TC::NPV];
-      TC::softmax_step(s, pk, o, m, l, p.c);
-      TC::values(o, pk, ml, stage_off);
+      TC::softmax_step(s, pk, o, m, l, c);
+      if constexpr (FP8) F8::values(o, pk, fl, stage_off);
+      else TC::values(o, pk, ml, stage_off);
     }
   }
 
@@ -252,7 +274,8 @@ void decode_split_kernel(DecodeParams p) {
   }
 
   const float lt = sum_across_halves(l);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  // FP8: the V scale multiplies every output column.
+  const float inv = lt > 0.0f ? (FP8 ? p.v_scale[g] : 1.0f) / lt : 0.0f;
   if (row_ok && hi == 0) p.lse_part[part] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   // Normalised partial output, bf16 (its rounding is far below the final bf16
   // rounding of O after the merge).  A lane holds pieces of one head's row,
@@ -263,7 +286,7 @@ void decode_split_kernel(DecodeParams p) {
     constexpr int NC = D / 8;              // 16-byte chunks per row
     constexpr int SW = NC < 16 ? NC : 16;  // swizzle span
     constexpr int RPI = 64 / NC;           // rows per store instruction
-    static_assert(BM * D * 2 <= RING_BYTES, "partial tile must fit in the ring");
+    static_assert(STORE_BYTES <= SMEM_BYTES, "partial tile must fit in LDS");
     __syncthreads();  // every wave is done with the last stage
     char *xw = reinterpret_cast<char *>(smem) + hgrp * 32 * D * 2;
 #pragma unroll
@@ -302,11 +325,11 @@ void decode_split_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int HG, int KG, int BN, int STAGES, int OCC, bool PAGED = false>
+template <int D, int HG, int KG, int BN, int STAGES, int OCC, bool PAGED = false, bool FP8 = false>
 hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream) {
   dim3 grid((unsigned)decode_grid_size(p.n_split, p.B, p.h_kv, p.n_hblk));
-  hipLaunchKernelGGL((decode_split_kernel<D, HG, KG, BN, STAGES, OCC, PAGED>), grid, dim3(HG * KG * 64), 0, stream,
-                     p);
+  hipLaunchKernelGGL((decode_split_kernel<D, HG, KG, BN, STAGES, OCC, PAGED, FP8>), grid, dim3(HG * KG * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

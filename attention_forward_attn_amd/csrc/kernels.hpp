@@ -21,6 +21,8 @@ int decode_block_rows(int d);
 hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s);
 // The same over a paged cache (p.block_table, p.page_shift, p.k_ps, p.v_ps set).
 hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s);
+// The same over an FP8 (E4M3) cache with per-kv-head scales (p.k_scale, p.v_scale); d = 128.
+hipError_t decode_split_fp8(int d, const DecodeParams &p, hipStream_t s);
 
 // LSE merge of fp32 partials (public entry point) / of bf16 partials (decode).
 hipError_t combine(const CombineParams &p, hipStream_t s);

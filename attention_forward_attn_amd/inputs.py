@@ -12,7 +12,9 @@ token-major, [sum_b L_b, h_kv, d], contiguous per sequence, with ``kv_start``
 the exclusive prefix sum of the lengths.  A paged cache holds the same draw
 in pages of ``page_size`` tokens, [n_pages, page_size, h_kv, d]; the pages of
 all sequences (plus ``spare`` unused ones) are placed in a random order drawn
-from a second generator (seed + 7919), so the values match the packed draw.
+from a second generator (seed + 7919), so the values match the packed draw.  An FP8
+cache holds the same draw as OCP E4M3 codes: per kv head, scale = max |x| / 448
+and code = E4M3(x / scale) (torch's round-to-nearest-even cast).
 """
 
 from __future__ import annotations
@@ -45,6 +47,7 @@ class Workload:
     len_hi: int = 0
     split: int = 512
     page_size: int = 0  # paged KV cache (0 = contiguous per sequence)
+    fp8: bool = False   # KV cache as E4M3 codes with per-kv-head scales
     notes: dict = field(default_factory=dict, compare=False)
 
 
@@ -78,6 +81,9 @@ WORKLOADS = {
            len_lo=1024, len_hi=8192),
         _w("mqa_decode_B64_hq128_d256", "decode", BASE_SEED + 3, 256, 128, 1, b=64,
            len_lo=1024, len_hi=8192),
+        # the same draw quantized to an FP8 (E4M3) cache
+        _w("mqa_decode_fp8_B64_hq128_d128", "decode", BASE_SEED + 3, 128, 128, 1, b=64,
+           len_lo=1024, len_hi=8192, fp8=True),
         # the same draw held in a paged cache of 64-token pages
         _w("mqa_decode_paged_B64_hq128_d128_p64", "decode", BASE_SEED + 3, 128, 128, 1, b=64,
            len_lo=1024, len_hi=8192, page_size=64),
@@ -130,6 +136,8 @@ def workload_inputs(w: Workload):
     """Inputs of a named workload (see WORKLOADS)."""
     if w.kind == "prefill":
         return prefill_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed, w.sinks)
+    if w.fp8:
+        return fp8_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed, w.sinks)
     if w.page_size:
         return paged_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.page_size, w.seed, w.sinks)
     return decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed, w.sinks)
@@ -165,5 +173,23 @@ def paged_decode_inputs(B: int, h_q: int, h_kv: int, d: int, len_lo: int, len_hi
             kc[phys, :n] = inp["k"][s0 + pg * page_size:s0 + pg * page_size + n]
             vc[phys, :n] = inp["v"][s0 + pg * page_size:s0 + pg * page_size + n]
     inp.update(k_cache=kc, v_cache=vc, block_table=table, page_size=page_size)
+    return inp
+
+
+def fp8_decode_inputs(B: int, h_q: int, h_kv: int, d: int, len_lo: int, len_hi: int, seed: int,
+                      with_sinks: bool = False):
+    """The draw of decode_inputs with K and V stored as E4M3 codes and per-kv-head scales.
+
+    Returns decode_inputs' dict plus k8, v8 (uint8 [T, h_kv, d]) and k_scale,
+    v_scale (fp32 [h_kv]).
+    """
+    inp = decode_inputs(B, h_q, h_kv, d, len_lo, len_hi, seed, with_sinks)
+    for name in ("k", "v"):
+        x = inp[name].to(torch.float32)
+        amax = x.abs().amax(dim=(0, 2)).clamp_min(1e-30)
+        sc = (amax / 448.0).to(torch.float32)
+        codes = (x / sc[None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        inp[name + "8"] = codes.contiguous()
+        inp[name + "_scale"] = sc
     return inp
 

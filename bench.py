@@ -56,7 +56,7 @@ def prefill_flops(w) -> int:
 
 
 def decode_bytes(w, total_tokens: int) -> int:
-    kv = total_tokens * w.h_kv * w.d * 2 * 2
+    kv = total_tokens * w.h_kv * w.d * 2 * (1 if w.fp8 else 2)  # K and V, 1 byte per FP8 code
     qo = 2 * w.b * w.h_q * w.d * 2
     return kv + qo + w.b * w.h_q * 4
 
@@ -280,6 +280,50 @@ class PagedDecodeCase(DecodeCase):
                          out=self.out, lse=self.lse)
 
 
+class Fp8DecodeCase(DecodeCase):
+    """The decode workload with K and V as E4M3 codes and per-kv-head scales."""
+
+    def __init__(self, w, n_sets: int, dev):
+        import torch
+
+        import attention_forward_attn_amd as afa
+        from attention_forward_attn_amd.inputs import fp8_decode_inputs
+
+        self.w = w
+        base = fp8_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed, w.sinks)
+        self.total = int(base["kv_len"].sum())
+        self.max_len = int(base["kv_len"].max())
+        self.kv_start = base["kv_start"].to(dev)
+        self.kv_len = base["kv_len"].to(dev)
+        self.k_scale = base["k_scale"].to(dev)
+        self.v_scale = base["v_scale"].to(dev)
+        self.sets = [{"q": base["q"].to(dev), "k": base["k8"].to(dev), "v": base["v8"].to(dev)}]
+        gen = torch.Generator(device=dev).manual_seed(w.seed + 1)
+        for _ in range(1, n_sets):  # further sets: fresh codes of the same shapes (no NaN codes)
+            st = {"q": torch.randn(self.sets[0]["q"].shape, generator=gen, device=dev).to(torch.bfloat16)}
+            for n in ("k", "v"):
+                st[n] = torch.randint(0, 0x7f, self.sets[0][n].shape, generator=gen, device=dev,
+                                      dtype=torch.int32).to(torch.uint8) | (
+                    torch.randint(0, 2, self.sets[0][n].shape, generator=gen, device=dev,
+                                  dtype=torch.int32).to(torch.uint8) << 7)
+            self.sets.append(st)
+        self.sinks = base["sinks"].to(dev) if base["sinks"] is not None else None
+        self.scale = 1.0 / math.sqrt(w.d)
+        self.ws = torch.empty(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
+                              dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.b, w.h_q, w.d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.b, w.h_q), dtype=torch.float32, device=dev)
+        self.bytes = decode_bytes(w, self.total)
+
+    def run(self, i: int):
+        import attention_forward_attn_amd as afa
+
+        s = self.sets[i % len(self.sets)]
+        afa.decode_fp8(s["q"], s["k"], s["v"], self.k_scale, self.v_scale, self.kv_start, self.kv_len,
+                       self.max_len, scale=self.scale, sinks=self.sinks, split_size=self.w.split,
+                       workspace=self.ws, out=self.out, lse=self.lse)
+
+
 def bench_one(name: str, steps: int, warmup: int, dev):
     """One JSON line for one named workload (prefill or decode) alone."""
     from attention_forward_attn_amd.inputs import WORKLOADS
@@ -291,7 +335,8 @@ def bench_one(name: str, steps: int, warmup: int, dev):
         r = roofline_prefill(c.flops, ms)
         return {"workload": name, "kind": "prefill", "ms": round(ms, 4), "TFLOP/s": r["achieved"],
                 "frac_of_peak": r["frac"], "gflop": round(c.flops / 1e9, 2)}
-    c = (PagedDecodeCase if w.page_size else DecodeCase)(w, 4 if w.d <= 128 else 2, dev)
+    kind = Fp8DecodeCase if w.fp8 else PagedDecodeCase if w.page_size else DecodeCase
+    c = kind(w, 4 if w.d <= 128 else 2, dev)
     (ms,), wall = timed([c], steps, warmup)
     r = roofline_decode(c.bytes, ms)
     return {"workload": name, "kind": "decode", "ms": round(ms, 4), "GB/s": r["achieved"],

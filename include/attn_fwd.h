@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 2
+#define ATTN_FWD_ABI_VERSION 3
 
 typedef enum {
   ATTN_OK = 0,
@@ -193,6 +193,45 @@ typedef struct {
 } attn_decode_paged_args;
 
 /*
+ * Decode over an FP8 KV cache: the same operation, split kernel and combine as
+ * attn_fwd_decode, with K and V held as 8-bit codes.  The pages plan a KV
+ * cache in fewer bits that is widened again on chip (DSV4 status page,
+ * priority 7) without fixing a format; the one taken here is OCP FP8 E4M3
+ * ("e4m3fn": bias 7, no infinities, 0x7f/0xff NaN) with one fp32 scale per kv
+ * head for K and one for V: key element = value(code) * k_scale[g], value
+ * element = value(code) * v_scale[g].  The kernel widens codes to bf16
+ * exactly after the LDS read and applies the scales outside the MMAs.
+ *
+ * k, v: uint8 codes; token tok of sequence bi, kv head g at
+ *       k + (kv_start[bi] + tok)*k_st + g*k_sh bytes (v: v_st, v_sh); token
+ *       and head strides multiples of 16 bytes (head stride 0 = MQA).
+ * k_scale, v_scale: DEVICE fp32 [h_kv].
+ * Supported: d = 128.  Other fields, the workspace (attn_fwd_decode_workspace_size)
+ * and its ownership are those of attn_fwd_decode.
+ */
+typedef struct {
+  const void *q;
+  const uint8_t *k;
+  const uint8_t *v;
+  const float *k_scale;
+  const float *v_scale;
+  const int64_t *kv_start;
+  const int32_t *kv_len;
+  void *o;
+  float *lse;
+  const float *sinks;
+  int32_t B, h_q, h_kv, d;
+  int32_t max_kv_len;
+  int32_t split_size;
+  int64_t q_sb, q_sh;
+  int64_t k_st, k_sh;
+  int64_t v_st, v_sh;
+  int64_t o_sb, o_sh;
+  int64_t lse_sb;
+  float scale;
+} attn_decode_fp8_args;
+
+/*
  * Merge n_parts partial attention results computed over DISJOINT key sets
  * (STAGE_D.md page, "O rescale (kt>0)" workaround): per row, with
  * M = max_p lse_p and w_p = exp(lse_p - M),
@@ -231,6 +270,8 @@ attn_status attn_fwd_decode(const attn_decode_args *args, void *workspace, size_
                             void *stream);
 attn_status attn_fwd_decode_paged(const attn_decode_paged_args *args, void *workspace,
                                   size_t workspace_bytes, void *stream);
+attn_status attn_fwd_decode_fp8(const attn_decode_fp8_args *args, void *workspace, size_t workspace_bytes,
+                                void *stream);
 attn_status attn_combine(const attn_combine_args *args, void *stream);
 
 /* Static, human-readable name of a status code. */

@@ -12,7 +12,8 @@ import re
 import pytest
 
 import attention_forward_attn_amd as afa
-from attention_forward_attn_amd._binding import CombineArgs, DecodeArgs, DecodePagedArgs, PrefillArgs
+from attention_forward_attn_amd._binding import (CombineArgs, DecodeArgs, DecodeFp8Args, DecodePagedArgs,
+                                                 PrefillArgs)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
@@ -29,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("attn_fwd_prefill", "attn_fwd_decode", "attn_fwd_decode_paged", "attn_combine",
+    for want in ("attn_fwd_prefill", "attn_fwd_decode", "attn_fwd_decode_paged", "attn_fwd_decode_fp8",
+                 "attn_combine",
                  "attn_fwd_decode_workspace_size", "attn_status_str", "attn_last_error",
                  "attn_abi_version"):
         assert want in names
@@ -39,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     lib = afa.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
 
 
 def test_status_strings():
@@ -209,6 +211,57 @@ def test_decode_paged_workspace_checks():
     assert lib.attn_fwd_decode_paged(ctypes.byref(a), None, need, None) == 6
     assert lib.attn_fwd_decode_paged(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
     assert lib.attn_fwd_decode_paged(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4
+
+
+def good_fp8(**over):
+    a = DecodeFp8Args()
+    a.q = a.k = a.v = a.o = FAKE
+    a.k_scale = a.v_scale = FAKE
+    a.kv_start = a.kv_len = FAKE
+    a.lse = None
+    a.sinks = None
+    a.B, a.h_q, a.h_kv, a.d = 4, 128, 1, 128
+    a.max_kv_len, a.split_size = 8192, 512
+    a.q_sb, a.q_sh = 128 * 128, 128
+    a.k_st, a.k_sh, a.v_st, a.v_sh = 128, 0, 128, 0
+    a.o_sb, a.o_sh = 128 * 128, 128
+    a.lse_sb = 128
+    a.scale = 0.088
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+FP8_BAD = [
+    ("null k_scale", dict(k_scale=None), 1),
+    ("null v_scale", dict(v_scale=None), 1),
+    ("d=64", dict(d=64), 2),
+    ("d=256", dict(d=256), 2),
+    ("ratio", dict(h_q=6, h_kv=4), 2),
+    ("split 100", dict(split_size=100), 2),
+    ("token stride 8 bytes", dict(k_st=8), 3),
+    ("head stride 24 bytes", dict(v_sh=24), 3),
+    ("huge token stride", dict(k_st=1 << 24), 3),
+    ("misaligned k", dict(k=FAKE + 8), 4),
+    ("misaligned scale", dict(v_scale=FAKE + 2), 4),
+]
+
+
+@pytest.mark.parametrize("name,over,code", FP8_BAD, ids=[c[0] for c in FP8_BAD])
+def test_decode_fp8_rejects(name, over, code):
+    lib = afa.load_library()
+    a = good_fp8(**over)
+    st = lib.attn_fwd_decode_fp8(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert st == code, (st, lib.attn_last_error())
+
+
+def test_decode_fp8_workspace_checks():
+    lib = afa.load_library()
+    a = good_fp8()
+    need = lib.attn_fwd_decode_workspace_size(4, 128, 128, 8192, 512)
+    assert lib.attn_fwd_decode_fp8(ctypes.byref(a), None, need, None) == 6
+    assert lib.attn_fwd_decode_fp8(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
+    assert lib.attn_fwd_decode_fp8(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4
 
 
 def test_decode_workspace_checks():

@@ -8,7 +8,7 @@ import torch
 
 import attention_forward_attn_amd as afa
 import oracle
-from attention_forward_attn_amd.inputs import WORKLOADS, decode_inputs, paged_decode_inputs
+from attention_forward_attn_amd.inputs import WORKLOADS, decode_inputs, fp8_decode_inputs, paged_decode_inputs
 from parity_util import check
 
 pytestmark = pytest.mark.gpu
@@ -206,5 +206,70 @@ def test_decode_paged_full_size():
     out, lse = run_paged(inp, w.len_hi, w.split)
     o_ref, l_ref = oracle.decode_ref(inp["q"], inp["k"], inp["v"], inp["kv_start"], inp["kv_len"],
                                      1 / math.sqrt(w.d))
+    check(out, lse, o_ref, l_ref, w.name)
+
+
+# --- FP8 (E4M3) KV cache --------------------------------------------------
+
+def run_fp8(inp, max_len, split=512, sinks=None):
+    q = inp["q"].to(DEV)
+    k8, v8 = inp["k8"].to(DEV), inp["v8"].to(DEV)
+    ksc, vsc = inp["k_scale"].to(DEV), inp["v_scale"].to(DEV)
+    ks, kl = inp["kv_start"].to(DEV), inp["kv_len"].to(DEV)
+    d = q.shape[-1]
+    ws = torch.full((afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split),),
+                    255, dtype=torch.uint8, device=DEV)  # NaN-poisoned partials
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+    sd = None if sinks is None else sinks.to(DEV)
+    afa.decode_fp8(q, k8, v8, ksc, vsc, ks, kl, max_len, sinks=sd, split_size=split, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+FP8 = [
+    # B, h_q, h_kv, len_lo, len_hi, split
+    (4, 128, 1, 1, 1500, 512),
+    (5, 16, 4, 0, 700, 128),
+    (3, 256, 2, 100, 1030, 256),
+    (2, 8, 8, 1, 300, 64),
+]
+
+
+@pytest.mark.parametrize("case", FP8, ids=[str(c) for c in FP8])
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_decode_fp8_small(case, with_sink):
+    B, h_q, h_kv, lo, hi, split = case
+    print(f"fp8 decode case {case} sink={with_sink}", flush=True)
+    inp = fp8_decode_inputs(B, h_q, h_kv, 128, lo, hi, 41, with_sink)
+    out, lse = run_fp8(inp, hi, split, inp["sinks"])
+    o_ref, l_ref = oracle.decode_fp8_ref(inp["q"], inp["k8"].numpy(), inp["v8"].numpy(), inp["k_scale"],
+                                         inp["v_scale"], inp["kv_start"], inp["kv_len"], 1 / math.sqrt(128),
+                                         sinks=inp["sinks"])
+    check(out, lse, o_ref, l_ref, str(case))
+
+
+def test_decode_fp8_equals_bf16_on_exact_values():
+    """Power-of-two scales make every dequantized value a bf16 value: the FP8 path
+    then matches the bf16 decode on the dequantized cache bit for bit."""
+    inp = fp8_decode_inputs(5, 64, 2, 128, 1, 1500, 42, True)
+    inp["k_scale"] = torch.tensor([2.0 ** -6, 2.0 ** -7])
+    inp["v_scale"] = torch.tensor([2.0 ** -5, 2.0 ** -8])
+    for n in ("k", "v"):
+        vals = inp[n + "8"].view(torch.float8_e4m3fn).to(torch.float32) * inp[n + "_scale"][None, :, None]
+        inp[n] = vals.to(torch.bfloat16)
+        assert torch.equal(inp[n].to(torch.float32), vals)
+    out8, lse8 = run_fp8(inp, 1500, 512, inp["sinks"])
+    outb, lseb = run_decode(inp, 1500, 512, inp["sinks"])
+    assert torch.equal(out8, outb) and torch.equal(lse8, lseb)
+
+
+def test_decode_fp8_full_size():
+    w = WORKLOADS["mqa_decode_fp8_B64_hq128_d128"]
+    print(f"full-size fp8 decode {w.name}", flush=True)
+    inp = fp8_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed)
+    out, lse = run_fp8(inp, w.len_hi, w.split)
+    o_ref, l_ref = oracle.decode_fp8_ref(inp["q"], inp["k8"].numpy(), inp["v8"].numpy(), inp["k_scale"],
+                                         inp["v_scale"], inp["kv_start"], inp["kv_len"], 1 / math.sqrt(w.d))
     check(out, lse, o_ref, l_ref, w.name)
 
