@@ -11,7 +11,7 @@ hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s) {
   switch (d) {
     case 64: return launch_decode_split<64, 4, 1, 64, 2, 4>(p, s);
     case 128: return launch_decode_split<128, 4, 1, 32, 2, 3>(p, s);
-    default: return launch_decode_split<256, 4, 1, 32, 2, 1>(p, s);
+    default: return launch_decode_split<256, 4, 1, 32, 2, 2>(p, s);
   }
 }
 
@@ -19,7 +19,7 @@ hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s) {
   switch (d) {
     case 64: return launch_decode_split<64, 4, 1, 64, 2, 4, true>(p, s);
     case 128: return launch_decode_split<128, 4, 1, 32, 2, 3, true>(p, s);
-    default: return launch_decode_split<256, 4, 1, 32, 2, 1, true>(p, s);
+    default: return launch_decode_split<256, 4, 1, 32, 2, 2, true>(p, s);
   }
 }
 
