@@ -6,9 +6,9 @@ namespace attn {
 
 hipError_t prefill_d64(const PrefillParams &p, int mask, int n_units, hipStream_t s) {
   switch (mask) {
-    case kMaskNone: return launch_prefill<64, 4, 128, false, false, 2>(p, n_units, s);
-    case kMaskCausal: return launch_prefill<64, 4, 128, true, false, 2>(p, n_units, s);
-    default: return launch_prefill<64, 4, 128, true, true, 2>(p, n_units, s);
+    case kMaskNone: return launch_prefill<64, 4, 64, false, false, 4>(p, n_units, s);
+    case kMaskCausal: return launch_prefill<64, 4, 64, true, false, 4>(p, n_units, s);
+    default: return launch_prefill<64, 4, 64, true, true, 4>(p, n_units, s);
   }
 }
 
