@@ -6,6 +6,7 @@ leg may import this package.  It shares no code with the HIP library.
 
 from .attention import (  # noqa: F401
     NEG_INF,
+    attention_backward_ref,
     attention_flops,
     attention_ref,
     fp8_e4m3_value,

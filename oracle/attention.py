@@ -31,6 +31,8 @@ What it computes, and where the pages define it:
   per-sequence KV cache, unsplit and split into fixed-size key chunks.
 * ``decode_paged_ref`` -- the same decode over a paged KV cache addressed
   through a block table (reading of the layout stated in its docstring).
+* ``attention_backward_ref`` -- dQ, dK, dV of the attention output for an
+  incoming gradient dO (reading stated in its docstring).
 * ``decode_fp8_ref`` -- the same decode over an FP8 (E4M3) KV cache with a
   per-kv-head scale for K and for V (``fp8_e4m3_value`` decodes the codes from
   the format's definition).
@@ -391,6 +393,54 @@ def decode_fp8_ref(q, k_codes, v_codes, k_scale, v_scale, kv_start, kv_len, scal
     k = fp8_e4m3_value(np.asarray(k_codes)) * ks[None, :, None]
     v = fp8_e4m3_value(np.asarray(v_codes)) * vs[None, :, None]
     return decode_ref(q, k, v, kv_start, kv_len, scale, sinks=sinks)
+
+
+def attention_backward_ref(q, k, v, d_o, scale: float, causal: bool = False):
+    """Gradients of the attention output: (dQ, dK, dV) in float64, shapes of q, k, v.
+
+    The pages name the backward kernels and ask for a deterministic one (SM120
+    research page, feature-parity and tuning notes) but define no algorithm
+    beyond the forward; the planner page says a backward needs its own design.
+    Reading used: the gradients of L = sum(dO * O) for O of attention_ref
+    (no incoming gradient on the LSE, no window, no sink), by the chain rule
+    through the softmax, per batch b and query head h (kv head g):
+
+        P    = softmax_j(scale * Q K^T + mask)          (rows that see no key: 0)
+        dV_g = sum_{h in g} P^T dO
+        dP   = dO V^T
+        D_i  = sum_t dO[i,t] O[i,t]   (= sum_j P_ij dP_ij)
+        dS   = P * (dP - D)
+        dQ   = scale * dS K,   dK_g = sum_{h in g} scale * dS^T Q
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    d_o = _as_f64(d_o)
+    b, h_q, h_kv, s_k, d = _check_shapes(q, k, v)
+    s_q = q.shape[2]
+    ratio = h_q // h_kv
+    vis = visible_keys(s_q, s_k, causal, 0)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for bi in range(b):
+        for h in range(h_q):
+            g = h // ratio
+            s = scale * (q[bi, h] @ k[bi, g].T)
+            s = np.where(vis, s, NEG_INF)
+            m = s.max(axis=1) if s_k > 0 else np.full(s_q, NEG_INF)
+            m_safe = np.where(np.isfinite(m), m, 0.0)
+            num = np.exp(s - m_safe[:, None])
+            z = num.sum(axis=1)
+            p = num / np.where(z > 0, z, 1.0)[:, None]
+            o = p @ v[bi, g]
+            dp = d_o[bi, h] @ v[bi, g].T
+            dd = (d_o[bi, h] * o).sum(axis=1)
+            ds = p * (dp - dd[:, None])
+            dq[bi, h] = scale * (ds @ k[bi, g])
+            dk[bi, g] += scale * (ds.T @ q[bi, h])
+            dv[bi, g] += p.T @ d_o[bi, h]
+    return dq, dk, dv
 
 
 def attention_flops(b: int, h_q: int, s_q: int, s_k: int, d: int, causal: bool,

@@ -13,6 +13,7 @@ disagrees with:
   permutation, empty rows, the flop count,
 * a textbook routine: torch's CPU fp64 ``scaled_dot_product_attention``,
 * the paged-cache decode against the brute force on the keys it scattered,
+* the backward gradients against torch's fp64 autograd,
 * the FP8 E4M3 decoder against torch's float8_e4m3fn type on all 256 codes,
   and the FP8 decode against the brute force on torch-dequantized values,
 * the streaming recurrence and the split/merge reformulation, and the
@@ -450,6 +451,37 @@ def pin_fp8_decode_matches_brute(orc):
             _close(l[bi], bl[0, :, 0], 1e-12, "fp8 decode LSE")
 
 
+def pin_backward_matches_autograd(orc):
+    """dQ, dK, dV equal torch's fp64 autograd through its textbook attention (GQA by repeated heads)."""
+    import torch
+
+    rng = _rng(27)
+    for (b, h_q, h_kv, s_q, s_k, d, causal) in [(1, 2, 2, 5, 5, 4, False), (2, 4, 2, 6, 6, 3, True),
+                                                 (1, 4, 1, 4, 7, 5, True), (1, 2, 1, 7, 3, 2, True)]:
+        q = rng.standard_normal((b, h_q, s_q, d))
+        k = rng.standard_normal((b, h_kv, s_k, d))
+        v = rng.standard_normal((b, h_kv, s_k, d))
+        do = rng.standard_normal((b, h_q, s_q, d))
+        dq, dk, dv = orc.attention_backward_ref(q, k, v, do, 0.6, causal)
+        tq = torch.tensor(q, requires_grad=True)
+        tk = torch.tensor(k, requires_grad=True)
+        tv = torch.tensor(v, requires_grad=True)
+        r = h_q // h_kv
+        kk = tk.repeat_interleave(r, dim=1)
+        vv = tv.repeat_interleave(r, dim=1)
+        s = 0.6 * tq @ kk.transpose(-1, -2)
+        if causal:
+            off = s_k - s_q
+            mask = torch.arange(s_k)[None, :] <= torch.arange(s_q)[:, None] + off
+            s = s.masked_fill(~mask, float("-inf"))
+        p = torch.softmax(s, dim=-1).nan_to_num(0.0)  # rows that see no key: zero
+        o = p @ vv
+        (o * torch.tensor(do)).sum().backward()
+        _close(dq, tq.grad.numpy(), 1e-10, "dQ")
+        _close(dk, tk.grad.numpy(), 1e-10, "dK")
+        _close(dv, tv.grad.numpy(), 1e-10, "dV")
+
+
 def pin_split_merge_equals_unsplit(orc):
     """Split-KV partials merged by LSE equal the unsplit decode (disjoint key sets)."""
     q, k, v, starts, lens = _decode_case(23)
@@ -520,6 +552,7 @@ PINS = [
     pin_paged_decode_matches_brute,
     pin_fp8_codes_match_library,
     pin_fp8_decode_matches_brute,
+    pin_backward_matches_autograd,
     pin_split_merge_equals_unsplit,
     pin_head_dim_halves_do_not_merge,
     pin_flop_count,

@@ -60,6 +60,10 @@ MUTATIONS = [
     ("fp8: sign dropped", "sign = np.where((c >> 7) & 1, -1.0, 1.0)", "sign = np.where((c >> 7) & 1, 1.0, 1.0)"),
     ("fp8: scales swapped", "k = fp8_e4m3_value(np.asarray(k_codes)) * ks[None, :, None]",
      "k = fp8_e4m3_value(np.asarray(k_codes)) * vs[None, :, None]"),
+    ("bwd: D from P", "dd = (d_o[bi, h] * o).sum(axis=1)", "dd = (d_o[bi, h] * o).sum(axis=1) * 0.0"),
+    ("bwd: dK without scale", "dk[bi, g] += scale * (ds.T @ q[bi, h])", "dk[bi, g] += (ds.T @ q[bi, h])"),
+    ("bwd: dV transposed P", "dv[bi, g] += p.T @ d_o[bi, h]", "dv[bi, g] += p[:, :v.shape[2]].T @ d_o[bi, h][:p.shape[1]]"),
+    ("bwd: dQ from V", "dq[bi, h] = scale * (ds @ k[bi, g])", "dq[bi, h] = scale * (ds @ v[bi, g])"),
     ("flops count 2d per pair", "return 4 * d * pairs * b * h_q", "return 2 * d * pairs * b * h_q"),
 ]
 
