@@ -9,6 +9,7 @@ library; the first call does, and raises if the library has not been built.
 from ._binding import (  # noqa: F401
     LIB_PATH,
     AttnError,
+    backward,
     combine,
     decode,
     decode_fp8,

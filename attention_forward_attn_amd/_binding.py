@@ -96,6 +96,20 @@ class DecodeFp8Args(ctypes.Structure):
     ]
 
 
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("d_o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("b", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+        ("s_q", ctypes.c_int32), ("s_k", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_ss", ctypes.c_int64),
+        ("k_sb", ctypes.c_int64), ("k_sh", ctypes.c_int64), ("k_ss", ctypes.c_int64),
+        ("lse_sb", ctypes.c_int64), ("lse_sh", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+    ]
+
+
 class CombineArgs(ctypes.Structure):
     _fields_ = [
         ("o_parts", ctypes.c_void_p), ("lse_parts", ctypes.c_void_p),
@@ -131,6 +145,10 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd_decode_fp8.argtypes = [ctypes.POINTER(DecodeFp8Args), ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]
     lib.attn_fwd_decode_fp8.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int32] * 3
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_combine.argtypes = [ctypes.POINTER(CombineArgs), ctypes.c_void_p]
     lib.attn_combine.restype = ctypes.c_int
     lib.attn_fwd_decode_workspace_size.argtypes = [ctypes.c_int32] * 5
@@ -396,6 +414,55 @@ def decode_fp8(q, k8, v8, k_scale, v_scale, kv_start, kv_len, max_kv_len: int, *
     _check(lib.attn_fwd_decode_fp8(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
+
+
+def backward(q, k, v, o, d_o, lse, *, scale: float | None = None, causal: bool = False, dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of the prefill for an incoming gradient d_o, from the forward's o and lse.
+
+    q, o, d_o: bf16 [b, h_q, s_q, d] with identical strides; k, v: bf16
+    [b, h_kv, s_k, d] with identical strides; lse: fp32 [b, h_q, s_q] (unit
+    stride along s).  Returns (dq, dk, dv) laid out like q, k and v.
+    """
+    import torch
+
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("d_o", d_o)):
+        _require_cuda_bf16(name, t, 4)
+    if o.stride() != q.stride() or d_o.stride() != q.stride() or o.shape != q.shape or d_o.shape != q.shape:
+        raise ValueError("o and d_o must have q's shape and strides")
+    if v.stride() != k.stride() or v.shape != k.shape:
+        raise ValueError("v must have k's shape and strides")
+    if lse.dtype != torch.float32 or lse.dim() != 3 or lse.stride(-1) != 1:
+        raise ValueError("lse must be float32 [b, h_q, s_q] with unit stride along s")
+    b, h_q, s_q, d = q.shape
+    h_kv, s_k = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dq is None:
+        dq = torch.empty_strided(q.shape, q.stride(), dtype=torch.bfloat16, device=q.device)
+    if dk is None:
+        dk = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=q.device)
+    if dv is None:
+        dv = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=q.device)
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != k.stride():
+        raise ValueError("dq must have q's strides, dk and dv k's strides")
+    need = int(lib.attn_bwd_workspace_size(b, h_q, s_q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    a = BwdArgs()
+    a.q, a.k, a.v, a.o, a.d_o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), d_o.data_ptr()
+    a.lse = lse.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.b, a.h_q, a.h_kv, a.s_q, a.s_k, a.d = b, h_q, h_kv, s_q, s_k, d
+    a.q_sb, a.q_sh, a.q_ss = q.stride(0), q.stride(1), q.stride(2)
+    a.k_sb, a.k_sh, a.k_ss = k.stride(0), k.stride(1), k.stride(2)
+    a.lse_sb, a.lse_sh = lse.stride(0), lse.stride(1)
+    a.scale = scale
+    a.causal = 1 if causal else 0
+    _check(lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
+                        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
 
 
 def combine(o_parts, lse_parts, *, out=None, lse=None, return_lse: bool = True, stream=None):

@@ -367,6 +367,65 @@ attn_status attn_fwd_decode_paged(const attn_decode_paged_args *a, void *workspa
                     stream);
 }
 
+size_t attn_bwd_workspace_size(int32_t b, int32_t h_q, int32_t s_q) {
+  if (b < 1 || h_q < 1 || s_q < 0) return 0;
+  return (size_t)b * h_q * (size_t)(s_q > 0 ? s_q : 1) * 4;
+}
+
+attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
+  if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
+  if (a->b < 1 || a->h_q < 1 || a->h_kv < 1 || a->s_q < 0 || a->s_k < 0)
+    return fail(ATTN_ERR_SHAPE, "need b, h_q, h_kv >= 1 and s_q, s_k >= 0");
+  if (a->h_q % a->h_kv != 0)
+    return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
+  if (a->d != 128) return fail(ATTN_ERR_SHAPE, "backward supports d = 128 (got %d)", a->d);
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1");
+  if (!(std::isfinite(a->scale) && a->scale > 0.0f))
+    return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+  if (!a->q || !a->k || !a->v || !a->o || !a->d_o || !a->lse || !a->dq || !a->dk || !a->dv)
+    return fail(ATTN_ERR_NULL, "q, k, v, o, d_o, lse, dq, dk and dv must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) || !aligned16(a->d_o) ||
+      !aligned16(a->dq) || !aligned16(a->dk) || !aligned16(a->dv) || !aligned4(a->lse))
+    return fail(ATTN_ERR_ALIGN, "bf16 tensors must be 16-byte aligned, lse 4-byte aligned");
+  const int64_t st[] = {a->q_sb, a->q_sh, a->q_ss, a->k_sb, a->k_sh, a->k_ss};
+  for (int64_t s : st)
+    if (!bf16_stride_ok(s)) return fail(ATTN_ERR_STRIDE, "bf16 strides must be non-negative multiples of 8 elements");
+  if (a->lse_sb < 0 || a->lse_sh < 0) return fail(ATTN_ERR_STRIDE, "lse strides must be >= 0");
+  if (a->q_ss >= kMaxRowStride || a->k_ss >= kMaxRowStride)
+    return fail(ATTN_ERR_STRIDE, "row strides must be below 2^24 elements");
+  if ((int64_t)a->b * a->h_q * ((a->s_q + 127) / 128) > INT32_MAX ||
+      (int64_t)a->b * a->h_kv * ((a->s_k + 127) / 128) > INT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "backward grid too large");
+  const size_t need = attn_bwd_workspace_size(a->b, a->h_q, a->s_q);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (a->s_q == 0 && a->s_k == 0) return ok();
+
+  attn::BwdParams p;
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k = static_cast<const uint16_t *>(a->k);
+  p.v = static_cast<const uint16_t *>(a->v);
+  p.o = static_cast<const uint16_t *>(a->o);
+  p.d_o = static_cast<const uint16_t *>(a->d_o);
+  p.lse = a->lse;
+  p.dq = static_cast<uint16_t *>(a->dq);
+  p.dk = static_cast<uint16_t *>(a->dk);
+  p.dv = static_cast<uint16_t *>(a->dv);
+  p.dsum = static_cast<float *>(workspace);
+  p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_ss = a->q_ss;
+  p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_ss = a->k_ss;
+  p.lse_sb = a->lse_sb; p.lse_sh = a->lse_sh;
+  p.b = a->b; p.h_q = a->h_q; p.h_kv = a->h_kv; p.s_q = a->s_q; p.s_k = a->s_k;
+  p.ratio = a->h_q / a->h_kv;
+  p.c = a->scale * attn::kLog2e;
+  p.scale = a->scale;
+  hipError_t e = attn::backward_d128(p, a->causal != 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
 attn_status attn_combine(const attn_combine_args *a, void *stream) {
   if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
   if (a->n_parts < 1 || a->n_parts > 1024) return fail(ATTN_ERR_SHAPE, "n_parts must be in [1, 1024]");

@@ -1,0 +1,280 @@
+// Attention backward at head dim 128: dQ, dK, dV for an incoming dO, from the
+// forward's O and LSE (no window, no sink), deterministic (no atomics).
+//
+// Two kernels, both built from the forward's tile engine:
+//   * dQ (one workgroup per 128 query rows, 4 waves x 32 rows): the forward
+//     layout S^T = K.Q^T (rows in lanes, keys in registers), plus
+//     dP^T = V.dO^T, then dQ^T += K^T.dS^T with dS = P * (dP - D).  It also
+//     writes D_i = sum_t dO[i,t] O[i,t] for the second kernel.
+//   * dK/dV (one workgroup per 128 keys of one kv head, 4 waves x 32 keys):
+//     the same shapes with the roles of queries and keys swapped: S = Q.K^T
+//     and dP = dO.V^T with keys in lanes and query rows in registers, then
+//     dV^T += dO^T.P and dK^T += Q^T.dS, summed over every query head of the
+//     kv group (a workgroup owns its keys, so no atomics are needed).
+// A streamed tile is needed both row-wise (score-like MMA, A operand from
+// 16-byte row segments) and transposed (value-like MMA, transpose reads), and
+// the two read patterns want different LDS chunk swizzles, so each such tile
+// is staged twice, once per swizzle.
+#pragma once
+
+#include "tile.hpp"
+
+namespace attn {
+
+// Packs eight f32 values of accumulator block (T>>1), registers 8(T&1)..+7,
+// into the bf16 operand of value-MMA k-step T (the order softmax_exp uses).
+template <int NKB, int NPV>
+__device__ __forceinline__ void pack_operand(const f32x16 (&x)[NKB], u32x4 (&pk)[NPV]) {
+#pragma unroll
+  for (int t = 0; t < NPV; ++t) {
+    const int kb = t >> 1, r0 = (t & 1) * 8;
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(x[kb][r0 + 2 * q], x[kb][r0 + 2 * q + 1]);
+    pk[t] = v;
+  }
+}
+
+// Loads the 32 x D bf16 block of rows r0.. (row stride rs) as the B operand
+// of the score MMA (lane: row r0 + lane%32, 8 columns per k-step); rows past
+// n_rows read row n_rows-1 (their results are never used).
+template <int NKK>
+__device__ __forceinline__ void load_b_rows(u32x4 (&reg)[NKK], const uint16_t *base, int64_t rs, int r,
+                                            int n_rows, int hi) {
+  const uint16_t *pr = base + (int64_t)min(r, n_rows - 1) * rs + 8 * hi;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) reg[kk] = *reinterpret_cast<const u32x4 *>(pr + kk * 16);
+}
+
+// Stores a transposed accumulator (lane = row, registers = head-dim columns)
+// times f as bf16 rows.
+template <int NDB>
+__device__ __forceinline__ void store_rows(uint16_t *op, const f32x16 (&a)[NDB], float f) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      u32x2 val;
+      val[0] = pack_bf16x2(a[db][4 * gi + 0] * f, a[db][4 * gi + 1] * f);
+      val[1] = pack_bf16x2(a[db][4 * gi + 2] * f, a[db][4 * gi + 3] * f);
+      *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and D).
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdParams p) {
+  using T = Tile<D, 4, BN>;
+  constexpr int BM = 128;
+  constexpr int STAGE = 3 * T::TILE_BYTES;  // [K, row swizzle][K, transpose swizzle][V, row swizzle]
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE / 2];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
+  const int n_qt = (p.s_q + BM - 1) / BM;
+  const int bh = blockIdx.x / n_qt, qt = blockIdx.x - bh * n_qt;
+  const int bi = bh / p.h_q, h = bh - bi * p.h_q;
+  const int g = h / p.ratio;
+  const int q0 = qt * BM;
+  const int off = p.s_k - p.s_q;
+  const int i_last = min(p.s_q, q0 + BM) - 1;
+  const int kend = CAUSAL ? max(0, min(p.s_k, i_last + off + 1)) : p.s_k;
+  const int n_tiles = (kend + BN - 1) / BN;
+
+  const int w_lo = q0 + wave * 32;
+  const int w_hi = min(w_lo + 31, p.s_q - 1);
+  const int row = w_lo + lr;
+  const bool row_ok = row < p.s_q;
+
+  const uint16_t *kbase = p.k + bi * p.k_sb + g * p.k_sh;
+  const uint16_t *vbase = p.v + bi * p.k_sb + g * p.k_sh;
+  const int64_t qrow0 = bi * p.q_sb + h * p.q_sh;  // q, o, do, dq share the row layout
+
+  u32x4 qreg[T::NKK], dreg[T::NKK];
+  load_b_rows(qreg, p.q + qrow0, p.q_ss, row, p.s_q, hi);
+  load_b_rows(dreg, p.d_o + qrow0, p.q_ss, row, p.s_q, hi);
+  // D = rowsum(dO * O) over this lane's half of the columns, then both halves.
+  float dsum = 0.0f;
+  {
+    u32x4 oreg[T::NKK];
+    load_b_rows(oreg, p.o + qrow0, p.q_ss, row, p.s_q, hi);
+#pragma unroll
+    for (int kk = 0; kk < T::NKK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t a = oreg[kk][e], b = dreg[kk][e];
+        dsum = fmaf(__uint_as_float(a << 16), __uint_as_float(b << 16), dsum);
+        dsum = fmaf(__uint_as_float(a & 0xffff0000u), __uint_as_float(b & 0xffff0000u), dsum);
+      }
+  }
+  const float dd = sum_across_halves(dsum);
+  const float lse = row_ok ? p.lse[bi * p.lse_sb + h * p.lse_sh + row] : kNegInf;
+  // A row that saw no key has P = 0: exp2(s*c - inf) = 0.
+  const float lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
+  if (row_ok && hi == 0) p.dsum[(bi * p.h_q + h) * (int64_t)p.s_q + row] = dd;
+
+  f32x16 acc[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) acc[db] = f32x16{};
+
+  typename T::Lane ln;
+  T::init_dma(ln, p.k_ss, p.k_ss, wave, lane);  // K and V share the row stride (checked on the host)
+  const uint32_t base = lds_offset(smem);
+  T::init_mma(ln, base, base + T::TILE_BYTES, lane);
+  auto load = [&](int buf, int t) {
+    uint16_t *st = smem + buf * (STAGE / 2);
+    T::dma1(ln, false, st, kbase, p.k_ss, t * BN, p.s_k, wave);
+    T::dma1(ln, true, st + T::TILE_ELEMS, kbase, p.k_ss, t * BN, p.s_k, wave);
+    T::dma1(ln, false, st + 2 * T::TILE_ELEMS, vbase, p.k_ss, t * BN, p.s_k, wave);
+  };
+  if (n_tiles > 0) load(0, 0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int cur = t & 1;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 1 < n_tiles) load(cur ^ 1, t + 1);
+    const int j0 = t * BN;
+    if (w_lo < p.s_q && (!CAUSAL || j0 <= w_hi + off)) {
+      const uint32_t so = cur * STAGE;
+      f32x16 s[T::NKB], dp[T::NKB];
+      T::scores(s, qreg, ln, so);
+      T::scores(dp, dreg, ln, so + 2 * T::TILE_BYTES);
+      const int lim = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = j0 + T::key_of(kb, i, hi);
+          const float pv = j > lim ? 0.0f : fast_exp2(fmaf(s[kb][i], p.c, -lse2));
+          s[kb][i] = pv * (dp[kb][i] - dd);  // dS
+        }
+      u32x4 pk[T::NPV];
+      pack_operand(s, pk);
+      T::values(acc, pk, ln, so);  // dQ^T += K^T . dS^T (K through the transpose-swizzled copy)
+    }
+  }
+  if (row_ok) store_rows(p.dq + qrow0 + (int64_t)row * p.q_ss + 4 * hi, acc, p.scale);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  Reads D written by bwd_dq_kernel.
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+  using T = Tile<D, 4, BN>;  // here the streamed "keys" of the engine are query rows
+  constexpr int BK = 128;    // keys per workgroup
+  constexpr int STAGE = 4 * T::TILE_BYTES;  // [Q row][Q transpose][dO row][dO transpose]
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE / 2];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
+  const int n_kt = (p.s_k + BK - 1) / BK;
+  const int bg = blockIdx.x / n_kt, kt = blockIdx.x - bg * n_kt;
+  const int bi = bg / p.h_kv, g = bg - bi * p.h_kv;
+  const int off = p.s_k - p.s_q;
+  const int w_key0 = kt * BK + wave * 32;
+  const int key = w_key0 + lr;
+  const bool key_ok = key < p.s_k;
+
+  const int64_t krow0 = bi * p.k_sb + g * p.k_sh;  // k, v, dk, dv share the row layout
+  u32x4 kreg[T::NKK], vreg[T::NKK];
+  load_b_rows(kreg, p.k + krow0, p.k_ss, key, p.s_k, hi);
+  load_b_rows(vreg, p.v + krow0, p.k_ss, key, p.s_k, hi);
+
+  f32x16 dk[T::NDB], dv[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) dk[db] = dv[db] = f32x16{};
+
+  // Query rows that see any key of this workgroup: i + off >= first key.
+  const int r_begin = CAUSAL ? max(0, kt * BK - off) : 0;
+  const int t_begin = r_begin / BN;
+  const int t_end = (p.s_q + BN - 1) / BN;
+  const int n_tiles = t_begin < t_end ? t_end - t_begin : 0;
+
+  typename T::Lane ln;
+  T::init_dma(ln, p.q_ss, p.q_ss, wave, lane);  // Q and dO share the row stride (checked on the host)
+  const uint32_t base = lds_offset(smem);
+  T::init_mma(ln, base, base + T::TILE_BYTES, lane);
+
+  for (int h = g * p.ratio; h < (g + 1) * p.ratio; ++h) {
+    const int64_t qrow0 = bi * p.q_sb + h * p.q_sh;
+    const uint16_t *qbase = p.q + qrow0, *dobase = p.d_o + qrow0;
+    const float *lse_h = p.lse + bi * p.lse_sb + h * p.lse_sh;
+    const float *d_h = p.dsum + (bi * p.h_q + h) * (int64_t)p.s_q;
+    auto load = [&](int buf, int t) {
+      uint16_t *st = smem + buf * (STAGE / 2);
+      T::dma1(ln, false, st, qbase, p.q_ss, t * BN, p.s_q, wave);
+      T::dma1(ln, true, st + T::TILE_ELEMS, qbase, p.q_ss, t * BN, p.s_q, wave);
+      T::dma1(ln, false, st + 2 * T::TILE_ELEMS, dobase, p.q_ss, t * BN, p.s_q, wave);
+      T::dma1(ln, true, st + 3 * T::TILE_ELEMS, dobase, p.q_ss, t * BN, p.s_q, wave);
+    };
+    __syncthreads();  // the previous head's last tile is consumed
+    if (n_tiles > 0) load(0, t_begin);
+    for (int n = 0; n < n_tiles; ++n) {
+      const int t = t_begin + n, cur = n & 1;
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (n + 1 < n_tiles) load(cur ^ 1, t + 1);
+      const int i0 = t * BN;
+      // this wave has keys, and (causal) the tile's last row reaches its first key
+      if (w_key0 < p.s_k && (!CAUSAL || min(i0 + BN, p.s_q) - 1 + off >= w_key0)) {
+        {
+          const uint32_t so = cur * STAGE;
+          f32x16 s[T::NKB], dp[T::NKB];
+          T::scores(s, kreg, ln, so);                        // S = Q.K^T: rows in registers, keys in lanes
+          T::scores(dp, vreg, ln, so + 2 * T::TILE_BYTES);   // dP = dO.V^T
+#pragma unroll
+          for (int rb = 0; rb < T::NKB; ++rb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              // rows i0 + 32rb + 8q4 + 4hi + 0..3 hold registers 4q4..4q4+3
+              const int r4 = i0 + 32 * rb + 8 * q4 + 4 * hi;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = r4 + e;
+                const bool vis = r < p.s_q && key_ok && (!CAUSAL || key <= r + off);
+                float pv = 0.0f, dsv = 0.0f;
+                if (vis) {
+                  const float l = lse_h[r];
+                  pv = l == kNegInf ? 0.0f : fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -l * kLog2e));
+                  dsv = pv * (dp[rb][4 * q4 + e] - d_h[r]);
+                }
+                s[rb][4 * q4 + e] = pv;
+                dp[rb][4 * q4 + e] = dsv;
+              }
+            }
+          u32x4 pp[T::NPV], pd[T::NPV];
+          pack_operand(s, pp);
+          pack_operand(dp, pd);
+          T::values(dv, pp, ln, so + 2 * T::TILE_BYTES);  // dV^T += dO^T . P
+          T::values(dk, pd, ln, so);                        // dK^T += Q^T . dS
+        }
+      }
+    }
+  }
+  if (key_ok) {
+    store_rows(p.dk + krow0 + (int64_t)key * p.k_ss + 4 * hi, dk, p.scale);
+    store_rows(p.dv + krow0 + (int64_t)key * p.k_ss + 4 * hi, dv, 1.0f);
+  }
+}
+
+template <int D, int BN, bool CAUSAL>
+hipError_t launch_backward(const BwdParams &p, hipStream_t stream) {
+  const int n_qt = (p.s_q + 127) / 128, n_kt = (p.s_k + 127) / 128;
+  if (n_qt > 0) {  // dQ (zero when there are no keys) and D
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL>), dim3(p.b * p.h_q * n_qt), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n_kt > 0) {  // dK, dV (zero when there are no rows)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BN, CAUSAL>), dim3(p.b * p.h_kv * n_kt), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace attn

@@ -36,6 +36,22 @@ struct PrefillParams {
   float c;           // scale * log2(e): logits in base-2 units
 };
 
+// Device-side parameters of the backward kernels.  q, o, d_o and dq share one
+// [b, h_q, s_q, d] layout (q strides); k, v, dk and dv share one [b, h_kv,
+// s_k, d] layout (k strides); dsum is fp32 [b, h_q, s_q] scratch.
+struct BwdParams {
+  const uint16_t *q, *k, *v, *o, *d_o;
+  const float *lse;
+  uint16_t *dq, *dk, *dv;
+  float *dsum;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t lse_sb, lse_sh;
+  int32_t b, h_q, h_kv, s_q, s_k, ratio;
+  float c;      // scale * log2(e)
+  float scale;
+};
+
 // Device-side parameters of the split-KV decode kernel.
 struct DecodeParams {
   const uint16_t *q, *k, *v;

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 3
+#define ATTN_FWD_ABI_VERSION 4
 
 typedef enum {
   ATTN_OK = 0,
@@ -232,6 +232,41 @@ typedef struct {
 } attn_decode_fp8_args;
 
 /*
+ * Backward of the prefill: dQ, dK, dV for an incoming gradient dO of O, from
+ * the forward's O and LSE.  The pages list backward kernels and a
+ * deterministic backward among the gaps to fill (SM120 research page) and
+ * leave the algorithm to a design of its own (FA4 planner page, boundaries);
+ * the one taken here is the chain rule through the softmax, with
+ * P = exp(scale*QK^T - LSE), D_i = sum_t dO[i,t] O[i,t], dS = P*(dP - D),
+ * dQ = scale*dS K, dK = scale*dS^T Q, dV = P^T dO (dK and dV summed over the
+ * query heads of each kv head).  No window and no sink; the LSE gets no
+ * gradient.  Deterministic: no atomics, every output element is written by
+ * exactly one thread in a fixed order.
+ *
+ * q, o, d_o, dq: bf16 [b, h_q, s_q, d], one shared stride set (q_sb, q_sh,
+ *       q_ss); k, v, dk, dv: bf16 [b, h_kv, s_k, d], one shared stride set
+ *       (k_*); lse: fp32 (bi, h, i) at lse + bi*lse_sb + h*lse_sh + i.
+ * workspace: attn_bwd_workspace_size(b, h_q, s_q) bytes, 16-byte aligned,
+ *       caller-owned (row sums D between the two kernels).
+ * Two kernels run on `stream` (dQ and D, then dK/dV).  Supported: d = 128;
+ * causal (bottom-right) or not; h_q % h_kv == 0.
+ */
+typedef struct {
+  const void *q, *k, *v, *o, *d_o;
+  const float *lse;
+  void *dq, *dk, *dv;
+  int32_t b, h_q, h_kv, s_q, s_k, d;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t lse_sb, lse_sh;
+  float scale;
+  int32_t causal;
+} attn_bwd_args;
+
+/* Bytes of device workspace attn_bwd needs (0 on invalid sizes). */
+size_t attn_bwd_workspace_size(int32_t b, int32_t h_q, int32_t s_q);
+
+/*
  * Merge n_parts partial attention results computed over DISJOINT key sets
  * (STAGE_D.md page, "O rescale (kt>0)" workaround): per row, with
  * M = max_p lse_p and w_p = exp(lse_p - M),
@@ -273,6 +308,7 @@ attn_status attn_fwd_decode_paged(const attn_decode_paged_args *args, void *work
 attn_status attn_fwd_decode_fp8(const attn_decode_fp8_args *args, void *workspace, size_t workspace_bytes,
                                 void *stream);
 attn_status attn_combine(const attn_combine_args *args, void *stream);
+attn_status attn_bwd(const attn_bwd_args *args, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *attn_status_str(attn_status s);

@@ -12,8 +12,8 @@ import re
 import pytest
 
 import attention_forward_attn_amd as afa
-from attention_forward_attn_amd._binding import (CombineArgs, DecodeArgs, DecodeFp8Args, DecodePagedArgs,
-                                                 PrefillArgs)
+from attention_forward_attn_amd._binding import (BwdArgs, CombineArgs, DecodeArgs, DecodeFp8Args,
+                                                 DecodePagedArgs, PrefillArgs)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("attn_fwd_prefill", "attn_fwd_decode", "attn_fwd_decode_paged", "attn_fwd_decode_fp8",
-                 "attn_combine",
+                 "attn_combine", "attn_bwd", "attn_bwd_workspace_size",
                  "attn_fwd_decode_workspace_size", "attn_status_str", "attn_last_error",
                  "attn_abi_version"):
         assert want in names
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     lib = afa.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
 
 
 def test_status_strings():
@@ -314,3 +314,50 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         afa.prefill(q, q, q)
+
+
+def good_bwd(**over):
+    a = BwdArgs()
+    a.q = a.k = a.v = a.o = a.d_o = a.lse = a.dq = a.dk = a.dv = FAKE
+    a.b, a.h_q, a.h_kv, a.s_q, a.s_k, a.d = 2, 16, 16, 4096, 4096, 128
+    a.q_sb, a.q_sh, a.q_ss = 16 * 4096 * 128, 4096 * 128, 128
+    a.k_sb, a.k_sh, a.k_ss = 16 * 4096 * 128, 4096 * 128, 128
+    a.lse_sb, a.lse_sh = 16 * 4096, 4096
+    a.scale = 0.088
+    a.causal = 1
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+BWD_BAD = [
+    ("null lse", dict(lse=None), 1),
+    ("null dv", dict(dv=None), 1),
+    ("d=64", dict(d=64), 2),
+    ("ratio", dict(h_q=6, h_kv=4), 2),
+    ("causal 2", dict(causal=2), 2),
+    ("zero scale", dict(scale=0.0), 2),
+    ("odd row stride", dict(q_ss=100), 3),
+    ("huge row stride", dict(k_ss=1 << 24), 3),
+    ("misaligned dq", dict(dq=FAKE + 8), 4),
+    ("misaligned lse", dict(lse=FAKE + 2), 4),
+]
+
+
+@pytest.mark.parametrize("name,over,code", BWD_BAD, ids=[c[0] for c in BWD_BAD])
+def test_bwd_rejects(name, over, code):
+    lib = afa.load_library()
+    a = good_bwd(**over)
+    st = lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert st == code, (st, lib.attn_last_error())
+
+
+def test_bwd_workspace_checks():
+    lib = afa.load_library()
+    a = good_bwd()
+    need = lib.attn_bwd_workspace_size(2, 16, 4096)
+    assert need == 2 * 16 * 4096 * 4
+    assert lib.attn_bwd(ctypes.byref(a), None, need, None) == 6
+    assert lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
+    assert lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4
+
