@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     AttnError,
     backward,
+    backward_workspace_size,
     combine,
     decode,
     decode_fp8,

@@ -416,6 +416,11 @@ def decode_fp8(q, k8, v8, k_scale, v_scale, kv_start, kv_len, max_kv_len: int, *
     return out, lse
 
 
+def backward_workspace_size(b: int, h_q: int, s_q: int) -> int:
+    """Bytes of device workspace backward() needs."""
+    return int(load_library().attn_bwd_workspace_size(b, h_q, s_q))
+
+
 def backward(q, k, v, o, d_o, lse, *, scale: float | None = None, causal: bool = False, dq=None, dk=None,
              dv=None, workspace=None, stream=None):
     """dQ, dK, dV of the prefill for an incoming gradient d_o, from the forward's o and lse.

@@ -46,6 +46,13 @@ __device__ __forceinline__ void load_b_rows(u32x4 (&reg)[NKK], const uint16_t *b
   for (int kk = 0; kk < NKK; ++kk) reg[kk] = *reinterpret_cast<const u32x4 *>(pr + kk * 16);
 }
 
+// Eight 16-byte LDS reads at addr + 32*I (I = 0..7) into f32x4 values.
+template <int I>
+__device__ __forceinline__ void lds_row4(f32x4 (&v)[8], uint32_t addr) {
+  v[I] = __builtin_bit_cast(f32x4, ds_read_b128<32 * I>(addr));
+  if constexpr (I + 1 < 8) lds_row4<I + 1>(v, addr);
+}
+
 // Stores a transposed accumulator (lane = row, registers = head-dim columns)
 // times f as bf16 rows.
 template <int NDB>
@@ -166,7 +173,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
   using T = Tile<D, 4, BN>;  // here the streamed "keys" of the engine are query rows
   constexpr int BK = 128;    // keys per workgroup
-  constexpr int STAGE = 4 * T::TILE_BYTES;  // [Q row][Q transpose][dO row][dO transpose]
+  // [Q row][Q transpose][dO row][dO transpose][LSE of the BN rows][D of the BN rows]
+  constexpr int STAGE = 4 * T::TILE_BYTES + 2 * BN * 4;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE / 2];
 
   const int tid = threadIdx.x;
@@ -211,6 +219,15 @@ void bwd_dkdv_kernel(BwdParams p) {
       T::dma1(ln, true, st + T::TILE_ELEMS, qbase, p.q_ss, t * BN, p.s_q, wave);
       T::dma1(ln, false, st + 2 * T::TILE_ELEMS, dobase, p.q_ss, t * BN, p.s_q, wave);
       T::dma1(ln, true, st + 3 * T::TILE_ELEMS, dobase, p.q_ss, t * BN, p.s_q, wave);
+      if (wave == 0) {  // LSE and D of the tile's rows, 4 bytes per lane; rows past s_q read as zero
+        const int r0 = t * BN, nr = max(0, min(BN, p.s_q - r0));
+        uint16_t *aux = st + 4 * T::TILE_ELEMS;
+        const uint32_t bytes = (uint32_t)(nr * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(nr > 0 ? lse_h + r0 : lse_h, bytes), (lds_void *)aux, 4,
+                                                 lane * 4, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(nr > 0 ? d_h + r0 : d_h, bytes),
+                                                 (lds_void *)(aux + 2 * BN), 4, lane * 4, 0, 0, 0);
+      }
     };
     __syncthreads();  // the previous head's last tile is consumed
     if (n_tiles > 0) load(0, t_begin);
@@ -227,21 +244,30 @@ void bwd_dkdv_kernel(BwdParams p) {
           f32x16 s[T::NKB], dp[T::NKB];
           T::scores(s, kreg, ln, so);                        // S = Q.K^T: rows in registers, keys in lanes
           T::scores(dp, vreg, ln, so + 2 * T::TILE_BYTES);   // dP = dO.V^T
+          // LSE and D of the rows this lane's registers hold (4 consecutive rows per read)
+          const uint32_t aux = base + so + 4 * T::TILE_BYTES + (4 * hi) * 4;
+          f32x4 lv[4 * T::NKB], dv4[4 * T::NKB];  // index 4rb + q4: rows 32rb + 8q4 + 4hi .. +3
+          static_assert(T::NKB == 2, "64-row tiles");
+          lds_row4<0>(lv, aux);
+          lds_row4<0>(dv4, aux + BN * 4);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
           for (int rb = 0; rb < T::NKB; ++rb)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
               // rows i0 + 32rb + 8q4 + 4hi + 0..3 hold registers 4q4..4q4+3
               const int r4 = i0 + 32 * rb + 8 * q4 + 4 * hi;
+              const f32x4 l4 = lv[4 * rb + q4];
+              const f32x4 d4 = dv4[4 * rb + q4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = r4 + e;
                 const bool vis = r < p.s_q && key_ok && (!CAUSAL || key <= r + off);
                 float pv = 0.0f, dsv = 0.0f;
                 if (vis) {
-                  const float l = lse_h[r];
+                  const float l = l4[e];
                   pv = l == kNegInf ? 0.0f : fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -l * kLog2e));
-                  dsv = pv * (dp[rb][4 * q4 + e] - d_h[r]);
+                  dsv = pv * (dp[rb][4 * q4 + e] - d4[e]);
                 }
                 s[rb][4 * q4 + e] = pv;
                 dp[rb][4 * q4 + e] = dsv;

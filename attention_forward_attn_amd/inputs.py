@@ -31,7 +31,7 @@ class Workload:
     """One synthetic workload: shapes, mask and the seed its inputs use."""
 
     name: str
-    kind: str  # "prefill" or "decode"
+    kind: str  # "prefill", "decode" or "backward"
     seed: int
     d: int
     h_q: int
@@ -87,6 +87,9 @@ WORKLOADS = {
         # the same draw held in a paged cache of 64-token pages
         _w("mqa_decode_paged_B64_hq128_d128_p64", "decode", BASE_SEED + 3, 128, 128, 1, b=64,
            len_lo=1024, len_hi=8192, page_size=64),
+        # backward of the dense causal MHA prefill (incoming dO ~ N(0,1), drawn after Q, K, V)
+        _w("bwd_mha_b2_h16_s4096_d128_causal", "backward", BASE_SEED + 1, 128, 16, 16, b=2, s_q=4096,
+           s_k=4096, causal=True),
         # family 4: large head dims, long context
         _w("long_b1_h8_s16384_d256_causal", "prefill", BASE_SEED + 4, 256, 8, 8, b=1,
            s_q=16384, s_k=16384, causal=True),
@@ -136,6 +139,8 @@ def workload_inputs(w: Workload):
     """Inputs of a named workload (see WORKLOADS)."""
     if w.kind == "prefill":
         return prefill_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed, w.sinks)
+    if w.kind == "backward":
+        return backward_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed)
     if w.fp8:
         return fp8_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed, w.sinks)
     if w.page_size:
@@ -192,4 +197,14 @@ def fp8_decode_inputs(B: int, h_q: int, h_kv: int, d: int, len_lo: int, len_hi: 
         inp[name + "8"] = codes.contiguous()
         inp[name + "_scale"] = sc
     return inp
+
+
+def backward_inputs(b: int, h_q: int, h_kv: int, s_q: int, s_k: int, d: int, seed: int):
+    """prefill_inputs plus an incoming gradient d_o (bf16 [b, h_q, s_q, d], N(0,1)) drawn after them."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    q = _randn_bf16((b, h_q, s_q, d), gen)
+    k = _randn_bf16((b, h_kv, s_k, d), gen)
+    v = _randn_bf16((b, h_kv, s_k, d), gen)
+    d_o = _randn_bf16((b, h_q, s_q, d), gen)
+    return {"q": q, "k": k, "v": v, "d_o": d_o, "sinks": None}
 

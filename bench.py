@@ -324,11 +324,52 @@ class Fp8DecodeCase(DecodeCase):
                        workspace=self.ws, out=self.out, lse=self.lse)
 
 
+class BackwardCase:
+    """dQ, dK, dV of the prefill for an incoming dO; O and LSE come from one forward outside the timing."""
+
+    def __init__(self, w, n_sets: int, dev):
+        import torch
+
+        import attention_forward_attn_amd as afa
+        from attention_forward_attn_amd.inputs import backward_inputs
+
+        self.w = w
+        base = backward_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed)
+        self.sets = [{n: base[n].to(dev) for n in ("q", "k", "v", "d_o")}]
+        gen = torch.Generator(device=dev).manual_seed(w.seed + 1)
+        for _ in range(1, n_sets):
+            self.sets.append({n: torch.randn(t.shape, generator=gen, device=dev).to(torch.bfloat16)
+                              for n, t in self.sets[0].items()})
+        for st in self.sets:
+            st["o"], st["lse"] = afa.prefill(st["q"], st["k"], st["v"], causal=w.causal)
+        self.ws = torch.empty(afa.backward_workspace_size(w.b, w.h_q, w.s_q),
+                              dtype=torch.uint8, device=dev)
+        q, k = self.sets[0]["q"], self.sets[0]["k"]
+        self.dq = torch.empty_like(q)
+        self.dk = torch.empty_like(k)
+        self.dv = torch.empty_like(k)
+        # 2.5x the forward's count: five products (S, dP, dV, dQ, dK) of 2*d flops per visible pair
+        self.flops = 10 * w.d * w.b * w.h_q * visible_pairs(w.s_q, w.s_k, w.causal, w.window)
+
+    def run(self, i: int):
+        import attention_forward_attn_amd as afa
+
+        s = self.sets[i % len(self.sets)]
+        afa.backward(s["q"], s["k"], s["v"], s["o"], s["d_o"], s["lse"], causal=self.w.causal, dq=self.dq,
+                     dk=self.dk, dv=self.dv, workspace=self.ws)
+
+
 def bench_one(name: str, steps: int, warmup: int, dev):
     """One JSON line for one named workload (prefill or decode) alone."""
     from attention_forward_attn_amd.inputs import WORKLOADS
 
     w = WORKLOADS[name]
+    if w.kind == "backward":
+        c = BackwardCase(w, 2, dev)
+        (ms,), wall = timed([c], steps, warmup)
+        r = roofline_prefill(c.flops, ms)
+        return {"workload": name, "kind": "backward", "ms": round(ms, 4), "TFLOP/s": r["achieved"],
+                "frac_of_peak": r["frac"], "gflop": round(c.flops / 1e9, 2)}
     if w.kind == "prefill":
         c = PrefillCase(w, 2, dev)
         (ms,), wall = timed([c], steps, warmup)
