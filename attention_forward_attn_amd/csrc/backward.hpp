@@ -82,7 +82,10 @@ void bwd_dq_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
   const int n_qt = (p.s_q + BM - 1) / BM;
-  const int bh = blockIdx.x / n_qt, qt = blockIdx.x - bh * n_qt;
+  // Under a causal mask later query tiles see more keys: hand them out first.
+  const int nbh = p.b * p.h_q;
+  const int lvl = blockIdx.x / nbh, bh = blockIdx.x - lvl * nbh;
+  const int qt = CAUSAL ? n_qt - 1 - lvl : lvl;
   const int bi = bh / p.h_q, h = bh - bi * p.h_q;
   const int g = h / p.ratio;
   const int q0 = qt * BM;
@@ -181,7 +184,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
   const int n_kt = (p.s_k + BK - 1) / BK;
-  const int bg = blockIdx.x / n_kt, kt = blockIdx.x - bg * n_kt;
+  // Under a causal mask earlier key blocks are seen by more rows: hand them out first.
+  const int nbg = p.b * p.h_kv;
+  const int kt = blockIdx.x / nbg, bg = blockIdx.x - kt * nbg;
   const int bi = bg / p.h_kv, g = bg - bi * p.h_kv;
   const int off = p.s_k - p.s_q;
   const int w_key0 = kt * BK + wave * 32;
