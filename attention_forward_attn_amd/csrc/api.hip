@@ -378,7 +378,7 @@ attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_b
     return fail(ATTN_ERR_SHAPE, "need b, h_q, h_kv >= 1 and s_q, s_k >= 0");
   if (a->h_q % a->h_kv != 0)
     return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
-  if (a->d != 128) return fail(ATTN_ERR_SHAPE, "backward supports d = 128 (got %d)", a->d);
+  if (a->d != 64 && a->d != 128) return fail(ATTN_ERR_SHAPE, "backward supports d = 64 or 128 (got %d)", a->d);
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1");
   if (!(std::isfinite(a->scale) && a->scale > 0.0f))
     return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
@@ -421,7 +421,7 @@ attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_b
   p.ratio = a->h_q / a->h_kv;
   p.c = a->scale * attn::kLog2e;
   p.scale = a->scale;
-  hipError_t e = attn::backward_d128(p, a->causal != 0, static_cast<hipStream_t>(stream));
+  hipError_t e = attn::backward(a->d, p, a->causal != 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
 }

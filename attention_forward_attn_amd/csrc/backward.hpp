@@ -1,4 +1,4 @@
-// Attention backward at head dim 128: dQ, dK, dV for an incoming dO, from the
+// Attention backward at head dims 64 and 128: dQ, dK, dV for an incoming dO, from the
 // forward's O and LSE (no window, no sink), deterministic (no atomics).
 //
 // Two kernels, both built from the forward's tile engine:

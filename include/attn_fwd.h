@@ -248,7 +248,7 @@ typedef struct {
  *       (k_*); lse: fp32 (bi, h, i) at lse + bi*lse_sb + h*lse_sh + i.
  * workspace: attn_bwd_workspace_size(b, h_q, s_q) bytes, 16-byte aligned,
  *       caller-owned (row sums D between the two kernels).
- * Two kernels run on `stream` (dQ and D, then dK/dV).  Supported: d = 128;
+ * Two kernels run on `stream` (dQ and D, then dK/dV).  Supported: d = 64 or 128;
  * causal (bottom-right) or not; h_q % h_kv == 0.
  */
 typedef struct {

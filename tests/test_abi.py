@@ -333,7 +333,7 @@ def good_bwd(**over):
 BWD_BAD = [
     ("null lse", dict(lse=None), 1),
     ("null dv", dict(dv=None), 1),
-    ("d=64", dict(d=64), 2),
+    ("d=256", dict(d=256), 2),
     ("ratio", dict(h_q=6, h_kv=4), 2),
     ("causal 2", dict(causal=2), 2),
     ("zero scale", dict(scale=0.0), 2),

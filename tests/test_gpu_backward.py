@@ -29,15 +29,15 @@ def grad_check(got, want, what):
     assert err <= tol, f"{what}: max-abs error {err:.3e} > {tol:.3e}"
 
 
-def run_case(b, h_q, h_kv, s_q, s_k, causal, seed):
-    inp = prefill_inputs(b, h_q, h_kv, s_q, s_k, 128, seed)
+def run_case(b, h_q, h_kv, s_q, s_k, causal, seed, d=128):
+    inp = prefill_inputs(b, h_q, h_kv, s_q, s_k, d, seed)
     gen = torch.Generator("cpu").manual_seed(seed + 99)
-    d_o = torch.randn(b, h_q, s_q, 128, generator=gen).to(torch.bfloat16)
+    d_o = torch.randn(b, h_q, s_q, d, generator=gen).to(torch.bfloat16)
     q, k, v = inp["q"].to(DEV), inp["k"].to(DEV), inp["v"].to(DEV)
     o, lse = afa.prefill(q, k, v, causal=causal)
     dq, dk, dv = afa.backward(q, k, v, o, d_o.to(DEV), lse, causal=causal)
     torch.cuda.synchronize()
-    rq, rk, rv = oracle.attention_backward_ref(inp["q"], inp["k"], inp["v"], d_o, 1 / math.sqrt(128), causal)
+    rq, rk, rv = oracle.attention_backward_ref(inp["q"], inp["k"], inp["v"], d_o, 1 / math.sqrt(d), causal)
     return (dq, dk, dv), (rq, rk, rv)
 
 
@@ -53,11 +53,12 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
-def test_backward_small(case):
-    print(f"backward case {case}", flush=True)
-    got, want = run_case(*case, seed=51)
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_small(case, d):
+    print(f"backward case {case} d={d}", flush=True)
+    got, want = run_case(*case, seed=51, d=d)
     for name, g, w in zip(("dQ", "dK", "dV"), got, want):
-        grad_check(g, w, f"{case} {name}")
+        grad_check(g, w, f"{case} d={d} {name}")
 
 
 def test_backward_long_heads():
