@@ -189,29 +189,41 @@ def timed(cases, steps: int, warmup: int):
     return per, wall_ms
 
 
-def kernel_source_hash() -> str:
-    """Short hash of the HIP sources; a recorded counter profile is valid only for this hash."""
+def kernel_source_hash(unit: str) -> str:
+    """Short hash of one HIP translation unit and every source it includes.
+
+    A recorded counter profile is valid only for the hash of the unit that
+    holds its kernel: a change anywhere in that unit's include closure voids it.
+    """
     import hashlib
+    import re
 
     d = os.path.join(ROOT, "attention_forward_attn_amd", "csrc")
+    seen, todo = set(), [unit]
+    while todo:
+        f = todo.pop()
+        if f in seen:
+            continue
+        seen.add(f)
+        with open(os.path.join(d, f)) as fh:
+            todo += [m for m in re.findall(r'^#include "([^"/]+)"', fh.read(), re.M)]
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hpp", ".hip")):
-            h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+    for f in sorted(seen):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic(*profiles: str):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from committed profile summaries.
 
-    Each summary ends with a `traffic_record:` line naming the kernel-source hash
-    it was measured on; if any summary is missing or was taken on other
-    sources, the traffic is unknown (None).
+    Each summary ends with a `traffic_record:` line naming the translation unit
+    of its kernel and that unit's source hash when it was measured; if any
+    summary is missing or was taken on other sources, the traffic is unknown
+    (None).
     """
     total = 0
-    want = kernel_source_hash()
     for name in profiles:
         path = os.path.join(ROOT, "profiles", name)
         if not os.path.exists(path):
@@ -221,7 +233,7 @@ def recorded_traffic(*profiles: str):
             for line in fh:
                 if line.startswith("traffic_record:"):
                     rec = dict(kv.split("=", 1) for kv in line.split()[1:])
-        if rec is None or rec.get("kernel_src_sha") != want:
+        if rec is None or "src" not in rec or rec.get("kernel_src_sha") != kernel_source_hash(rec["src"]):
             return None
         total += int(float(rec["fetch_bytes"])) + int(float(rec["write_bytes"]))
     return total
