@@ -136,6 +136,11 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     lib.attn_fwd_prefill.argtypes = [ctypes.POINTER(PrefillArgs), ctypes.c_void_p]
     lib.attn_fwd_prefill.restype = ctypes.c_int
+    lib.attn_fwd_prefill_chunked.argtypes = [ctypes.POINTER(PrefillArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.c_void_p]
+    lib.attn_fwd_prefill_chunked.restype = ctypes.c_int
+    lib.attn_fwd_prefill_chunked_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
+    lib.attn_fwd_prefill_chunked_workspace_size.restype = ctypes.c_size_t
     lib.attn_fwd_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_void_p]
     lib.attn_fwd_decode.restype = ctypes.c_int
@@ -218,13 +223,20 @@ def prefill_args(q, k, v, out, lse, sinks, scale, causal, window) -> PrefillArgs
 
 
 def prefill(q, k, v, *, scale: float | None = None, causal: bool = False, window: int = 0,
-            sinks=None, out=None, lse=None, return_lse: bool = True, stream=None):
+            sinks=None, out=None, lse=None, return_lse: bool = True, chunked: bool = True,
+            workspace=None, stream=None):
     """Fused attention forward over [b, h, s, d]-indexed bf16 device tensors.
 
     q is [b, h_q, s_q, d]; k and v are [b, h_kv, s_k, d] (any strides with a
     unit head-dim stride, e.g. a transposed [b, s, h, d] view).  Returns
     (O, LSE): O bf16 shaped like q, LSE fp32 [b, h_q, s_q] (None when
     ``return_lse`` is False and no ``lse`` buffer is given).
+
+    With ``chunked`` (the default) the call goes through
+    attn_fwd_prefill_chunked, which cuts long causal key ranges into chunks
+    when the library's plan says so (d = 512); ``workspace`` (uint8 device
+    tensor) is then used if given, else allocated.  ``chunked=False`` always
+    runs the single-pass attn_fwd_prefill.
     """
     import torch
 
@@ -246,8 +258,16 @@ def prefill(q, k, v, *, scale: float | None = None, causal: bool = False, window
     if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
         raise ValueError("sinks must be a contiguous float32 device tensor")
     a = prefill_args(q, k, v, out, lse, sinks, scale, causal, window)
-    _check(lib.attn_fwd_prefill(ctypes.byref(a), _stream(stream)))
+    need = int(lib.attn_fwd_prefill_chunked_workspace_size(ctypes.byref(a))) if chunked else 0
+    if need == 0:
+        _check(lib.attn_fwd_prefill(ctypes.byref(a), _stream(stream)))
+        return out, lse
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.attn_fwd_prefill_chunked(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
+
 
 
 def decode_workspace_size(B: int, h_q: int, d: int, max_kv_len: int, split_size: int = 512) -> int:

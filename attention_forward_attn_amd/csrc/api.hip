@@ -3,8 +3,10 @@
 // HIP call, so a rejected call has no side effect.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -134,7 +136,73 @@ const char *attn_status_str(attn_status s) {
 
 const char *attn_last_error(void) { return g_err; }
 
-attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
+namespace {
+
+// Plan of the chunked causal prefill (d = 512; see attn_fwd_prefill_chunked).
+// The key range of each query tile is cut into chunks of `chunk_tiles` key
+// tiles, with the chunk length set so that one chunk is about one compute
+// unit's share of the whole causal work (256 CUs), but no shorter than
+// kMinChunkTiles; the (query tile, chunk) pairs are launched longest first.
+constexpr int kChunkTargetCUs = 256;
+constexpr int kMinChunkTiles = 8;
+
+struct ChunkPlan {
+  int chunk_tiles = 0, qt0 = 0, max_chunks = 0, n_rank = 0;
+  uint32_t rank[attn::kMaxChunkRanks];
+  int64_t o_bytes = 0, lse_bytes = 0;  // partial buffers; o_bytes is a multiple of 256
+};
+
+// Fills pl and returns true when the call would be chunked; false leaves the
+// single-pass kernel in charge.  Arguments must already be valid.
+bool plan_chunks(const attn_prefill_args *a, ChunkPlan &pl) {
+  if (a->d != 512 || !a->causal || a->window > 0 || a->s_q == 0 || a->s_k == 0) return false;
+  const int bm = attn::prefill_block_rows(512, attn::kMaskCausal);
+  const int bn = attn::prefill_block_keys(512, attn::kMaskCausal);
+  const int64_t nq = (a->s_q + bm - 1) / bm;
+  const int64_t off = (int64_t)a->s_k - a->s_q;
+  const int64_t bh = (int64_t)a->b * a->h_q;
+  std::vector<int64_t> T(nq);
+  int64_t total = 0, tmax = 0;
+  for (int64_t qt = 0; qt < nq; ++qt) {
+    const int64_t i_last = std::min<int64_t>(a->s_q, (qt + 1) * bm) - 1;
+    const int64_t kend = std::max<int64_t>(0, std::min<int64_t>(a->s_k, i_last + off + 1));
+    T[qt] = (kend + bn - 1) / bn;
+    total += T[qt];
+    tmax = std::max(tmax, T[qt]);
+  }
+  total *= bh;
+  const int64_t c = std::max<int64_t>(kMinChunkTiles, (total + kChunkTargetCUs - 1) / kChunkTargetCUs);
+  if (c >= tmax) return false;  // enough query tiles already: nothing to balance
+  struct E { int64_t len, qt, ch; };
+  std::vector<E> es;
+  for (int64_t qt = 0; qt < nq; ++qt) {
+    const int64_t n = T[qt] > 0 ? (T[qt] + c - 1) / c : 1;
+    if (n > 255) return false;
+    for (int64_t ch = 0; ch < n; ++ch) es.push_back({T[qt] > 0 ? std::min(c, T[qt] - ch * c) : 0, qt, ch});
+  }
+  if ((int64_t)es.size() > attn::kMaxChunkRanks || (int64_t)es.size() * bh > kMaxIndex || nq >= (1 << 23))
+    return false;
+  std::stable_sort(es.begin(), es.end(), [](const E &x, const E &y) {
+    return x.len != y.len ? x.len > y.len : x.qt > y.qt;
+  });
+  pl.chunk_tiles = (int)c;
+  pl.n_rank = (int)es.size();
+  for (int i = 0; i < pl.n_rank; ++i) pl.rank[i] = (uint32_t)(es[i].qt << 8) | (uint32_t)es[i].ch;
+  int64_t qt0 = nq;
+  while (qt0 > 0 && T[qt0 - 1] > c) --qt0;  // T is non-decreasing in qt
+  pl.qt0 = (int)qt0;
+  pl.max_chunks = (int)((tmax + c - 1) / c);
+  const int64_t rows = bh * (nq - qt0) * pl.max_chunks * bm;
+  pl.o_bytes = (rows * a->d * 2 + 255) / 256 * 256;
+  pl.lse_bytes = rows * 4;
+  return true;
+}
+
+// Validation and parameter block of a prefill call; on success *done is set
+// when there is nothing to launch (s_q == 0).
+attn_status prepare_prefill(const attn_prefill_args *a, attn::PrefillParams &p, int &mask, int64_t &n_units,
+                            bool &done) {
+  done = false;
   if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
   if (a->b < 1 || a->h_q < 1 || a->h_kv < 1 || a->s_q < 0 || a->s_k < 0)
     return fail(ATTN_ERR_SHAPE, "need b, h_q, h_kv >= 1 and s_q, s_k >= 0 (got b=%d h_q=%d h_kv=%d s_q=%d s_k=%d)",
@@ -148,7 +216,10 @@ attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1");
   if (a->window < 0) return fail(ATTN_ERR_SHAPE, "window must be >= 0");
   if (a->window > 0 && !a->causal) return fail(ATTN_ERR_SHAPE, "a window requires causal = 1");
-  if (a->s_q == 0) return ok();
+  if (a->s_q == 0) {
+    done = true;
+    return ok();
+  }
   if (!a->q || !a->o || (a->s_k > 0 && (!a->k || !a->v)))
     return fail(ATTN_ERR_NULL, "q, o (and k, v when s_k > 0) must be non-NULL");
   if (!aligned16(a->q) || !aligned16(a->o) || (a->s_k > 0 && (!aligned16(a->k) || !aligned16(a->v))))
@@ -170,13 +241,12 @@ attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
       omax > (int64_t(1) << 40))
     return fail(ATTN_ERR_SHAPE, "tensor extent exceeds 2^40 elements");
 
-  const int mask = a->window > 0 ? attn::kMaskCausalWindow : (a->causal ? attn::kMaskCausal : attn::kMaskNone);
+  mask = a->window > 0 ? attn::kMaskCausalWindow : (a->causal ? attn::kMaskCausal : attn::kMaskNone);
   const int bm = attn::prefill_block_rows(a->d, mask);
   const int64_t n_qtiles = (a->s_q + bm - 1) / bm;
-  const int64_t n_units = n_qtiles * a->b * a->h_q;
+  n_units = n_qtiles * a->b * a->h_q;
   if (n_units > kMaxIndex) return fail(ATTN_ERR_SHAPE, "too many work units (%lld)", (long long)n_units);
 
-  attn::PrefillParams p;
   p.q = static_cast<const uint16_t *>(a->q);
   p.k = static_cast<const uint16_t *>(a->k);
   p.v = static_cast<const uint16_t *>(a->v);
@@ -193,7 +263,11 @@ attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
   p.window = a->window;
   p.n_qtiles = (int32_t)n_qtiles;
   p.c = a->scale * attn::kLog2e;
+  return ok();
+}
 
+attn_status launch_prefill(const attn_prefill_args *a, const attn::PrefillParams &p, int mask, int64_t n_units,
+                           void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (a->d) {
@@ -203,6 +277,59 @@ attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
     default: e = attn::prefill_d512(p, mask, (int)n_units, s); break;
   }
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+}  // namespace
+
+attn_status attn_fwd_prefill(const attn_prefill_args *a, void *stream) {
+  attn::PrefillParams p;
+  int mask;
+  int64_t n_units;
+  bool done;
+  attn_status st = prepare_prefill(a, p, mask, n_units, done);
+  if (st != ATTN_OK || done) return st;
+  return launch_prefill(a, p, mask, n_units, stream);
+}
+
+size_t attn_fwd_prefill_chunked_workspace_size(const attn_prefill_args *a) {
+  attn::PrefillParams p;
+  int mask;
+  int64_t n_units;
+  bool done;
+  if (prepare_prefill(a, p, mask, n_units, done) != ATTN_OK || done) return 0;
+  static thread_local ChunkPlan pl;
+  if (!plan_chunks(a, pl)) return 0;
+  return (size_t)(pl.o_bytes + pl.lse_bytes);
+}
+
+attn_status attn_fwd_prefill_chunked(const attn_prefill_args *a, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+  attn::PrefillParams p;
+  int mask;
+  int64_t n_units;
+  bool done;
+  attn_status st = prepare_prefill(a, p, mask, n_units, done);
+  if (st != ATTN_OK || done) return st;
+  static thread_local ChunkPlan pl;
+  if (!plan_chunks(a, pl)) return launch_prefill(a, p, mask, n_units, stream);
+  const size_t need = (size_t)(pl.o_bytes + pl.lse_bytes);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "chunked prefill needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
+                workspace == nullptr ? ", NULL" : "");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  attn::PrefillChunks ck;
+  ck.o_part = static_cast<uint16_t *>(workspace);
+  ck.lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.o_bytes);
+  ck.chunk_tiles = pl.chunk_tiles;
+  ck.qt0 = pl.qt0;
+  ck.max_chunks = pl.max_chunks;
+  ck.n_rank = pl.n_rank;
+  std::memcpy(ck.rank, pl.rank, sizeof(uint32_t) * pl.n_rank);
+  std::memset(ck.rank + pl.n_rank, 0, sizeof(uint32_t) * (attn::kMaxChunkRanks - pl.n_rank));
+  hipError_t e = attn::prefill_d512_chunked(p, ck, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "chunked prefill launch");
   return ok();
 }
 
@@ -479,6 +606,16 @@ int prefill_block_rows(int d, int mask) {
     case 128: return mask == kMaskCausalWindow ? 128 : 256;
     case 256: return 256;
     case 512: return 64;
+    default: return 0;
+  }
+}
+
+int prefill_block_keys(int d, int mask) {
+  (void)mask;
+  switch (d) {
+    case 64: case 128: return 64;
+    case 256: return 32;
+    case 512: return 32;
     default: return 0;
   }
 }

@@ -36,6 +36,21 @@ struct PrefillParams {
   float c;           // scale * log2(e): logits in base-2 units
 };
 
+// Chunked causal prefill: the (query tile, key chunk) pairs in launch order and
+// the partial buffers of the query tiles that have more than one chunk
+// (qt >= qt0): partial (bh, qt, c) is slot (bh*(n_qtiles-qt0) + qt-qt0)*max_chunks + c,
+// holding BM rows of d bf16 values in o_part and BM fp32 LSEs in lse_part.
+constexpr int kMaxChunkRanks = 384;
+struct PrefillChunks {
+  uint16_t *o_part;
+  float *lse_part;
+  int32_t chunk_tiles;  // key tiles per chunk
+  int32_t qt0;          // first query tile with more than one chunk
+  int32_t max_chunks;   // chunks of the longest query tile
+  int32_t n_rank;       // entries of rank[] in use
+  uint32_t rank[kMaxChunkRanks];  // (qt << 8) | chunk, longest first
+};
+
 // Device-side parameters of the backward kernels.  q, o, d_o and dq share one
 // [b, h_q, s_q, d] layout (q strides); k, v, dk and dv share one [b, h_kv,
 // s_k, d] layout (k strides); dsum is fp32 [b, h_q, s_q] scratch.

@@ -15,6 +15,10 @@ hipError_t prefill_d64(const PrefillParams &p, int mask, int n_units, hipStream_
 hipError_t prefill_d128(const PrefillParams &p, int mask, int n_units, hipStream_t s);
 hipError_t prefill_d256(const PrefillParams &p, int mask, int n_units, hipStream_t s);
 hipError_t prefill_d512(const PrefillParams &p, int mask, int n_units, hipStream_t s);
+// Key tiles per step of the prefill kernel for head dim d and mask kind.
+int prefill_block_keys(int d, int mask);
+// Causal d = 512 prefill with chunked key ranges (ck filled by the host) and the merge of the partials.
+hipError_t prefill_d512_chunked(const PrefillParams &p, const PrefillChunks &ck, hipStream_t s);
 
 // Query heads per decode workgroup (0 if unsupported).
 int decode_block_rows(int d);

@@ -18,6 +18,7 @@
 //
 #pragma once
 
+#include "combine.hpp"
 #include "tile.hpp"
 
 namespace attn {
@@ -68,9 +69,20 @@ __device__ __forceinline__ void prefill_unit(const PrefillParams &p, int v, int 
   }
 }
 
-template <int D, int NW, int BN, bool CAUSAL, bool WINDOW, int OCC, int DS = D>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-void prefill_kernel(PrefillParams p) {
+// One key chunk of a query tile whose key range is split (KSPLIT): the tile's
+// visible key tiles [t_begin, t_end) are cut into chunks of `tiles` key tiles;
+// chunk `index` is processed, and when the tile has more than one chunk the
+// normalised partial O (bf16) and its natural-log LSE go to slot `part` of the
+// partial buffers, to be merged by prefill_merge_kernel.
+struct KeyChunk {
+  int index, tiles;
+  int64_t part;
+  uint16_t *o_part;
+  float *lse_part;
+};
+
+template <int D, int NW, int BN, bool CAUSAL, bool WINDOW, int DS, bool KSPLIT>
+__device__ __forceinline__ void prefill_body(const PrefillParams &p, int bh, int qt, const KeyChunk &kc) {
   using T = Tile<D, NW, BN, DS>;
   constexpr int BM = T::BM;
   constexpr int SPLIT = T::SPLIT;
@@ -83,8 +95,6 @@ void prefill_kernel(PrefillParams p) {
   const int w = wave / SPLIT;      // row block of this wave
   const int slice = wave % SPLIT;  // head-dim slice of this wave
 
-  int bh, qt;
-  prefill_unit<CAUSAL && !WINDOW>(p, blockIdx.x, bh, qt);
   const int bi = bh / p.h_q, h = bh - bi * p.h_q;
   const int g = h / p.ratio;
   const int q0 = qt * BM;
@@ -96,8 +106,15 @@ void prefill_kernel(PrefillParams p) {
   if (CAUSAL) kend = max(0, min(kend, i_last + off + 1));
   int kbeg = 0;
   if (WINDOW) kbeg = max(0, q0 + off - p.window + 1);
-  const int t_begin = kbeg / BN;
-  const int t_end = kbeg < kend ? (kend + BN - 1) / BN : t_begin;
+  int t_begin = kbeg / BN;
+  int t_end = kbeg < kend ? (kend + BN - 1) / BN : t_begin;
+  bool partial = false;  // this chunk is one of several: write a partial result
+  if constexpr (KSPLIT) {
+    const int nt = t_end - t_begin;
+    partial = nt > kc.tiles;
+    t_begin += kc.index * kc.tiles;
+    t_end = min(t_end, t_begin + kc.tiles);
+  }
 
   // This wave's rows.
   const int w_lo = q0 + w * 32;
@@ -117,7 +134,7 @@ void prefill_kernel(PrefillParams p) {
   }
 
   float m = kNegInf, l = 0.0f;
-  if (p.sinks != nullptr) {
+  if (p.sinks != nullptr && (!KSPLIT || kc.index == 0)) {  // the sink joins one chunk only
     m = p.sinks[h] * kLog2e;
     l = hi == 0 ? 1.0f : 0.0f;
   }
@@ -231,9 +248,25 @@ void prefill_kernel(PrefillParams p) {
   }
 
   // Epilogue: O / l once, bf16 round-to-nearest-even; LSE = ln2 * (m + log2 l).
+  // A partial chunk writes the same two quantities into its slot instead.
   const float lt = sum_across_halves(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (row_ok) {
+  if (KSPLIT && partial) {
+    if (row_ok) {
+      const int64_t prow = kc.part * BM + (row - q0);
+      uint16_t *op = kc.o_part + prow * D + slice * DS + 4 * hi;
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          u32x2 val;
+          val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
+          val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
+          *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
+        }
+      if (hi == 0 && slice == 0) kc.lse_part[prow] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+    }
+  } else if (row_ok) {
     uint16_t *op = p.o + bi * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss + slice * DS + 4 * hi;
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db)
@@ -247,6 +280,63 @@ void prefill_kernel(PrefillParams p) {
     if (p.lse != nullptr && hi == 0 && slice == 0)
       p.lse[bi * p.lse_sb + h * p.lse_sh + row] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   }
+}
+
+template <int D, int NW, int BN, bool CAUSAL, bool WINDOW, int OCC, int DS = D>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void prefill_kernel(PrefillParams p) {
+  int bh, qt;
+  prefill_unit<CAUSAL && !WINDOW>(p, blockIdx.x, bh, qt);
+  prefill_body<D, NW, BN, CAUSAL, WINDOW, DS, false>(p, bh, qt, KeyChunk{});
+}
+
+// Causal prefill with the key ranges of long query tiles cut into chunks, so
+// that the work units are of similar length when there are too few query
+// tiles to keep the chip busy (the d = 512 shapes: 64-row tiles, one
+// workgroup per CU).  Unit v is (rank v / (b*h_q), head v % (b*h_q)); the rank
+// table, built on the host, lists the (query tile, chunk) pairs longest first.
+template <int D, int NW, int BN, int OCC, int DS = D>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void prefill_chunked_kernel(PrefillParams p, PrefillChunks ck) {
+  const int BH = p.b * p.h_q;
+  const int rank = blockIdx.x / BH, bh = blockIdx.x - rank * BH;
+  const uint32_t e = ck.rank[rank];
+  const int qt = (int)(e >> 8), c = (int)(e & 255u);
+  KeyChunk kc;
+  kc.index = c;
+  kc.tiles = ck.chunk_tiles;
+  kc.part = qt >= ck.qt0 ? ((int64_t)bh * (p.n_qtiles - ck.qt0) + (qt - ck.qt0)) * ck.max_chunks + c : 0;
+  kc.o_part = ck.o_part;
+  kc.lse_part = ck.lse_part;
+  prefill_body<D, NW, BN, true, false, DS, true>(p, bh, qt, kc);
+}
+
+// LSE merge of the chunk partials of the split query tiles (qt >= qt0): one
+// thread per row and 8 output columns, parts merged as in the decode combine.
+template <int D, int BM, int BN>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p, PrefillChunks ck) {
+  constexpr int CPR = D / 8;
+  const int nsq = p.n_qtiles - ck.qt0;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)p.b * p.h_q * nsq * BM * CPR) return;
+  const int ch = (int)(gid % CPR);
+  const int64_t rr = gid / CPR;
+  const int r = (int)(rr % BM);
+  const int64_t tq = rr / BM;  // bh * nsq + (qt - qt0)
+  const int qt = ck.qt0 + (int)(tq % nsq);
+  const int bh = (int)(tq / nsq);
+  const int row = qt * BM + r;
+  if (row >= p.s_q) return;
+  // Chunks of this query tile (the kernel's own visible-range arithmetic).
+  const int i_last = min(p.s_q, qt * BM + BM) - 1;
+  const int kend = max(0, min(p.s_k, i_last + (p.s_k - p.s_q) + 1));
+  const int nt = (kend + BN - 1) / BN;
+  const int n = (nt + ck.chunk_tiles - 1) / ck.chunk_tiles;
+  const int bi = bh / p.h_q, h = bh - bi * p.h_q;
+  const int64_t part0 = tq * ck.max_chunks;
+  merge_chunk<uint16_t, 16>(ck.lse_part + part0 * BM + r, BM, ck.o_part + (part0 * BM + r) * D + ch * 8,
+                            (int64_t)BM * D, n, p.o + bi * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss + ch * 8,
+                            p.lse != nullptr && ch == 0 ? p.lse + bi * p.lse_sb + h * p.lse_sh + row : nullptr);
 }
 
 // Ping-pong prefill (SPLIT == 1 head dims): 8 waves in two groups of 4 that
@@ -457,6 +547,22 @@ template <int D, int NW, int BN, bool CAUSAL, bool WINDOW, int OCC, int DS = D>
 hipError_t launch_prefill(const PrefillParams &p, int n_units, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_kernel<D, NW, BN, CAUSAL, WINDOW, OCC, DS>), dim3(n_units), dim3(NW * 64),
                      0, stream, p);
+  return hipGetLastError();
+}
+
+// Host-side launcher of the chunked causal prefill and its merge.
+template <int D, int NW, int BN, int OCC, int DS = D>
+hipError_t launch_prefill_chunked(const PrefillParams &p, const PrefillChunks &ck, hipStream_t stream) {
+  using T = Tile<D, NW, BN, DS>;
+  const int64_t units = (int64_t)ck.n_rank * p.b * p.h_q;
+  hipLaunchKernelGGL((prefill_chunked_kernel<D, NW, BN, OCC, DS>), dim3((unsigned)units), dim3(NW * 64), 0,
+                     stream, p, ck);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = (int64_t)p.b * p.h_q * (p.n_qtiles - ck.qt0) * T::BM * (D / 8);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_merge_kernel<D, T::BM, BN>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, p, ck);
   return hipGetLastError();
 }
 

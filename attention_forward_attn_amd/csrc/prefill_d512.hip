@@ -12,4 +12,8 @@ hipError_t prefill_d512(const PrefillParams &p, int mask, int n_units, hipStream
   }
 }
 
+hipError_t prefill_d512_chunked(const PrefillParams &p, const PrefillChunks &ck, hipStream_t s) {
+  return launch_prefill_chunked<512, 4, 32, 1, 256>(p, ck, s);
+}
+
 }  // namespace attn

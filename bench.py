@@ -76,13 +76,24 @@ class PrefillCase:
         self.out = torch.empty((w.b, w.h_q, w.s_q, w.d), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((w.b, w.h_q, w.s_q), dtype=torch.float32, device=dev)
         self.flops = prefill_flops(w)
+        # workspace of the chunked schedule (d = 512 causal), allocated once outside the timed loop
+        import ctypes
+
+        import attention_forward_attn_amd as afa
+
+        s0 = self.sets[0]
+        a = afa._binding.prefill_args(s0["q"], s0["k"], s0["v"], self.out, self.lse, s0["sinks"], self.scale,
+                                      w.causal, w.window)
+        need = int(afa.load_library().attn_fwd_prefill_chunked_workspace_size(ctypes.byref(a)))
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
 
     def run(self, i: int):
         import attention_forward_attn_amd as afa
 
         s = self.sets[i % len(self.sets)]
         afa.prefill(s["q"], s["k"], s["v"], scale=self.scale, causal=self.w.causal,
-                    window=self.w.window, sinks=s["sinks"], out=self.out, lse=self.lse)
+                    window=self.w.window, sinks=s["sinks"], out=self.out, lse=self.lse,
+                    workspace=self.workspace)
 
 
 class DecodeCase:

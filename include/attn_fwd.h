@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 4
+#define ATTN_FWD_ABI_VERSION 5
 
 typedef enum {
   ATTN_OK = 0,
@@ -56,7 +56,7 @@ typedef enum {
   ATTN_ERR_STRIDE = 3,      /* a stride is negative or not a multiple of 8 elements */
   ATTN_ERR_ALIGN = 4,       /* a base pointer is misaligned */
   ATTN_ERR_UNSUPPORTED = 5, /* a valid request this build has no kernel for */
-  ATTN_ERR_WORKSPACE = 6,   /* decode workspace missing or too small */
+  ATTN_ERR_WORKSPACE = 6,   /* workspace missing or too small */
   ATTN_ERR_HIP = 7          /* the HIP runtime rejected a launch */
 } attn_status;
 
@@ -301,6 +301,35 @@ size_t attn_fwd_decode_workspace_size(int32_t B, int32_t h_q, int32_t d, int32_t
                                       int32_t split_size);
 
 attn_status attn_fwd_prefill(const attn_prefill_args *args, void *stream);
+
+/*
+ * Chunked causal prefill: the same operation and arguments as
+ * attn_fwd_prefill, scheduled for shapes with too few query tiles to fill the
+ * chip evenly under a causal mask (head dim 512, the STAGE_D.md page's hd=512
+ * case: 64-row tiles, one workgroup per compute unit).  The visible key range
+ * of each long query tile is cut into chunks of about one compute unit's share
+ * of the total work; each chunk runs as its own work unit, longest first, and
+ * writes its normalised partial output (rounded to bf16) and fp32 LSE into the
+ * workspace; a second kernel merges the chunks of each row by their LSEs (the
+ * per-segment merge of the same page's "O rescale (kt>0)" workaround).  A sink
+ * enters the first chunk only.  Results equal attn_fwd_prefill's up to rounding
+ * (the partials pass through bf16), not bit for bit.
+ *
+ * attn_fwd_prefill_chunked_workspace_size returns the bytes of workspace a
+ * call with these arguments needs, or 0 when the call would not be chunked
+ * (any head dim other than 512, no causal mask, a window, or enough query
+ * tiles already) or the arguments are invalid; with 0, workspace may be NULL
+ * and the call runs exactly attn_fwd_prefill.  Otherwise the workspace must be
+ * at least that large and 256-byte aligned (ATTN_ERR_WORKSPACE /
+ * ATTN_ERR_ALIGN), is owned by the caller, must stay allocated until the
+ * stream has run both kernels, and must not be shared by calls that may
+ * overlap.  The returned size depends on every field that shapes the work (b,
+ * h_q, s_q, s_k, d, causal, window), so query it with the same arguments.
+ */
+size_t attn_fwd_prefill_chunked_workspace_size(const attn_prefill_args *args);
+attn_status attn_fwd_prefill_chunked(const attn_prefill_args *args, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
 attn_status attn_fwd_decode(const attn_decode_args *args, void *workspace, size_t workspace_bytes,
                             void *stream);
 attn_status attn_fwd_decode_paged(const attn_decode_paged_args *args, void *workspace,

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("attn_fwd_prefill", "attn_fwd_decode", "attn_fwd_decode_paged", "attn_fwd_decode_fp8",
+    for want in ("attn_fwd_prefill", "attn_fwd_prefill_chunked", "attn_fwd_prefill_chunked_workspace_size",
+                 "attn_fwd_decode", "attn_fwd_decode_paged", "attn_fwd_decode_fp8",
                  "attn_combine", "attn_bwd", "attn_bwd_workspace_size",
                  "attn_fwd_decode_workspace_size", "attn_status_str", "attn_last_error",
                  "attn_abi_version"):
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     lib = afa.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
 
 
 def test_status_strings():
@@ -101,6 +102,57 @@ def test_prefill_rejects(name, over, code):
     st = lib.attn_fwd_prefill(ctypes.byref(a), None)
     assert st == code, (st, lib.attn_last_error())
     assert lib.attn_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("name,over,code", PREFILL_BAD, ids=[c[0] for c in PREFILL_BAD])
+def test_prefill_chunked_rejects(name, over, code):
+    lib = afa.load_library()
+    a = good_prefill(**over)
+    st = lib.attn_fwd_prefill_chunked(ctypes.byref(a), None, 0, None)
+    assert st == code, (st, lib.attn_last_error())
+    assert lib.attn_fwd_prefill_chunked_workspace_size(ctypes.byref(a)) == 0
+
+
+def wide_prefill(**over):
+    """b=1, h=4, s=4096, d=512 causal, BHSD-contiguous strides."""
+    s, d = over.pop("s", 4096), 512
+    h = over.get("h_q", 4)
+    base = dict(b=1, h_q=h, h_kv=h, s_q=s, s_k=s, d=d, causal=1,
+                q_sb=h * s * d, q_sh=s * d, q_ss=d, k_sb=h * s * d, k_sh=s * d, k_ss=d,
+                v_sb=h * s * d, v_sh=s * d, v_ss=d, o_sb=h * s * d, o_sh=s * d, o_ss=d)
+    base.update(over)
+    return good_prefill(**base)
+
+
+def test_prefill_chunked_plan_sizes():
+    lib = afa.load_library()
+    size = lambda a: lib.attn_fwd_prefill_chunked_workspace_size(ctypes.byref(a))
+    # 64 query tiles of 64 rows; tile qt sees 2(qt+1) key tiles of 32; the work
+    # of the 4 heads is 4 * 4160 tiles, 65 per CU, so chunks are 65 tiles long:
+    # tiles 32..63 get 2 chunks each (parts: 4 heads x 32 tiles x 2 chunks x 64 rows).
+    rows = 4 * 32 * 2 * 64
+    assert size(wide_prefill()) == rows * 512 * 2 + rows * 4
+    # nothing to balance, or not a chunked shape: 0
+    assert size(wide_prefill(causal=0)) == 0
+    assert size(wide_prefill(window=1024)) == 0
+    assert size(wide_prefill(h_q=64)) == 0   # 4096 query tiles: enough units already
+    assert size(wide_prefill(s=0)) == 0
+    a = good_prefill(causal=1, s_q=4096, s_k=4096, q_ss=128, k_ss=128, v_ss=128, o_ss=128,
+                     q_sh=4096 * 128, k_sh=4096 * 128, v_sh=4096 * 128, o_sh=4096 * 128,
+                     q_sb=2 * 4096 * 128, k_sb=4096 * 128, v_sb=4096 * 128, o_sb=2 * 4096 * 128)
+    assert size(a) == 0                      # head dim 128 runs the single-pass kernel
+
+
+def test_prefill_chunked_workspace_checks():
+    lib = afa.load_library()
+    a = wide_prefill()
+    need = lib.attn_fwd_prefill_chunked_workspace_size(ctypes.byref(a))
+    assert need > 0
+    assert lib.attn_fwd_prefill_chunked(ctypes.byref(a), None, need, None) == 6
+    assert lib.attn_fwd_prefill_chunked(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
+    assert lib.attn_fwd_prefill_chunked(ctypes.byref(a), ctypes.c_void_p(FAKE + 16), need, None) == 4
+    e = wide_prefill(s=0)
+    assert lib.attn_fwd_prefill_chunked(ctypes.byref(e), None, 0, None) == 0
 
 
 def test_prefill_null_args():

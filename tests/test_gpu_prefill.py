@@ -23,7 +23,7 @@ DEV = "cuda"
 
 
 def run_case(b, h_q, h_kv, s_q, s_k, d, causal=False, window=0, sink=False, seed=7, scale=None,
-             layout="bhsd", q_mul=1.0):
+             layout="bhsd", q_mul=1.0, chunked=True):
     inp = prefill_inputs(b, h_q, h_kv, s_q, s_k, d, seed, with_sinks=sink)
     q, k, v, sinks = inp["q"], inp["k"], inp["v"], inp["sinks"]
     if q_mul != 1.0:
@@ -38,7 +38,8 @@ def run_case(b, h_q, h_kv, s_q, s_k, d, causal=False, window=0, sink=False, seed
     sd = sinks.to(DEV) if sinks is not None else None
     out = torch.full((b, h_q, s_q, d), float("nan"), dtype=torch.bfloat16, device=DEV)
     lse = torch.full((b, h_q, s_q), float("nan"), dtype=torch.float32, device=DEV)
-    afa.prefill(qd, kd, vd, scale=scale, causal=causal, window=window, sinks=sd, out=out, lse=lse)
+    afa.prefill(qd, kd, vd, scale=scale, causal=causal, window=window, sinks=sd, out=out, lse=lse,
+                chunked=chunked)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.attention_ref(q, k, v, scale, causal=causal, window=window, sinks=sinks)
     return out, lse, o_ref, l_ref
@@ -72,6 +73,35 @@ def test_prefill_small(case):
     print(f"prefill case {case}", flush=True)
     out, lse, o_ref, l_ref = run_case(b, h_q, h_kv, s_q, s_k, d, causal, window, sink)
     check(out, lse, o_ref, l_ref, str(case))
+
+
+def chunked_workspace(b, h_q, h_kv, s_q, s_k, d, causal, window=0):
+    """Workspace bytes the library's chunk plan asks for (0: single pass)."""
+    q = torch.empty((b, h_q, s_q, d), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty((b, h_kv, s_k, d), dtype=torch.bfloat16, device=DEV)
+    a = afa._binding.prefill_args(q, k, k, q, None, None, 1.0 / math.sqrt(d), causal, window)
+    return int(afa.load_library().attn_fwd_prefill_chunked_workspace_size(afa._binding.ctypes.byref(a)))
+
+
+# d = 512 causal shapes whose key ranges the library cuts into chunks
+CHUNKED = [
+    # b, h_q, h_kv, s_q, s_k, sink
+    (1, 1, 1, 1024, 1024, False),  # tiles of 32 keys, chunks of 8 tiles: up to 4 chunks per query tile
+    (1, 2, 1, 1000, 1100, True),   # GQA, s_k > s_q, ragged tail, sink in the first chunk only
+    (1, 2, 2, 700, 500, False),    # s_q > s_k: leading rows see no key, later chunks partly empty
+    (2, 2, 2, 640, 640, True),
+]
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=[str(c) for c in CHUNKED])
+def test_prefill_chunked(case):
+    b, h_q, h_kv, s_q, s_k, sink = case
+    print(f"chunked prefill case {case}", flush=True)
+    assert chunked_workspace(b, h_q, h_kv, s_q, s_k, 512, True) > 0, "shape is not chunked"
+    out, lse, o_ref, l_ref = run_case(b, h_q, h_kv, s_q, s_k, 512, True, 0, sink)
+    check(out, lse, o_ref, l_ref, f"chunked {case}")
+    one, one_lse, _, _ = run_case(b, h_q, h_kv, s_q, s_k, 512, True, 0, sink, chunked=False)
+    check(one, one_lse, o_ref, l_ref, f"single pass {case}")
 
 
 EDGE_LENGTHS = [1, 17, 63, 64, 65, 255, 257, 1000]
