@@ -605,7 +605,7 @@ int prefill_block_rows(int d, int mask) {
     case 64: return 128;
     case 128: return mask == kMaskCausalWindow ? 128 : 256;
     case 256: return 256;
-    case 512: return 64;
+    case 512: return 128;
     default: return 0;
   }
 }

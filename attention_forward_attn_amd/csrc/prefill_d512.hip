@@ -6,14 +6,14 @@ namespace attn {
 
 hipError_t prefill_d512(const PrefillParams &p, int mask, int n_units, hipStream_t s) {
   switch (mask) {
-    case kMaskNone: return launch_prefill<512, 4, 32, false, false, 1, 256>(p, n_units, s);
-    case kMaskCausal: return launch_prefill<512, 4, 32, true, false, 1, 256>(p, n_units, s);
-    default: return launch_prefill<512, 4, 32, true, true, 1, 256>(p, n_units, s);
+    case kMaskNone: return launch_prefill<512, 8, 32, false, false, 2, 256>(p, n_units, s);
+    case kMaskCausal: return launch_prefill<512, 8, 32, true, false, 2, 256>(p, n_units, s);
+    default: return launch_prefill<512, 8, 32, true, true, 2, 256>(p, n_units, s);
   }
 }
 
 hipError_t prefill_d512_chunked(const PrefillParams &p, const PrefillChunks &ck, hipStream_t s) {
-  return launch_prefill_chunked<512, 4, 32, 1, 256>(p, ck, s);
+  return launch_prefill_chunked<512, 8, 32, 2, 256>(p, ck, s);
 }
 
 }  // namespace attn

@@ -306,7 +306,7 @@ attn_status attn_fwd_prefill(const attn_prefill_args *args, void *stream);
  * Chunked causal prefill: the same operation and arguments as
  * attn_fwd_prefill, scheduled for shapes with too few query tiles to fill the
  * chip evenly under a causal mask (head dim 512, the STAGE_D.md page's hd=512
- * case: 64-row tiles, one workgroup per compute unit).  The visible key range
+ * case: 128-row tiles, two workgroups per compute unit).  The visible key range
  * of each long query tile is cut into chunks of about one compute unit's share
  * of the total work; each chunk runs as its own work unit, longest first, and
  * writes its normalised partial output (rounded to bf16) and fp32 LSE into the

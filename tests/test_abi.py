@@ -127,10 +127,11 @@ def wide_prefill(**over):
 def test_prefill_chunked_plan_sizes():
     lib = afa.load_library()
     size = lambda a: lib.attn_fwd_prefill_chunked_workspace_size(ctypes.byref(a))
-    # 64 query tiles of 64 rows; tile qt sees 2(qt+1) key tiles of 32; the work
-    # of the 4 heads is 4 * 4160 tiles, 65 per CU, so chunks are 65 tiles long:
-    # tiles 32..63 get 2 chunks each (parts: 4 heads x 32 tiles x 2 chunks x 64 rows).
-    rows = 4 * 32 * 2 * 64
+    # 32 query tiles of 128 rows; tile qt sees 4(qt+1) key tiles of 32; the work
+    # of the 4 heads is 4 * 2112 tiles, 33 per CU, so chunks are 33 tiles long:
+    # tiles 8..31 (36..128 key tiles) get 2..4 chunks (parts: 4 heads x 24 tiles
+    # x 4 chunk slots x 128 rows).
+    rows = 4 * 24 * 4 * 128
     assert size(wide_prefill()) == rows * 512 * 2 + rows * 4
     # nothing to balance, or not a chunked shape: 0
     assert size(wide_prefill(causal=0)) == 0
