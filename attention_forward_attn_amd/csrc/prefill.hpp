@@ -251,34 +251,28 @@ __device__ __forceinline__ void prefill_body(const PrefillParams &p, int bh, int
   // A partial chunk writes the same two quantities into its slot instead.
   const float lt = sum_across_halves(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (KSPLIT && partial) {
-    if (row_ok) {
-      const int64_t prow = kc.part * BM + (row - q0);
-      uint16_t *op = kc.o_part + prow * D + slice * DS + 4 * hi;
-#pragma unroll
-      for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          u32x2 val;
-          val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
-          val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
-          *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
-        }
-      if (hi == 0 && slice == 0) kc.lse_part[prow] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
-    }
+  // Staged: the output tile goes through the (now idle) K/V stages, and every
+  // wave passes both barriers.
+  const bool part_out = KSPLIT && partial;
+  uint16_t *const dst = part_out ? kc.o_part + (kc.part * BM + (w_lo - q0)) * D + slice * DS
+                                 : p.o + bi * p.o_sb + h * p.o_sh + (int64_t)w_lo * p.o_ss + slice * DS;
+  const int64_t dst_rs = part_out ? (int64_t)D : p.o_ss;
+  if constexpr (T::STAGED_OUT) {
+    static_assert(NW * T::OUT_BYTES <= 2 * T::STAGE_BYTES, "staged output must fit in the K/V stages");
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with the last stage
+    char *xw = reinterpret_cast<char *>(smem) + wave * T::OUT_BYTES;
+    T::stage_out(o, inv, xw, lane);
+    __syncthreads();
+    T::store_out(xw, lane, dst, dst_rs, max(0, min(32, p.s_q - w_lo)));
   } else if (row_ok) {
-    uint16_t *op = p.o + bi * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss + slice * DS + 4 * hi;
-#pragma unroll
-    for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        u32x2 val;
-        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
-        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
-        *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
-      }
-    if (p.lse != nullptr && hi == 0 && slice == 0)
-      p.lse[bi * p.lse_sb + h * p.lse_sh + row] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+    T::store_direct(o, inv, dst + (row - w_lo) * dst_rs, lane);
+  }
+  if (part_out) {
+    if (row_ok && hi == 0 && slice == 0)
+      kc.lse_part[kc.part * BM + (row - q0)] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  } else if (p.lse != nullptr && row_ok && hi == 0 && slice == 0) {
+    p.lse[bi * p.lse_sb + h * p.lse_sh + row] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   }
 }
 
@@ -516,24 +510,25 @@ void prefill_pp_kernel(PrefillParams p) {
       }
     }
   }
-  wait_vmcnt<0>();
+  wait_vmcnt<0>();  // every load into the ring (empty tiles included) has landed
 
   const float lt = sum_across_halves(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (row_ok) {
-    uint16_t *op = p.o + bi * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss + 4 * hi;
-#pragma unroll
-    for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        u32x2 val;
-        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
-        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
-        *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
-      }
-    if (p.lse != nullptr && hi == 0)
-      p.lse[bi * p.lse_sb + h * p.lse_sh + row] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  // Staged: the output tile goes through the idle ring, and every wave passes
+  // both barriers.
+  uint16_t *const dst = p.o + bi * p.o_sb + h * p.o_sh + (int64_t)w_lo * p.o_ss;
+  if constexpr (T::STAGED_OUT) {
+    static_assert(8 * T::OUT_BYTES <= STAGES * T::STAGE_BYTES, "staged output must fit in the ring");
+    __syncthreads();  // every wave is done with the ring
+    char *xw = reinterpret_cast<char *>(smem) + wave * T::OUT_BYTES;
+    T::stage_out(o, inv, xw, lane);
+    __syncthreads();
+    T::store_out(xw, lane, dst, p.o_ss, max(0, min(32, p.s_q - w_lo)));
+  } else if (row_ok) {
+    T::store_direct(o, inv, dst + (int64_t)(row - w_lo) * p.o_ss, lane);
   }
+  if (p.lse != nullptr && row_ok && hi == 0)
+    p.lse[bi * p.lse_sb + h * p.lse_sh + row] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
 }
 
 template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>

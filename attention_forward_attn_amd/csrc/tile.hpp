@@ -588,6 +588,62 @@ struct Tile {
     fine_step<0>(o, pk, s, qreg, vpre, fb, ln, v_off, k_off, hook);
   }
 
+  // Output epilogue of one wave: its 32 x DS tile of O, normalised by inv and
+  // rounded to bf16, goes to memory through LDS.  A lane holds 8-byte pieces of
+  // one row (columns db*32 + 8*gi + 4*hi .. +3), so stores straight from the
+  // accumulators would touch 32 rows per instruction; stage_out puts the
+  // pieces into a 32 x DS tile at xw (16-byte chunks XOR-swizzled by row),
+  // and store_out then writes whole 16-byte chunks of consecutive row
+  // segments.  Row r goes to dst + r * row_stride; rows at or past n_rows are
+  // not written.  Between the two calls the workgroup must pass a barrier (the
+  // tile is read back by other lanes), and xw must not be in use by any load.
+  static constexpr int OUT_BYTES = 32 * DS * 2;  // LDS bytes of one wave's staged tile
+  // Staging pays at slices up to 128 columns; at 256 the kernels already hold
+  // (nearly) all 256 VGPRs and its registers spill into the tile loop, so
+  // those store straight from the accumulators (store_direct).
+  static constexpr bool STAGED_OUT = DS <= 128;
+  __device__ static __forceinline__ void store_direct(const f32x16 (&o)[NDB], float inv, uint16_t *dst_row,
+                                                      int lane) {
+    uint16_t *op = dst_row + 4 * (lane >> 5);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        u32x2 val;
+        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
+        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
+        *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
+      }
+  }
+  __device__ static __forceinline__ void stage_out(const f32x16 (&o)[NDB], float inv, char *xw, int lane) {
+    constexpr int NC = DS / 8;             // 16-byte chunks per row segment
+    constexpr int SW = NC < 16 ? NC : 16;  // swizzle span
+    const int lr = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        u32x2 val;
+        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
+        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
+        *reinterpret_cast<u32x2 *>(xw + lr * DS * 2 + ((db * 4 + gi) ^ (lr % SW)) * 16 + 8 * hi) = val;
+      }
+  }
+  __device__ static __forceinline__ void store_out(const char *xw, int lane, uint16_t *dst, int64_t row_stride,
+                                                   int n_rows) {
+    constexpr int NC = DS / 8;
+    constexpr int SW = NC < 16 ? NC : 16;
+    constexpr int RPI = 64 / NC;  // rows per store instruction
+    static_assert(64 % NC == 0 && NC <= 64, "whole row segments per store");
+    const int c = lane % NC;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / NC;
+      const u32x4 val = *reinterpret_cast<const u32x4 *>(xw + r * DS * 2 + (c ^ (r % SW)) * 16);
+      if (r < n_rows) *reinterpret_cast<u32x4 *>(dst + r * row_stride + c * 8) = val;
+    }
+  }
+
   // Key index (relative to the tile start) held by accumulator register i of block kb.
   __device__ static __forceinline__ int key_of(int kb, int i, int hi) {
     return kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
