@@ -179,8 +179,16 @@ struct Tile {
   // keeps at most 8 + 4 LDS addresses.
   static constexpr int NKL = NKK < 8 ? NKK : 8;
   static constexpr int NVL = NDB < 4 ? NDB : 4;
+  // At D = 512 one 1-KiB load is exactly one row (64 chunks), so a load's
+  // offsets are lane * 16 XOR the row's swizzle plus the row's (wave-uniform)
+  // start; they are formed when the load issues and the lane keeps only
+  // lane * 16, which frees 2 * LOADS - 1 VGPRs for the wide head dim.  The
+  // row start stays in the vector offset: the buffer range check, which
+  // zero-fills rows past the end of the keys, does not see the scalar offset.
+  static constexpr bool ROW_DMA = CH == 64;
   struct Lane {
-    uint32_t kg[LOADS], vg[LOADS];  // global byte offsets (tile-relative)
+    uint32_t kg[LOADS], vg[LOADS];  // global byte offsets (tile-relative); unused with ROW_DMA
+    uint32_t l16;                   // lane * 16 (ROW_DMA only)
     uint32_t kl[NKL];               // LDS address of the K operand of k-step kk (mod 8), key block 0
     uint32_t vl[NVL];               // LDS address of the V^T operand of head-dim block db (mod 4), k-step 0
   };
@@ -188,12 +196,16 @@ struct Tile {
   // DMA offsets: wave w of the NW loading waves, writing a BN x D tile.
   __device__ static __forceinline__ void init_dma(Lane &ln, int64_t k_rs, int64_t v_rs, int w, int lane) {
     static_assert(LOADS_EXACT * 64 * NW * 8 == TILE_ELEMS, "tile must split into whole 1-KiB wave loads");
+    if constexpr (ROW_DMA) {
+      ln.l16 = (uint32_t)lane * 16;
+    } else {
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int pch = (u * NW + w) * 64 + lane;  // physical 16-byte chunk written by this lane
-      const int r = pch / CH;
-      ln.kg[u] = (uint32_t)(r * k_rs * 2) + (uint32_t)(((pch % CH) ^ kswz(r)) * 16);
-      ln.vg[u] = (uint32_t)(r * v_rs * 2) + (uint32_t)(((pch % CH) ^ vswz(r)) * 16);
+      for (int u = 0; u < LOADS; ++u) {
+        const int pch = (u * NW + w) * 64 + lane;  // physical 16-byte chunk written by this lane
+        const int r = pch / CH;
+        ln.kg[u] = (uint32_t)(r * k_rs * 2) + (uint32_t)(((pch % CH) ^ kswz(r)) * 16);
+        ln.vg[u] = (uint32_t)(r * v_rs * 2) + (uint32_t)(((pch % CH) ^ vswz(r)) * 16);
+      }
     }
   }
 
@@ -238,9 +250,18 @@ struct Tile {
     const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * rs * 2 + D * 2) : 0u;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(rows > 0 ? base + j0 * rs : base, bytes);
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (u * NW + w) * 512), 16,
-                                               is_v ? ln.vg[u] : ln.kg[u], 0, 0, 0);
+    for (int u = 0; u < LOADS; ++u) {
+      uint32_t off;
+      if constexpr (ROW_DMA) {
+        const int row = u * NW + w;  // the tile row this load writes
+        uint32_t l16 = ln.l16;
+        asm volatile("" : "+v"(l16));  // keep the offsets from being hoisted into registers held all loop
+        off = (l16 ^ (uint32_t)((is_v ? vswz(row) : kswz(row)) * 16)) + (uint32_t)(row * rs * 2);
+      } else {
+        off = is_v ? ln.vg[u] : ln.kg[u];
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (u * NW + w) * 512), 16, off, 0, 0, 0);
+    }
   }
   __device__ static __forceinline__ void dma_k(const Lane &ln, uint16_t *dst, const uint16_t *base,
                                                int64_t rs, int j0, int nkeys, int w) {
