@@ -7,6 +7,7 @@
 #include <climits>
 #include <cmath>
 #include <vector>
+#include <functional>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -140,11 +141,22 @@ namespace {
 
 // Plan of the chunked causal prefill (d = 512; see attn_fwd_prefill_chunked).
 // The key range of each query tile is cut into chunks of `chunk_tiles` key
-// tiles, with the chunk length set so that one chunk is about one compute
-// unit's share of the whole causal work (256 CUs), but no shorter than
-// kMinChunkTiles; the (query tile, chunk) pairs are launched longest first.
+// tiles; the (query tile, chunk) pairs are launched longest first.  The chunk
+// length is chosen by simulating that launch for each candidate length and
+// keeping the shortest makespan: unit v of the grid goes to XCD v % 8 and, on
+// its XCD, starts on whichever of the 32 compute units frees first (one
+// workgroup per compute unit at d = 512); a unit costs its key tiles plus
+// kUnitFixedTiles, the per-unit cost of its prologue, epilogue and share of
+// the merge, measured in key tiles (with it the simulated makespan tracked the
+// measured time of eight chunk lengths on the b1 h4 s4096 workload to within
+// 1 us).  Candidates run from three quarters to twice the even share of the
+// work per compute unit (never below kMinChunkTiles); ties go to the longer
+// chunk (fewer partials to merge).
 constexpr int kChunkTargetCUs = 256;
+constexpr int kXcds = 8;
+constexpr int kCusPerXcd = 32;
 constexpr int kMinChunkTiles = 8;
+constexpr int64_t kUnitFixedTiles = 10;
 
 struct ChunkPlan {
   int chunk_tiles = 0, qt0 = 0, max_chunks = 0, n_rank = 0;
@@ -152,10 +164,58 @@ struct ChunkPlan {
   int64_t o_bytes = 0, lse_bytes = 0;  // partial buffers; o_bytes is a multiple of 256
 };
 
+struct ChunkUnit { int64_t len, qt, ch; };
+
+// Units of chunk length c in launch order (longest first, later query tiles
+// first among equals); false if the plan exceeds the rank table or 255 chunks.
+bool chunk_units(const std::vector<int64_t> &T, int64_t c, std::vector<ChunkUnit> &es) {
+  es.clear();
+  for (int64_t qt = 0; qt < (int64_t)T.size(); ++qt) {
+    const int64_t n = T[qt] > 0 ? (T[qt] + c - 1) / c : 1;
+    if (n > 255) return false;
+    for (int64_t ch = 0; ch < n; ++ch) es.push_back({T[qt] > 0 ? std::min(c, T[qt] - ch * c) : 0, qt, ch});
+  }
+  if ((int64_t)es.size() > attn::kMaxChunkRanks) return false;
+  std::stable_sort(es.begin(), es.end(), [](const ChunkUnit &x, const ChunkUnit &y) {
+    return x.len != y.len ? x.len > y.len : x.qt > y.qt;
+  });
+  return true;
+}
+
+// Simulated makespan (key tiles) of the launch of es, each rank repeated for
+// the bh heads (grid index = rank * bh + head).
+int64_t chunk_makespan(const std::vector<ChunkUnit> &es, int64_t bh) {
+  std::vector<int64_t> cu[kXcds];
+  for (auto &v : cu) v.assign(kCusPerXcd, 0);
+  int64_t v = 0, mk = 0;
+  for (const ChunkUnit &e : es)
+    for (int64_t j = 0; j < bh; ++j, ++v) {
+      std::vector<int64_t> &h = cu[v % kXcds];  // min-heap of finish times
+      std::pop_heap(h.begin(), h.end(), std::greater<int64_t>());
+      h.back() += e.len + kUnitFixedTiles;
+      mk = std::max(mk, h.back());
+      std::push_heap(h.begin(), h.end(), std::greater<int64_t>());
+    }
+  return mk;
+}
+
+struct PlanMemo {  // the last plan this thread made, keyed by the shape
+  bool valid = false, chunked = false;
+  int64_t b, h_q, s_q, s_k, d;
+  ChunkPlan pl;
+};
+thread_local PlanMemo g_plan_memo;
+
 // Fills pl and returns true when the call would be chunked; false leaves the
 // single-pass kernel in charge.  Arguments must already be valid.
 bool plan_chunks(const attn_prefill_args *a, ChunkPlan &pl) {
   if (a->d != 512 || !a->causal || a->window > 0 || a->s_q == 0 || a->s_k == 0) return false;
+  PlanMemo &mm = g_plan_memo;
+  if (mm.valid && mm.b == a->b && mm.h_q == a->h_q && mm.s_q == a->s_q && mm.s_k == a->s_k && mm.d == a->d) {
+    if (mm.chunked) pl = mm.pl;
+    return mm.chunked;
+  }
+  mm.valid = false;
   const int bm = attn::prefill_block_rows(512, attn::kMaskCausal);
   const int bn = attn::prefill_block_keys(512, attn::kMaskCausal);
   const int64_t nq = (a->s_q + bm - 1) / bm;
@@ -171,31 +231,36 @@ bool plan_chunks(const attn_prefill_args *a, ChunkPlan &pl) {
     tmax = std::max(tmax, T[qt]);
   }
   total *= bh;
-  const int64_t c = std::max<int64_t>(kMinChunkTiles, (total + kChunkTargetCUs - 1) / kChunkTargetCUs);
-  if (c >= tmax) return false;  // enough query tiles already: nothing to balance
-  struct E { int64_t len, qt, ch; };
-  std::vector<E> es;
-  for (int64_t qt = 0; qt < nq; ++qt) {
-    const int64_t n = T[qt] > 0 ? (T[qt] + c - 1) / c : 1;
-    if (n > 255) return false;
-    for (int64_t ch = 0; ch < n; ++ch) es.push_back({T[qt] > 0 ? std::min(c, T[qt] - ch * c) : 0, qt, ch});
+  const int64_t c0 = std::max<int64_t>(kMinChunkTiles, (total + kChunkTargetCUs - 1) / kChunkTargetCUs);
+  bool chunked = false;
+  std::vector<ChunkUnit> es, best;
+  if (c0 < tmax && nq < (1 << 23)) {
+    int64_t best_c = 0, best_mk = 0;
+    const int64_t lo = std::max<int64_t>(kMinChunkTiles, c0 * 3 / 4), hi = std::min(tmax - 1, 2 * c0);
+    for (int64_t c = lo; c <= hi; ++c) {
+      if (!chunk_units(T, c, es) || (int64_t)es.size() * bh > kMaxIndex) continue;
+      const int64_t mk = chunk_makespan(es, bh);
+      if (best_c == 0 || mk <= best_mk) best_c = c, best_mk = mk, best = es;
+    }
+    if (best_c > 0) {
+      chunked = true;
+      pl.chunk_tiles = (int)best_c;
+      pl.n_rank = (int)best.size();
+      for (int i = 0; i < pl.n_rank; ++i) pl.rank[i] = (uint32_t)(best[i].qt << 8) | (uint32_t)best[i].ch;
+      int64_t qt0 = nq;
+      while (qt0 > 0 && T[qt0 - 1] > best_c) --qt0;  // T is non-decreasing in qt
+      pl.qt0 = (int)qt0;
+      pl.max_chunks = (int)((tmax + best_c - 1) / best_c);
+      const int64_t rows = bh * (nq - qt0) * pl.max_chunks * bm;
+      pl.o_bytes = (rows * a->d * 2 + 255) / 256 * 256;
+      pl.lse_bytes = rows * 4;
+    }
   }
-  if ((int64_t)es.size() > attn::kMaxChunkRanks || (int64_t)es.size() * bh > kMaxIndex || nq >= (1 << 23))
-    return false;
-  std::stable_sort(es.begin(), es.end(), [](const E &x, const E &y) {
-    return x.len != y.len ? x.len > y.len : x.qt > y.qt;
-  });
-  pl.chunk_tiles = (int)c;
-  pl.n_rank = (int)es.size();
-  for (int i = 0; i < pl.n_rank; ++i) pl.rank[i] = (uint32_t)(es[i].qt << 8) | (uint32_t)es[i].ch;
-  int64_t qt0 = nq;
-  while (qt0 > 0 && T[qt0 - 1] > c) --qt0;  // T is non-decreasing in qt
-  pl.qt0 = (int)qt0;
-  pl.max_chunks = (int)((tmax + c - 1) / c);
-  const int64_t rows = bh * (nq - qt0) * pl.max_chunks * bm;
-  pl.o_bytes = (rows * a->d * 2 + 255) / 256 * 256;
-  pl.lse_bytes = rows * 4;
-  return true;
+  mm.b = a->b; mm.h_q = a->h_q; mm.s_q = a->s_q; mm.s_k = a->s_k; mm.d = a->d;
+  mm.chunked = chunked;
+  if (chunked) mm.pl = pl;
+  mm.valid = true;
+  return chunked;
 }
 
 // Validation and parameter block of a prefill call; on success *done is set

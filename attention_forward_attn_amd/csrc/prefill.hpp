@@ -286,8 +286,8 @@ void prefill_kernel(PrefillParams p) {
 
 // Causal prefill with the key ranges of long query tiles cut into chunks, so
 // that the work units are of similar length when there are too few query
-// tiles to keep the chip busy (the d = 512 shapes: 128-row tiles, two
-// workgroups per CU).  Unit v is (rank v / (b*h_q), head v % (b*h_q)); the rank
+// tiles to keep the chip busy (the d = 512 shapes: 128-row tiles, one
+// 8-wave workgroup per CU).  Unit v is (rank v / (b*h_q), head v % (b*h_q)); the rank
 // table, built on the host, lists the (query tile, chunk) pairs longest first.
 template <int D, int NW, int BN, int OCC, int DS = D>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))

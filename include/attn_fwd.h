@@ -33,8 +33,9 @@
  *    stride must be a multiple of 16 bytes (8 elements); fp32 pointers must be
  *    4-byte aligned.
  *  - Reentrancy: there is no global mutable state besides the thread-local
- *    error text, so calls from several host threads are safe as long as they
- *    do not write the same output buffers.
+ *    error text and a thread-local memo of the last chunk plan (a pure
+ *    function of the shape), so calls from several host threads are safe as
+ *    long as they do not write the same output buffers.
  *  - Every output row is written, including rows that see no key.
  */
 #ifndef ATTN_FWD_H
@@ -306,9 +307,12 @@ attn_status attn_fwd_prefill(const attn_prefill_args *args, void *stream);
  * Chunked causal prefill: the same operation and arguments as
  * attn_fwd_prefill, scheduled for shapes with too few query tiles to fill the
  * chip evenly under a causal mask (head dim 512, the STAGE_D.md page's hd=512
- * case: 128-row tiles, two workgroups per compute unit).  The visible key range
- * of each long query tile is cut into chunks of about one compute unit's share
- * of the total work; each chunk runs as its own work unit, longest first, and
+ * case: 128-row tiles, one 8-wave workgroup per compute unit).  The visible key
+ * range of each long query tile is cut into chunks whose length the host picks
+ * by simulating the launch (units dealt to the 8 XCDs in grid order, each
+ * starting on the first free compute unit of its XCD) for lengths around one
+ * compute unit's share of the work and keeping the shortest makespan; each
+ * chunk runs as its own work unit, longest first, and
  * writes its normalised partial output (rounded to bf16) and fp32 LSE into the
  * workspace; a second kernel merges the chunks of each row by their LSEs (the
  * per-segment merge of the same page's "O rescale (kt>0)" workaround).  A sink

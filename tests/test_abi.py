@@ -124,15 +124,46 @@ def wide_prefill(**over):
     return good_prefill(**base)
 
 
+def _chunk_plan_rows(b, h, s_q, s_k, bm=128, bn=32, fixed=10, xcds=8, cus=32, target=256, min_tiles=8):
+    """The chunk plan's rule restated: partial rows of the chunk length whose simulated launch ends first."""
+    import heapq
+    nq = -(-s_q // bm)
+    T = [-(-max(0, min(s_k, min(s_q, (qt + 1) * bm) - 1 + s_k - s_q + 1)) // bn) for qt in range(nq)]
+    bh, tmax = b * h, max(T)
+    c0 = max(min_tiles, -(-sum(T) * bh // target))
+    if c0 >= tmax:
+        return 0
+    best = None
+    for c in range(max(min_tiles, c0 * 3 // 4), min(tmax - 1, 2 * c0) + 1):
+        units = sorted(((min(c, T[qt] - ch * c), qt) for qt in range(nq) for ch in range(-(-T[qt] // c))),
+                       key=lambda u: (-u[0], -u[1]))
+        heaps = [[0] * cus for _ in range(xcds)]
+        mk, v = 0, 0
+        for length, _ in units:
+            for _ in range(bh):
+                t = heapq.heappop(heaps[v % xcds]) + length + fixed
+                heapq.heappush(heaps[v % xcds], t)
+                mk, v = max(mk, t), v + 1
+        if best is None or mk <= best[0]:
+            best = (mk, c)
+    c = best[1]
+    qt0 = sum(1 for t in T if t <= c)
+    return bh * (nq - qt0) * -(-tmax // c) * bm
+
+
 def test_prefill_chunked_plan_sizes():
     lib = afa.load_library()
     size = lambda a: lib.attn_fwd_prefill_chunked_workspace_size(ctypes.byref(a))
-    # 32 query tiles of 128 rows; tile qt sees 4(qt+1) key tiles of 32; the work
-    # of the 4 heads is 4 * 2112 tiles, 33 per CU, so chunks are 33 tiles long:
-    # tiles 8..31 (36..128 key tiles) get 2..4 chunks (parts: 4 heads x 24 tiles
-    # x 4 chunk slots x 128 rows).
-    rows = 4 * 24 * 4 * 128
+    # 32 query tiles of 128 rows; tile qt sees 4(qt+1) key tiles of 32.  The
+    # simulated launch ends first with 36-tile chunks: tiles 9..31 (40..128 key
+    # tiles) get 2..4 chunks (parts: 4 heads x 23 tiles x 4 chunk slots x 128 rows).
+    rows = 4 * 23 * 4 * 128
+    assert _chunk_plan_rows(1, 4, 4096, 4096) == rows
     assert size(wide_prefill()) == rows * 512 * 2 + rows * 4
+    for s in (1024, 2048, 3000, 8192):
+        r = _chunk_plan_rows(1, 4, s, s)
+        want = (r * 512 * 2 + 255) // 256 * 256 + r * 4 if r else 0
+        assert size(wide_prefill(s=s)) == want, s
     # nothing to balance, or not a chunked shape: 0
     assert size(wide_prefill(causal=0)) == 0
     assert size(wide_prefill(window=1024)) == 0
