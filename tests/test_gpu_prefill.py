@@ -84,12 +84,16 @@ def chunked_workspace(b, h_q, h_kv, s_q, s_k, d, causal, window=0):
 
 
 # d = 512 causal shapes whose key ranges the library cuts into chunks
+# (key tiles of 32; the chunk length is the one the host plan's launch simulation picks)
 CHUNKED = [
     # b, h_q, h_kv, s_q, s_k, sink
-    (1, 1, 1, 1024, 1024, False),  # tiles of 32 keys, chunks of 8 tiles: up to 4 chunks per query tile
-    (1, 2, 1, 1000, 1100, True),   # GQA, s_k > s_q, ragged tail, sink in the first chunk only
+    (1, 1, 1, 1024, 1024, False),  # 8-tile chunks, up to 4 per 128-row query tile
+    (1, 2, 1, 1000, 1100, True),   # GQA, s_k > s_q, ragged tail, sink in the first chunk only (8-tile chunks)
     (1, 2, 2, 700, 500, False),    # s_q > s_k: leading rows see no key, later chunks partly empty
     (2, 2, 2, 640, 640, True),
+    (1, 3, 3, 3000, 3000, False),  # 16-tile chunks, up to 6 per query tile, ragged last query tile
+    (2, 4, 4, 1536, 2048, False),  # 18-tile chunks, s_k > s_q
+    (1, 8, 8, 2048, 2048, True),   # 20-tile chunks
 ]
 
 
