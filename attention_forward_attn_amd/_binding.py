@@ -232,11 +232,13 @@ def prefill(q, k, v, *, scale: float | None = None, causal: bool = False, window
     (O, LSE): O bf16 shaped like q, LSE fp32 [b, h_q, s_q] (None when
     ``return_lse`` is False and no ``lse`` buffer is given).
 
-    With ``chunked`` (the default) the call goes through
-    attn_fwd_prefill_chunked, which cuts long causal key ranges into chunks
-    when the library's plan says so (d = 512); ``workspace`` (uint8 device
-    tensor) is then used if given, else allocated.  ``chunked=False`` always
-    runs the single-pass attn_fwd_prefill.
+    With ``chunked`` (the default) the call goes through the scheduled
+    attn_fwd_prefill_chunked: long causal key ranges cut into chunks when the
+    library's plan says so (d = 512), or query tiles taken from per-XCD work
+    queues (d = 256); ``workspace`` (uint8 device tensor
+    whose first 256 bytes are zero before its first use, as every call leaves
+    them) is then used if given, else allocated zeroed.  ``chunked=False``
+    always runs the single-pass attn_fwd_prefill.
     """
     import torch
 
@@ -263,7 +265,7 @@ def prefill(q, k, v, *, scale: float | None = None, causal: bool = False, window
         _check(lib.attn_fwd_prefill(ctypes.byref(a), _stream(stream)))
         return out, lse
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zeroed queue header
     _check(lib.attn_fwd_prefill_chunked(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse

@@ -263,6 +263,19 @@ bool plan_chunks(const attn_prefill_args *a, ChunkPlan &pl) {
   return chunked;
 }
 
+// Workspace of the scheduled prefill: a 256-byte header holding the work-queue
+// counters (two uint32; zero before first use, left zero by every call), then
+// the chunk partials of a chunked plan.
+constexpr size_t kQueueBytes = 256;
+// Shapes whose scheduled form takes query tiles from the work queue: the
+// ping-pong kernel at d = 256 (b1 h8 s16384 causal: 1180 -> 1015..1036 us).
+// At d = 128 the queued form of the same kernel measured 1-7 % slower than
+// the fixed placement, so d = 128 keeps it.
+bool queue_shape(int d, int mask) {
+  (void)mask;
+  return d == 256;
+}
+
 // Validation and parameter block of a prefill call; on success *done is set
 // when there is nothing to launch (s_q == 0).
 attn_status prepare_prefill(const attn_prefill_args *a, attn::PrefillParams &p, int &mask, int64_t &n_units,
@@ -364,8 +377,8 @@ size_t attn_fwd_prefill_chunked_workspace_size(const attn_prefill_args *a) {
   bool done;
   if (prepare_prefill(a, p, mask, n_units, done) != ATTN_OK || done) return 0;
   static thread_local ChunkPlan pl;
-  if (!plan_chunks(a, pl)) return 0;
-  return (size_t)(pl.o_bytes + pl.lse_bytes);
+  if (plan_chunks(a, pl)) return kQueueBytes + (size_t)(pl.o_bytes + pl.lse_bytes);
+  return queue_shape(a->d, mask) ? kQueueBytes : 0;
 }
 
 attn_status attn_fwd_prefill_chunked(const attn_prefill_args *a, void *workspace, size_t workspace_bytes,
@@ -377,23 +390,37 @@ attn_status attn_fwd_prefill_chunked(const attn_prefill_args *a, void *workspace
   attn_status st = prepare_prefill(a, p, mask, n_units, done);
   if (st != ATTN_OK || done) return st;
   static thread_local ChunkPlan pl;
-  if (!plan_chunks(a, pl)) return launch_prefill(a, p, mask, n_units, stream);
-  const size_t need = (size_t)(pl.o_bytes + pl.lse_bytes);
+  const bool chunked = plan_chunks(a, pl);
+  const bool queued = !chunked && queue_shape(a->d, mask);
+  if (!chunked && !queued) return launch_prefill(a, p, mask, n_units, stream);
+  const size_t need = kQueueBytes + (chunked ? (size_t)(pl.o_bytes + pl.lse_bytes) : 0);
   if (workspace == nullptr || workspace_bytes < need)
-    return fail(ATTN_ERR_WORKSPACE, "chunked prefill needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
-                workspace == nullptr ? ", NULL" : "");
+    return fail(ATTN_ERR_WORKSPACE, "scheduled prefill needs %zu workspace bytes (got %zu%s)", need,
+                workspace_bytes, workspace == nullptr ? ", NULL" : "");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (queued) {
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "device query");
+    uint32_t *queue = static_cast<uint32_t *>(workspace);
+    e = attn::prefill_d256_queue(p, mask, (int)n_units, std::max(n_cu, 1), queue, s);
+    if (e != hipSuccess) return hip_fail(e, "queued prefill launch");
+    return ok();
+  }
+  char *parts = static_cast<char *>(workspace) + kQueueBytes;
   attn::PrefillChunks ck;
-  ck.o_part = static_cast<uint16_t *>(workspace);
-  ck.lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.o_bytes);
+  ck.o_part = reinterpret_cast<uint16_t *>(parts);
+  ck.lse_part = reinterpret_cast<float *>(parts + pl.o_bytes);
   ck.chunk_tiles = pl.chunk_tiles;
   ck.qt0 = pl.qt0;
   ck.max_chunks = pl.max_chunks;
   ck.n_rank = pl.n_rank;
   std::memcpy(ck.rank, pl.rank, sizeof(uint32_t) * pl.n_rank);
   std::memset(ck.rank + pl.n_rank, 0, sizeof(uint32_t) * (attn::kMaxChunkRanks - pl.n_rank));
-  hipError_t e = attn::prefill_d512_chunked(p, ck, static_cast<hipStream_t>(stream));
+  hipError_t e = attn::prefill_d512_chunked(p, ck, s);
   if (e != hipSuccess) return hip_fail(e, "chunked prefill launch");
   return ok();
 }

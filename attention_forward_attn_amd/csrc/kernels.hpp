@@ -15,6 +15,11 @@ hipError_t prefill_d64(const PrefillParams &p, int mask, int n_units, hipStream_
 hipError_t prefill_d128(const PrefillParams &p, int mask, int n_units, hipStream_t s);
 hipError_t prefill_d256(const PrefillParams &p, int mask, int n_units, hipStream_t s);
 hipError_t prefill_d512(const PrefillParams &p, int mask, int n_units, hipStream_t s);
+// Work-queue form of the ping-pong prefill at d = 256: n_wg workgroups take
+// query tiles from the per-XCD counters at queue (a 256-byte header, zero
+// before the first launch, left zero by every launch).
+hipError_t prefill_d256_queue(const PrefillParams &p, int mask, int n_units, int n_wg, uint32_t *queue,
+                              hipStream_t s);
 // Key tiles per step of the prefill kernel for head dim d and mask kind.
 int prefill_block_keys(int d, int mask);
 // Causal d = 512 prefill with chunked key ranges (ck filled by the host) and the merge of the partials.

@@ -18,6 +18,8 @@
 //
 #pragma once
 
+#include <type_traits>
+
 #include "combine.hpp"
 #include "tile.hpp"
 
@@ -355,21 +357,27 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p, Pre
 // before A_i.  Every wave's loads of tile i+1 are waited for before A_{i+1},
 // so they have a full iteration or more to land.  The value operands of a tile are read ahead at
 // the end of the softmax, so the MMA phase is mostly MMA issue.
-template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_pp_kernel(PrefillParams p) {
+struct NoUnitHook {
+  __device__ void operator()() const {}
+};
+// on_loop_end() runs in every thread right after the tile loop, before the
+// output epilogue (the work queue takes its next ticket there).
+template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES, typename Hook = NoUnitHook>
+__device__ __forceinline__ void pp_unit(const PrefillParams &p, int bh, int qt, Hook on_loop_end = Hook{}) {
   using T = Tile<D, 8, BN>;
   constexpr int BM = T::BM;
   static_assert(T::SPLIT == 1 && BM == 256 && STAGES >= 3, "ping-pong shape");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * T::STAGE_BYTES / 2];
 
-  const int tid = threadIdx.x;
+  // In the work-queue loop the thread index is made opaque: the compiler would
+  // otherwise hoist the per-lane address set-up of every unit out of the loop
+  // and hold it in registers across the whole launch (spilling).
+  int tid = threadIdx.x;
+  if constexpr (!std::is_same<Hook, NoUnitHook>::value) asm volatile("" : "+v"(tid));
   const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
   const int grp = wave >> 2;
   const int rb = 2 * (wave & 3) + grp;  // 32-row block of this wave inside the query tile
 
-  int bh, qt;
-  prefill_unit<CAUSAL && !WINDOW>(p, blockIdx.x, bh, qt);
   const int bi = bh / p.h_q, h = bh - bi * p.h_q;
   const int g = h / p.ratio;
   const int q0 = qt * BM;
@@ -511,6 +519,7 @@ void prefill_pp_kernel(PrefillParams p) {
     }
   }
   wait_vmcnt<0>();  // every load into the ring (empty tiles included) has landed
+  on_loop_end();
 
   const float lt = sum_across_halves(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
@@ -532,8 +541,102 @@ void prefill_pp_kernel(PrefillParams p) {
 }
 
 template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_pp_kernel(PrefillParams p) {
+  int bh, qt;
+  prefill_unit<CAUSAL && !WINDOW>(p, blockIdx.x, bh, qt);
+  pp_unit<D, BN, CAUSAL, WINDOW, STAGES>(p, bh, qt);
+}
+
+// Work-queue form of the ping-pong prefill.  The grid has one workgroup per
+// compute unit.  The units are those of the fixed placement (unit v belongs to
+// XCD v % 8, which keeps a kv head's query tiles on one XCD and its K/V in one
+// L2; prefill_unit), held in one queue per XCD in the same order (longest
+// first under a plain causal mask): queue x hands out units x, x + 8, x + 16,
+// ... through the ticket counter queue[4x].  A workgroup first drains the
+// queue of the XCD it runs on (read from the XCC_ID hardware register) and
+// then takes what is left in the others, so when the XCDs of a chip settle at
+// different clocks the fast ones finish the slow ones' last (shortest) tiles
+// instead of waiting for them.  Tickets are taken with returning atomics, so a
+// workgroup increments the exit counter (queue[32]) only after its failing
+// ticket of every queue has been counted; the workgroup that exits last
+// therefore sees no ticket after it and resets all counters to zero for the
+// next launch.  queue must be zero before the first launch, and launches
+// sharing a queue must not overlap.
+constexpr int kQueueXcds = 8;
+constexpr uint32_t kQueueDone = 0xffffffffu;  // no unit left in any queue
+constexpr uint32_t kQueueRetry = 0xfffffffeu; // lost a race for a queue's last unit: look again
+template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_pp_queue_kernel(PrefillParams p, uint32_t *queue) {
+  __shared__ uint32_t s_unit;
+  const uint32_t n_units = (uint32_t)(p.b * p.h_q * p.n_qtiles);
+  const int home = __builtin_amdgcn_s_getreg((31 << 11) | 20) & (kQueueXcds - 1);  // XCC_ID
+  bool stealing = false;  // the home queue is empty
+  // Thread 0 only: the next unit, kQueueRetry when none has been taken yet.
+  uint32_t ahead = kQueueRetry;
+  auto home_ticket = [&]() -> uint32_t {
+    const uint64_t v = (uint64_t)home + (uint64_t)kQueueXcds * atomicAdd(queue + 4 * home, 1u);
+    return v < n_units ? (uint32_t)v : kQueueRetry;
+  };
+  // A unit from another queue that still has some (all eight counters read in
+  // one round trip; a queue that looks empty is not touched); kQueueRetry
+  // after a lost race for a last unit, kQueueDone when every queue is empty.
+  auto steal_ticket = [&]() -> uint32_t {
+    uint32_t c[kQueueXcds];
+#pragma unroll
+    for (int j = 0; j < kQueueXcds; ++j)
+      c[j] = __hip_atomic_load(queue + 4 * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int x = -1;
+#pragma unroll
+    for (int j = 1; j <= kQueueXcds; ++j) {
+      const int y = (home + j) & (kQueueXcds - 1);
+      const uint32_t size = n_units > (uint32_t)y ? (n_units - 1 - y) / kQueueXcds + 1 : 0;
+      if (x < 0 && c[y] < size) x = y;
+    }
+    if (x < 0) return kQueueDone;
+    const uint64_t v = (uint64_t)x + (uint64_t)kQueueXcds * atomicAdd(queue + 4 * x, 1u);
+    return v < n_units ? (uint32_t)v : kQueueRetry;
+  };
+  for (;;) {
+    if (threadIdx.x == 0) s_unit = ahead != kQueueRetry ? ahead : stealing ? steal_ticket() : home_ticket();
+    __syncthreads();
+    const uint32_t u = s_unit;
+    __syncthreads();  // every wave has read the unit before thread 0 takes the next
+    if (u == kQueueDone) break;
+    if (u == kQueueRetry) {  // the home queue is empty, or a steal lost its race
+      stealing = true;
+      continue;
+    }
+    ahead = kQueueRetry;
+    int bh, qt;
+    prefill_unit<CAUSAL && !WINDOW>(p, (int)u, bh, qt);
+    // The home queue's next ticket is taken when this unit's tile loop ends,
+    // so the atomic's round trip overlaps the output epilogue (its wait would
+    // otherwise also wait for the epilogue's stores).
+    pp_unit<D, BN, CAUSAL, WINDOW, STAGES>(p, bh, qt, [&] {
+      if (threadIdx.x == 0 && !stealing) ahead = home_ticket();
+    });
+    __syncthreads();  // the LDS ring is free before the next tile's loads
+  }
+  if (threadIdx.x == 0 && atomicAdd(queue + 4 * kQueueXcds, 1u) == gridDim.x - 1) {
+    for (int x = 0; x <= kQueueXcds; ++x) atomicExch(queue + 4 * x, 0u);
+  }
+}
+
+template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>
 hipError_t launch_prefill_pp(const PrefillParams &p, int n_units, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_pp_kernel<D, BN, CAUSAL, WINDOW, STAGES>), dim3(n_units), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+// n_wg: workgroups of the grid (one per compute unit); queue: two zeroed uint32.
+template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>
+hipError_t launch_prefill_pp_queue(const PrefillParams &p, int n_units, int n_wg, uint32_t *queue,
+                                   hipStream_t stream) {
+  const int grid = n_units < n_wg ? n_units : n_wg;
+  hipLaunchKernelGGL((prefill_pp_queue_kernel<D, BN, CAUSAL, WINDOW, STAGES>), dim3(grid), dim3(512), 0, stream, p,
+                     queue);
   return hipGetLastError();
 }
 

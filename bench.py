@@ -85,7 +85,7 @@ class PrefillCase:
         a = afa._binding.prefill_args(s0["q"], s0["k"], s0["v"], self.out, self.lse, s0["sinks"], self.scale,
                                       w.causal, w.window)
         need = int(afa.load_library().attn_fwd_prefill_chunked_workspace_size(ctypes.byref(a)))
-        self.workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        self.workspace = torch.zeros(need, dtype=torch.uint8, device=dev) if need else None  # zeroed queue header
 
     def run(self, i: int):
         import attention_forward_attn_amd as afa

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 5
+#define ATTN_FWD_ABI_VERSION 6
 
 typedef enum {
   ATTN_OK = 0,
@@ -304,31 +304,47 @@ size_t attn_fwd_decode_workspace_size(int32_t B, int32_t h_q, int32_t d, int32_t
 attn_status attn_fwd_prefill(const attn_prefill_args *args, void *stream);
 
 /*
- * Chunked causal prefill: the same operation and arguments as
- * attn_fwd_prefill, scheduled for shapes with too few query tiles to fill the
- * chip evenly under a causal mask (head dim 512, the STAGE_D.md page's hd=512
- * case: 128-row tiles, one 8-wave workgroup per compute unit).  The visible key
- * range of each long query tile is cut into chunks whose length the host picks
- * by simulating the launch (units dealt to the 8 XCDs in grid order, each
- * starting on the first free compute unit of its XCD) for lengths around one
- * compute unit's share of the work and keeping the shortest makespan; each
- * chunk runs as its own work unit, longest first, and
- * writes its normalised partial output (rounded to bf16) and fp32 LSE into the
- * workspace; a second kernel merges the chunks of each row by their LSEs (the
- * per-segment merge of the same page's "O rescale (kt>0)" workaround).  A sink
- * enters the first chunk only.  Results equal attn_fwd_prefill's up to rounding
- * (the partials pass through bf16), not bit for bit.
+ * Scheduled prefill: the same operation and arguments as attn_fwd_prefill,
+ * with a caller workspace that lets the library schedule the work better.
+ *
+ * Chunked causal prefill (head dim 512, causal, no window, too few query tiles
+ * to fill the chip evenly; the STAGE_D.md page's hd=512 case: 128-row tiles,
+ * one 8-wave workgroup per compute unit).  The visible key range of each long
+ * query tile is cut into chunks whose length the host picks by simulating the
+ * launch (units dealt to the 8 XCDs in grid order, each starting on the first
+ * free compute unit of its XCD) for lengths around one compute unit's share of
+ * the work and keeping the shortest makespan; each chunk runs as its own work
+ * unit, longest first, and writes its normalised partial output (rounded to
+ * bf16) and fp32 LSE into the workspace; a second kernel merges the chunks of
+ * each row by their LSEs (the per-segment merge of the same page's "O rescale
+ * (kt>0)" workaround).  A sink enters the first chunk only.  Results equal
+ * attn_fwd_prefill's up to rounding (the partials pass through bf16), not bit
+ * for bit.
+ *
+ * Work-queue prefill (head dim 256): one workgroup per compute unit takes
+ * query tiles from counters in the workspace, one queue per XCD holding the
+ * tiles attn_fwd_prefill would place on that XCD (longest first under a plain
+ * causal mask); a workgroup drains its own XCD's queue and then takes what is
+ * left in the others, so XCDs that run at a lower clock take fewer tiles.
+ * Each tile is computed exactly as by attn_fwd_prefill: results are
+ * bit-identical.
+ *
+ * The workspace starts with a 256-byte header holding the work-queue counters
+ * (the chunk partials follow it).  The header must be zero before the first
+ * call that uses the workspace; every call leaves it zero, and a call that
+ * fails to launch does not touch it.  A workspace must not be shared by calls
+ * that may overlap, and must stay allocated until the stream has run the
+ * call's kernels.
  *
  * attn_fwd_prefill_chunked_workspace_size returns the bytes of workspace a
- * call with these arguments needs, or 0 when the call would not be chunked
- * (any head dim other than 512, no causal mask, a window, or enough query
- * tiles already) or the arguments are invalid; with 0, workspace may be NULL
- * and the call runs exactly attn_fwd_prefill.  Otherwise the workspace must be
- * at least that large and 256-byte aligned (ATTN_ERR_WORKSPACE /
- * ATTN_ERR_ALIGN), is owned by the caller, must stay allocated until the
- * stream has run both kernels, and must not be shared by calls that may
- * overlap.  The returned size depends on every field that shapes the work (b,
- * h_q, s_q, s_k, d, causal, window), so query it with the same arguments.
+ * call with these arguments needs, or 0 when neither schedule applies (head
+ * dim 64 or 128, head dim 512 without a causal mask, with a window or with
+ * enough query tiles already) or the arguments are invalid;
+ * with 0, workspace may be NULL and the call runs exactly attn_fwd_prefill.
+ * Otherwise the workspace must be at least that large and 256-byte aligned
+ * (ATTN_ERR_WORKSPACE / ATTN_ERR_ALIGN) and is owned by the caller.  The
+ * returned size depends on every field that shapes the work (b, h_q, s_q, s_k,
+ * d, causal, window), so query it with the same arguments.
  */
 size_t attn_fwd_prefill_chunked_workspace_size(const attn_prefill_args *args);
 attn_status attn_fwd_prefill_chunked(const attn_prefill_args *args, void *workspace, size_t workspace_bytes,

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     lib = afa.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
 
 
 def test_status_strings():
@@ -159,10 +159,10 @@ def test_prefill_chunked_plan_sizes():
     # tiles) get 2..4 chunks (parts: 4 heads x 23 tiles x 4 chunk slots x 128 rows).
     rows = 4 * 23 * 4 * 128
     assert _chunk_plan_rows(1, 4, 4096, 4096) == rows
-    assert size(wide_prefill()) == rows * 512 * 2 + rows * 4
+    assert size(wide_prefill()) == 256 + rows * 512 * 2 + rows * 4  # queue header, then the partials
     for s in (1024, 2048, 3000, 8192):
         r = _chunk_plan_rows(1, 4, s, s)
-        want = (r * 512 * 2 + 255) // 256 * 256 + r * 4 if r else 0
+        want = 256 + (r * 512 * 2 + 255) // 256 * 256 + r * 4 if r else 0
         assert size(wide_prefill(s=s)) == want, s
     # nothing to balance, or not a chunked shape: 0
     assert size(wide_prefill(causal=0)) == 0
@@ -185,6 +185,15 @@ def test_prefill_chunked_workspace_checks():
     assert lib.attn_fwd_prefill_chunked(ctypes.byref(a), ctypes.c_void_p(FAKE + 16), need, None) == 4
     e = wide_prefill(s=0)
     assert lib.attn_fwd_prefill_chunked(ctypes.byref(e), None, 0, None) == 0
+    # the work-queue shapes (d = 256, any mask) check their 256-byte header the same way
+    for d in (256,):
+        q = good_prefill(causal=1, s_q=1024, s_k=1024, d=d, q_ss=d, k_ss=d, v_ss=d, o_ss=d, q_sh=1024 * d,
+                         k_sh=1024 * d, v_sh=1024 * d, o_sh=1024 * d, q_sb=1024 * d, k_sb=1024 * d,
+                         v_sb=1024 * d, o_sb=1024 * d)
+        assert lib.attn_fwd_prefill_chunked_workspace_size(ctypes.byref(q)) == 256
+        assert lib.attn_fwd_prefill_chunked(ctypes.byref(q), None, 256, None) == 6
+        assert lib.attn_fwd_prefill_chunked(ctypes.byref(q), ctypes.c_void_p(FAKE), 255, None) == 6
+        assert lib.attn_fwd_prefill_chunked(ctypes.byref(q), ctypes.c_void_p(FAKE + 16), 256, None) == 4
 
 
 def test_prefill_null_args():

@@ -242,3 +242,36 @@ def test_prefill_full_size_sampled(name):
     l_g = lse[ib, ih, ii]
     check(o_g, l_g, o_ref, l_ref, name)
     assert torch.isfinite(out.float()).all()
+
+
+# Work-queue schedule of the d = 256 ping-pong kernel (per-XCD queues with stealing)
+QUEUE = [
+    # b, h_q, h_kv, s_q, s_k, d, causal, window
+    (1, 8, 8, 16384, 16384, 256, True, 0),  # the long-context workload: 512 query tiles
+    (1, 4, 2, 1000, 1200, 256, False, 0),
+    (1, 2, 2, 300, 300, 256, True, 0),      # fewer query tiles than compute units
+    (1, 8, 4, 2048, 2048, 256, True, 512),
+    (3, 5, 5, 777, 900, 256, True, 0),      # unit count not a multiple of 8: ragged per-XCD queues
+]
+
+
+@pytest.mark.parametrize("case", QUEUE, ids=[str(c) for c in QUEUE])
+def test_prefill_queue_bitwise(case):
+    """Each tile is computed as by the single-pass launch; the queue header is left zero."""
+    b, h_q, h_kv, s_q, s_k, d, causal, window = case
+    print(f"queued prefill case {case}", flush=True)
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(b, h_q, s_q, d, generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.randn(b, h_kv, s_k, d, generator=g).to(torch.bfloat16).to(DEV)
+    v = torch.randn(b, h_kv, s_k, d, generator=g).to(torch.bfloat16).to(DEV)
+    small = (q[:, :1, :200].contiguous(), k[:, :1, :230].contiguous(), v[:, :1, :230].contiguous())
+    ws = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
+    o0, l0 = afa.prefill(q, k, v, causal=causal, window=window, chunked=False)
+    s0, sl0 = afa.prefill(*small, causal=causal, window=window, chunked=False)
+    for rep in range(2):  # each call finds the header as the previous one left it
+        o1, l1 = afa.prefill(q, k, v, causal=causal, window=window, workspace=ws)
+        s1, sl1 = afa.prefill(*small, causal=causal, window=window, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o0) and torch.equal(l1, l0), f"rep {rep}"
+        assert torch.equal(s1, s0) and torch.equal(sl1, sl0), f"small, rep {rep}"
+        assert int(ws[:256].count_nonzero()) == 0
