@@ -275,3 +275,41 @@ def test_prefill_queue_bitwise(case):
         assert torch.equal(o1, o0) and torch.equal(l1, l0), f"rep {rep}"
         assert torch.equal(s1, s0) and torch.equal(sl1, sl0), f"small, rep {rep}"
         assert int(ws[:256].count_nonzero()) == 0
+
+
+def test_prefill_queue_graph_replays():
+    """The d = 256 work-queue prefill captured in a HIP graph: every replay equals the eager call.
+
+    The queue counters are reset by the kernel itself (no memset node), so each
+    replay starts from the zero header the previous one left; eager launches on
+    the same workspace run between the replays.
+    """
+    print("queued prefill under graph capture", flush=True)
+    g = torch.Generator().manual_seed(13)
+    b, h, s, d = 1, 4, 1536, 256
+    q = torch.randn(b, h, s, d, generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.randn(b, h, s, d, generator=g).to(torch.bfloat16).to(DEV)
+    v = torch.randn(b, h, s, d, generator=g).to(torch.bfloat16).to(DEV)
+    ref_o, ref_l = afa.prefill(q, k, v, causal=True, chunked=False)
+    ws = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(b, h, s, dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream, as torch recommends
+        afa.prefill(q, k, v, causal=True, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        afa.prefill(q, k, v, causal=True, out=out, lse=lse, workspace=ws)
+    for rep in range(3):
+        out.zero_()
+        lse.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep}"
+        assert int(ws[:256].count_nonzero()) == 0
+        eo, el = afa.prefill(q, k, v, causal=True, workspace=ws)  # eager work on the same workspace
+        torch.cuda.synchronize()
+        assert torch.equal(eo, ref_o) and torch.equal(el, ref_l)
