@@ -4,9 +4,16 @@
 
 namespace attn {
 
+// Waves per workgroup: the staged tiles allow one workgroup per compute unit,
+// so dQ runs 8 waves (two per SIMD); dK/dV keeps 4 (at 8 it spills).
+constexpr int BWD_NWQ = 8;
+constexpr int BWD_NWK = 4;
 hipError_t backward(int d, const BwdParams &p, bool causal, hipStream_t s) {
-  if (d == 64) return causal ? launch_backward<64, 64, true>(p, s) : launch_backward<64, 64, false>(p, s);
-  return causal ? launch_backward<128, 64, true>(p, s) : launch_backward<128, 64, false>(p, s);
+  if (d == 64)
+    return causal ? launch_backward<64, 64, true, BWD_NWQ, BWD_NWK>(p, s)
+                  : launch_backward<64, 64, false, BWD_NWQ, BWD_NWK>(p, s);
+  return causal ? launch_backward<128, 64, true, BWD_NWQ, BWD_NWK>(p, s)
+                : launch_backward<128, 64, false, BWD_NWQ, BWD_NWK>(p, s);
 }
 
 }  // namespace attn

@@ -2,11 +2,11 @@
 // forward's O and LSE (no window, no sink), deterministic (no atomics).
 //
 // Two kernels, both built from the forward's tile engine:
-//   * dQ (one workgroup per 128 query rows, 4 waves x 32 rows): the forward
+//   * dQ (one workgroup per NW x 32 query rows, NW waves x 32 rows): the forward
 //     layout S^T = K.Q^T (rows in lanes, keys in registers), plus
 //     dP^T = V.dO^T, then dQ^T += K^T.dS^T with dS = P * (dP - D).  It also
 //     writes D_i = sum_t dO[i,t] O[i,t] for the second kernel.
-//   * dK/dV (one workgroup per 128 keys of one kv head, 4 waves x 32 keys):
+//   * dK/dV (one workgroup per NW x 32 keys of one kv head, NW waves x 32 keys):
 //     the same shapes with the roles of queries and keys swapped: S = Q.K^T
 //     and dP = dO.V^T with keys in lanes and query rows in registers, then
 //     dV^T += dO^T.P and dK^T += Q^T.dS, summed over every query head of the
@@ -70,11 +70,11 @@ __device__ __forceinline__ void store_rows(uint16_t *op, const f32x16 (&a)[NDB],
 
 // ---------------------------------------------------------------------------
 // dQ (and D).
-template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int BN, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dq_kernel(BwdParams p) {
-  using T = Tile<D, 4, BN>;
-  constexpr int BM = 128;
+  using T = Tile<D, NW, BN>;
+  constexpr int BM = 32 * NW;
   constexpr int STAGE = 3 * T::TILE_BYTES;  // [K, row swizzle][K, transpose swizzle][V, row swizzle]
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE / 2];
 
@@ -171,11 +171,11 @@ void bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dK, dV.  Reads D written by bwd_dq_kernel.
-template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int BN, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dkdv_kernel(BwdParams p) {
-  using T = Tile<D, 4, BN>;  // here the streamed "keys" of the engine are query rows
-  constexpr int BK = 128;    // keys per workgroup
+  using T = Tile<D, NW, BN>;  // here the streamed "keys" of the engine are query rows
+  constexpr int BK = 32 * NW;  // keys per workgroup
   // [Q row][Q transpose][dO row][dO transpose][LSE of the BN rows][D of the BN rows]
   constexpr int STAGE = 4 * T::TILE_BYTES + 2 * BN * 4;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE / 2];
@@ -293,16 +293,20 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-template <int D, int BN, bool CAUSAL>
+// NWQ waves per dQ workgroup (NWQ x 32 query rows), NWK per dK/dV workgroup
+// (NWK x 32 keys).
+template <int D, int BN, bool CAUSAL, int NWQ, int NWK>
 hipError_t launch_backward(const BwdParams &p, hipStream_t stream) {
-  const int n_qt = (p.s_q + 127) / 128, n_kt = (p.s_k + 127) / 128;
+  const int n_qt = (p.s_q + 32 * NWQ - 1) / (32 * NWQ), n_kt = (p.s_k + 32 * NWK - 1) / (32 * NWK);
   if (n_qt > 0) {  // dQ (zero when there are no keys) and D
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL>), dim3(p.b * p.h_q * n_qt), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL, NWQ>), dim3(p.b * p.h_q * n_qt), dim3(NWQ * 64), 0, stream,
+                       p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (n_kt > 0) {  // dK, dV (zero when there are no rows)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BN, CAUSAL>), dim3(p.b * p.h_kv * n_kt), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BN, CAUSAL, NWK>), dim3(p.b * p.h_kv * n_kt), dim3(NWK * 64), 0,
+                       stream, p);
     return hipGetLastError();
   }
   return hipSuccess;
