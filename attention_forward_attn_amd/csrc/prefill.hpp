@@ -551,52 +551,60 @@ void prefill_pp_kernel(PrefillParams p) {
 // Work-queue form of the ping-pong prefill.  The grid has one workgroup per
 // compute unit.  The units are those of the fixed placement (unit v belongs to
 // XCD v % 8, which keeps a kv head's query tiles on one XCD and its K/V in one
-// L2; prefill_unit), held in one queue per XCD in the same order (longest
-// first under a plain causal mask): queue x hands out units x, x + 8, x + 16,
-// ... through the ticket counter queue[4x].  A workgroup first drains the
-// queue of the XCD it runs on (read from the XCC_ID hardware register) and
-// then takes what is left in the others, so when the XCDs of a chip settle at
-// different clocks the fast ones finish the slow ones' last (shortest) tiles
-// instead of waiting for them.  Tickets are taken with returning atomics, so a
-// workgroup increments the exit counter (queue[32]) only after its failing
-// ticket of every queue has been counted; the workgroup that exits last
-// therefore sees no ticket after it and resets all counters to zero for the
-// next launch.  queue must be zero before the first launch, and launches
-// sharing a queue must not overlap.
+// L2; prefill_unit), held in one double-ended queue per XCD in the same order
+// (longest first under a plain causal mask): queue x holds units x, x + 8,
+// x + 16, ...  A workgroup takes units from the front of the queue of the XCD
+// it runs on (read from the XCC_ID hardware register); once that is empty it
+// takes from the back of the others, i.e. their shortest units, so when the
+// XCDs of a chip settle at different clocks the fast ones finish the slow
+// ones' last tiles instead of waiting for them, without taking the long units
+// the owners would run next.  Each queue is one 64-bit word, front count in
+// the low half and back count in the high half: a claim is valid when
+// front + back was below the queue's size at its atomic, so front and back
+// claims never overlap.  Claims are returning atomics, so a workgroup
+// increments the exit counter only after its last claim has been counted; the
+// workgroup that exits last therefore sees no claim after it and resets every
+// counter to zero for the next launch.  queue must be zero before the first
+// launch, and launches sharing a queue must not overlap.
 constexpr int kQueueXcds = 8;
+constexpr int kQueueExit = 32;                 // uint32 index of the exit counter (after 8 x 16 bytes)
 constexpr uint32_t kQueueDone = 0xffffffffu;  // no unit left in any queue
-constexpr uint32_t kQueueRetry = 0xfffffffeu; // lost a race for a queue's last unit: look again
+constexpr uint32_t kQueueRetry = 0xfffffffeu; // none taken: look again (from the other queues)
 template <int D, int BN, bool CAUSAL, bool WINDOW, int STAGES>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_pp_queue_kernel(PrefillParams p, uint32_t *queue) {
   __shared__ uint32_t s_unit;
+  unsigned long long *q64 = reinterpret_cast<unsigned long long *>(queue);  // queue x at q64[2x]
   const uint32_t n_units = (uint32_t)(p.b * p.h_q * p.n_qtiles);
   const int home = __builtin_amdgcn_s_getreg((31 << 11) | 20) & (kQueueXcds - 1);  // XCC_ID
+  auto qsize = [&](int x) -> uint32_t { return n_units > (uint32_t)x ? (n_units - 1 - x) / kQueueXcds + 1 : 0; };
   bool stealing = false;  // the home queue is empty
   // Thread 0 only: the next unit, kQueueRetry when none has been taken yet.
   uint32_t ahead = kQueueRetry;
   auto home_ticket = [&]() -> uint32_t {
-    const uint64_t v = (uint64_t)home + (uint64_t)kQueueXcds * atomicAdd(queue + 4 * home, 1u);
-    return v < n_units ? (uint32_t)v : kQueueRetry;
+    const unsigned long long w = atomicAdd(q64 + 2 * home, 1ull);
+    const uint32_t f = (uint32_t)w, b = (uint32_t)(w >> 32);
+    return (uint64_t)f + b < qsize(home) ? (uint32_t)home + kQueueXcds * f : kQueueRetry;
   };
-  // A unit from another queue that still has some (all eight counters read in
-  // one round trip; a queue that looks empty is not touched); kQueueRetry
-  // after a lost race for a last unit, kQueueDone when every queue is empty.
+  // The back (shortest) unit of another queue that still has some (all eight
+  // words read in one round trip; a queue that looks empty is not touched);
+  // kQueueRetry after a lost race, kQueueDone when every queue is empty.
   auto steal_ticket = [&]() -> uint32_t {
-    uint32_t c[kQueueXcds];
+    unsigned long long c[kQueueXcds];
 #pragma unroll
     for (int j = 0; j < kQueueXcds; ++j)
-      c[j] = __hip_atomic_load(queue + 4 * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      c[j] = __hip_atomic_load(q64 + 2 * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int x = -1;
 #pragma unroll
     for (int j = 1; j <= kQueueXcds; ++j) {
       const int y = (home + j) & (kQueueXcds - 1);
-      const uint32_t size = n_units > (uint32_t)y ? (n_units - 1 - y) / kQueueXcds + 1 : 0;
-      if (x < 0 && c[y] < size) x = y;
+      if (x < 0 && (uint64_t)(uint32_t)c[y] + (uint32_t)(c[y] >> 32) < qsize(y)) x = y;
     }
     if (x < 0) return kQueueDone;
-    const uint64_t v = (uint64_t)x + (uint64_t)kQueueXcds * atomicAdd(queue + 4 * x, 1u);
-    return v < n_units ? (uint32_t)v : kQueueRetry;
+    const unsigned long long w = atomicAdd(q64 + 2 * x, 1ull << 32);
+    const uint32_t f = (uint32_t)w, b = (uint32_t)(w >> 32);
+    const uint32_t size = qsize(x);
+    return (uint64_t)f + b < size ? (uint32_t)x + kQueueXcds * (size - 1 - b) : kQueueRetry;
   };
   for (;;) {
     if (threadIdx.x == 0) s_unit = ahead != kQueueRetry ? ahead : stealing ? steal_ticket() : home_ticket();
@@ -611,7 +619,7 @@ void prefill_pp_queue_kernel(PrefillParams p, uint32_t *queue) {
     ahead = kQueueRetry;
     int bh, qt;
     prefill_unit<CAUSAL && !WINDOW>(p, (int)u, bh, qt);
-    // The home queue's next ticket is taken when this unit's tile loop ends,
+    // The home queue's next unit is claimed when this unit's tile loop ends,
     // so the atomic's round trip overlaps the output epilogue (its wait would
     // otherwise also wait for the epilogue's stores).
     pp_unit<D, BN, CAUSAL, WINDOW, STAGES>(p, bh, qt, [&] {
@@ -619,8 +627,9 @@ void prefill_pp_queue_kernel(PrefillParams p, uint32_t *queue) {
     });
     __syncthreads();  // the LDS ring is free before the next tile's loads
   }
-  if (threadIdx.x == 0 && atomicAdd(queue + 4 * kQueueXcds, 1u) == gridDim.x - 1) {
-    for (int x = 0; x <= kQueueXcds; ++x) atomicExch(queue + 4 * x, 0u);
+  if (threadIdx.x == 0 && atomicAdd(queue + kQueueExit, 1u) == gridDim.x - 1) {
+    for (int x = 0; x < kQueueXcds; ++x) atomicExch(q64 + 2 * x, 0ull);
+    atomicExch(queue + kQueueExit, 0u);
   }
 }
 
