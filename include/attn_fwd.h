@@ -324,8 +324,9 @@ attn_status attn_fwd_prefill(const attn_prefill_args *args, void *stream);
  * Work-queue prefill (head dim 256): one workgroup per compute unit takes
  * query tiles from counters in the workspace, one queue per XCD holding the
  * tiles attn_fwd_prefill would place on that XCD (longest first under a plain
- * causal mask); a workgroup drains its own XCD's queue and then takes what is
- * left in the others, so XCDs that run at a lower clock take fewer tiles.
+ * causal mask); a workgroup takes from the front of its own XCD's queue and
+ * then from the back (the shortest tiles) of the others, so XCDs that run at a
+ * lower clock take fewer tiles.
  * Each tile is computed exactly as by attn_fwd_prefill: results are
  * bit-identical.
  *
