@@ -689,12 +689,13 @@ attn_status attn_combine(const attn_combine_args *a, void *stream) {
 }  // extern "C"
 
 namespace attn {
-// d = 128 and 256 run the 8-wave ping-pong kernel on 256 rows, except that a
-// sliding window at d = 128 keeps the 4-wave kernel on 128 rows: with the
-// window's two masked edges, the smaller tile wastes less of each tile range.
+// d = 128 and 256 run the 8-wave ping-pong kernel on 256 rows and d = 64 the
+// 8-wave single-group kernel on 256 rows, except that a sliding window at
+// d = 64 and 128 keeps the 4-wave kernel on 128 rows: with the window's two
+// masked edges, the smaller tile wastes less of each tile range.
 int prefill_block_rows(int d, int mask) {
   switch (d) {
-    case 64: return 128;
+    case 64: return mask == kMaskCausalWindow ? 128 : 256;
     case 128: return mask == kMaskCausalWindow ? 128 : 256;
     case 256: return 256;
     case 512: return 128;
