@@ -150,13 +150,15 @@ namespace {
 // the merge, measured in key tiles (with it the simulated makespan tracked the
 // measured time of eight chunk lengths on the b1 h4 s4096 workload to within
 // 1 us).  Candidates run from three quarters to twice the even share of the
-// work per compute unit (never below kMinChunkTiles); ties go to the longer
-// chunk (fewer partials to merge).
+// work per compute unit (never below kMinChunkTiles), at most
+// kMaxChunkCandidates of them evenly spaced, so a first call plans in well
+// under a millisecond; ties go to the longer chunk (fewer partials to merge).
 constexpr int kChunkTargetCUs = 256;
 constexpr int kXcds = 8;
 constexpr int kCusPerXcd = 32;
 constexpr int kMinChunkTiles = 8;
 constexpr int64_t kUnitFixedTiles = 10;
+constexpr int64_t kMaxChunkCandidates = 64;  // lengths simulated at most (evenly spaced)
 
 struct ChunkPlan {
   int chunk_tiles = 0, qt0 = 0, max_chunks = 0, n_rank = 0;
@@ -237,7 +239,8 @@ bool plan_chunks(const attn_prefill_args *a, ChunkPlan &pl) {
   if (c0 < tmax && nq < (1 << 23)) {
     int64_t best_c = 0, best_mk = 0;
     const int64_t lo = std::max<int64_t>(kMinChunkTiles, c0 * 3 / 4), hi = std::min(tmax - 1, 2 * c0);
-    for (int64_t c = lo; c <= hi; ++c) {
+    const int64_t step = std::max<int64_t>(1, (hi - lo) / (kMaxChunkCandidates - 1));
+    for (int64_t c = lo; c <= hi; c += step) {
       if (!chunk_units(T, c, es) || (int64_t)es.size() * bh > kMaxIndex) continue;
       const int64_t mk = chunk_makespan(es, bh);
       if (best_c == 0 || mk <= best_mk) best_c = c, best_mk = mk, best = es;

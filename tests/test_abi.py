@@ -134,7 +134,8 @@ def _chunk_plan_rows(b, h, s_q, s_k, bm=128, bn=32, fixed=10, xcds=8, cus=32, ta
     if c0 >= tmax:
         return 0
     best = None
-    for c in range(max(min_tiles, c0 * 3 // 4), min(tmax - 1, 2 * c0) + 1):
+    lo, hi = max(min_tiles, c0 * 3 // 4), min(tmax - 1, 2 * c0)
+    for c in range(lo, hi + 1, max(1, (hi - lo) // 63)):
         units = sorted(((min(c, T[qt] - ch * c), qt) for qt in range(nq) for ch in range(-(-T[qt] // c))),
                        key=lambda u: (-u[0], -u[1]))
         heaps = [[0] * cus for _ in range(xcds)]
@@ -160,7 +161,7 @@ def test_prefill_chunked_plan_sizes():
     rows = 4 * 23 * 4 * 128
     assert _chunk_plan_rows(1, 4, 4096, 4096) == rows
     assert size(wide_prefill()) == 256 + rows * 512 * 2 + rows * 4  # queue header, then the partials
-    for s in (1024, 2048, 3000, 8192):
+    for s in (1024, 2048, 3000, 8192, 16384):  # at s = 16384 the candidates are spaced
         r = _chunk_plan_rows(1, 4, s, s)
         want = 256 + (r * 512 * 2 + 255) // 256 * 256 + r * 4 if r else 0
         assert size(wide_prefill(s=s)) == want, s
