@@ -15,7 +15,10 @@ not read K/V out of the 256 MB last-level cache.
 bytes: K and V of every cached token plus Q, O and LSE) is reported beside it.
 Kernel times come from HIP events recorded on the stream the kernels run on:
 the K timed steps run as K prefill launches and then K decode passes, each
-block between two events (see timed()).
+block between two events (see timed()).  A separate pass afterwards brackets
+each of up to 100 further launches with events of its own and reports the
+median, p10 and p90 of single launches beside the block average
+(launch_spread()).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
 """
@@ -198,6 +201,28 @@ def timed(cases, steps: int, warmup: int):
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     per = [evs[j].elapsed_time(evs[j + 1]) / steps for j in range(len(cases))]
     return per, wall_ms
+
+
+def launch_spread(case, n: int, start: int):
+    """Per-launch times (ms) of n launches, each between two events of its own.
+
+    Run after the timed block, outside it: events around every launch keep the
+    launches from running back to back, so these figures describe the spread
+    of single launches (median, p10, p90), while the block average is the
+    throughput.
+    """
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        case.run(start + i)
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    pick = lambda q: t[min(n - 1, int(round(q * (n - 1))))]
+    return {"launches": n, "median_ms": round(pick(0.5), 4), "p10_ms": round(pick(0.1), 4),
+            "p90_ms": round(pick(0.9), 4)}
 
 
 def kernel_source_hash(unit: str) -> str:
@@ -455,6 +480,9 @@ def main():
     (pre_ms, dec_ms), wall_ms = timed([pc, dc], args.steps, args.warmup)
     pre = roofline_prefill(pc.flops, pre_ms, recorded_traffic(*PREFILL_PROFILE))
     dec = roofline_decode(dc.bytes, dec_ms, recorded_traffic(*DECODE_PROFILES))
+    n_spread = max(10, min(args.steps, 100))
+    pre_spread = launch_spread(pc, n_spread, args.warmup + args.steps)
+    dec_spread = launch_spread(dc, n_spread, args.warmup + args.steps)
     line = {
         "metric": "attn fwd TFLOPS (bf16, causal-adjusted) + decode HBM GB/s, 1xMI355X",
         "value": pre["achieved"],
@@ -476,8 +504,9 @@ def main():
                    "decode_tokens": dc.total},
         "prefill_ms": round(pre_ms, 4),
         "roofline": pre,
+        "prefill_launch_spread": pre_spread,
         "decode": {"value": dec["achieved"], "unit": "GB/s", "ms": round(dec_ms, 4),
-                   "bytes": dc.bytes, "roofline": dec},
+                   "bytes": dc.bytes, "roofline": dec, "launch_spread": dec_spread},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(wp)
