@@ -18,7 +18,10 @@ the K timed steps run as K prefill launches and then K decode passes, each
 block between two events (see timed()).  A separate pass afterwards brackets
 each of up to 100 further launches with events of its own and reports the
 median, p10 and p90 of single launches beside the block average
-(launch_spread()).
+(launch_spread()), and a last pass of about one second of back-to-back
+prefill launches reads the GFX clock through amdsmi, so that the prefill
+fraction is also given against the bf16 peak at the clock the chip ran at
+(sampled_clock()).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
 """
@@ -223,6 +226,94 @@ def launch_spread(case, n: int, start: int):
     pick = lambda q: t[min(n - 1, int(round(q * (n - 1))))]
     return {"launches": n, "median_ms": round(pick(0.5), 4), "p10_ms": round(pick(0.1), 4),
             "p90_ms": round(pick(0.9), 4)}
+
+
+def _smi_handle(dev_index: int):
+    """amdsmi handle of torch device dev_index, matched by PCI domain and bus."""
+    import amdsmi
+    import torch
+
+    props = torch.cuda.get_device_properties(dev_index)
+    handles = amdsmi.amdsmi_get_processor_handles()
+    for hd in handles:
+        bdf = amdsmi.amdsmi_get_gpu_device_bdf(hd)  # "dddd:bb:dd.f"
+        dom, bus = bdf.split(":")[:2]
+        if int(dom, 16) == props.pci_domain_id and int(bus, 16) == props.pci_bus_id:
+            return hd
+    return handles[0] if len(handles) == 1 else None
+
+
+def sampled_clock(case, start: int, ms_per_launch: float, seconds: float = 1.0):
+    """GFX clock while the case runs back to back, read through amdsmi.
+
+    A pass of its own after the timed block: about `seconds` of back-to-back
+    launches while a thread reads the device's clock every 10 ms (per XCD from
+    the GPU metrics table where it lists them, else the GFX clock).  Samples
+    from the second half of the pass (steady clock) are kept; the median over
+    them and over the XCDs is the sampled clock.  The bf16 dense peak is linear
+    in the clock (4096 flop per CU and cycle), so the peak at the sampled clock
+    is 2516.6 x clk / 2400 TFLOP/s.  Returns {"error": ...} when amdsmi cannot
+    read the clock; the timed figures do not depend on this pass.
+    """
+    import threading
+
+    import torch
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+    except Exception as e:  # no amdsmi or no driver access
+        return {"error": f"amdsmi unavailable: {e}"}
+    try:
+        hd = _smi_handle(torch.cuda.current_device())
+        if hd is None:
+            return {"error": "no amdsmi device matches the torch device"}
+
+        def read():
+            try:
+                clks = amdsmi.amdsmi_get_gpu_metrics_info(hd).get("current_gfxclks")
+                if isinstance(clks, list):
+                    xs = [c for c in clks if isinstance(c, int) and 0 < c < 10000]
+                    if xs:
+                        return xs
+            except Exception:
+                pass
+            c = amdsmi.amdsmi_get_clock_info(hd, amdsmi.AmdSmiClkType.GFX).get("clk")
+            return [c] if isinstance(c, int) else []
+
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                samples.append((time.perf_counter(), read()))
+                stop.wait(0.01)
+
+        n = max(100, int(seconds / (ms_per_launch * 1e-3)))
+        th = threading.Thread(target=sampler, daemon=True)
+        t0 = time.perf_counter()
+        th.start()
+        for i in range(n):
+            case.run(start + i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stop.set()
+        th.join()
+        kept = [xs for t, xs in samples if t >= t0 + 0.5 * (t1 - t0) and xs]
+        if not kept:
+            return {"error": "no clock samples while the kernels ran"}
+        per_xcd = [sorted(col)[len(col) // 2] for col in zip(*kept)] if len({len(x) for x in kept}) == 1 else []
+        flat = sorted(c for xs in kept for c in xs)
+        mhz = flat[len(flat) // 2]
+        return {"source": "amdsmi", "launches": n, "samples": len(kept), "gfx_mhz_median": mhz,
+                "gfx_mhz_per_xcd": per_xcd, "peak_at_clock": round(PEAK_BF16_TFLOPS * mhz / 2400.0, 1)}
+    except Exception as e:
+        return {"error": f"clock sampling failed: {e}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def kernel_source_hash(unit: str) -> str:
@@ -483,6 +574,9 @@ def main():
     n_spread = max(10, min(args.steps, 100))
     pre_spread = launch_spread(pc, n_spread, args.warmup + args.steps)
     dec_spread = launch_spread(dc, n_spread, args.warmup + args.steps)
+    clock = sampled_clock(pc, args.warmup + args.steps + n_spread, pre_ms)
+    if "peak_at_clock" in clock:
+        clock["frac_at_clock"] = round(pre["achieved"] / clock["peak_at_clock"], 4)
     line = {
         "metric": "attn fwd TFLOPS (bf16, causal-adjusted) + decode HBM GB/s, 1xMI355X",
         "value": pre["achieved"],
@@ -505,6 +599,7 @@ def main():
         "prefill_ms": round(pre_ms, 4),
         "roofline": pre,
         "prefill_launch_spread": pre_spread,
+        "prefill_clock": clock,
         "decode": {"value": dec["achieved"], "unit": "GB/s", "ms": round(dec_ms, 4),
                    "bytes": dc.bytes, "roofline": dec, "launch_spread": dec_spread},
     }
