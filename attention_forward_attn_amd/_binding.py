@@ -183,9 +183,39 @@ def _stream(stream):
 
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, ctypes.c_void_p):
+        return stream
     if hasattr(stream, "cuda_stream"):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def _on_stream(fn):
+    """Run a binding call with its ``stream`` as torch's current stream.
+
+    Outputs and workspaces the call allocates are then allocated on the stream
+    the kernels run on, so the caching allocator orders any reuse of that
+    memory after those kernels, and a workspace zeroed here is zeroed on that
+    stream before the kernels read it.  The inputs must already be ready on
+    that stream (as with any torch op issued there).  ``stream`` may be a
+    torch stream, a raw hipStream_t handle (int) or None (torch's current
+    stream).
+    """
+    import functools
+
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        import torch
+
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        if not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(stream.cuda_stream if hasattr(stream, "cuda_stream")
+                                               else int(stream))
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+
+    return call
 
 
 def _require_cuda_bf16(name, t, ndim):
@@ -222,6 +252,7 @@ def prefill_args(q, k, v, out, lse, sinks, scale, causal, window) -> PrefillArgs
     return a
 
 
+@_on_stream
 def prefill(q, k, v, *, scale: float | None = None, causal: bool = False, window: int = 0,
             sinks=None, out=None, lse=None, return_lse: bool = True, chunked: bool = True,
             workspace=None, stream=None):
@@ -276,6 +307,7 @@ def decode_workspace_size(B: int, h_q: int, d: int, max_kv_len: int, split_size:
     return int(load_library().attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
 
 
+@_on_stream
 def decode(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = None, sinks=None,
            split_size: int = 512, workspace=None, out=None, lse=None, return_lse: bool = True,
            stream=None):
@@ -326,6 +358,7 @@ def decode(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = 
     return out, lse
 
 
+@_on_stream
 def decode_paged(q, k_cache, v_cache, block_table, kv_len, max_kv_len: int, *, scale: float | None = None,
                  sinks=None, split_size: int = 512, workspace=None, out=None, lse=None,
                  return_lse: bool = True, stream=None):
@@ -383,6 +416,7 @@ def decode_paged(q, k_cache, v_cache, block_table, kv_len, max_kv_len: int, *, s
     return out, lse
 
 
+@_on_stream
 def decode_fp8(q, k8, v8, k_scale, v_scale, kv_start, kv_len, max_kv_len: int, *, scale: float | None = None,
                sinks=None, split_size: int = 512, workspace=None, out=None, lse=None,
                return_lse: bool = True, stream=None):
@@ -443,6 +477,7 @@ def backward_workspace_size(b: int, h_q: int, s_q: int) -> int:
     return int(load_library().attn_bwd_workspace_size(b, h_q, s_q))
 
 
+@_on_stream
 def backward(q, k, v, o, d_o, lse, *, scale: float | None = None, causal: bool = False, dq=None, dk=None,
              dv=None, workspace=None, stream=None):
     """dQ, dK, dV of the prefill for an incoming gradient d_o, from the forward's o and lse.
@@ -492,6 +527,7 @@ def backward(q, k, v, o, d_o, lse, *, scale: float | None = None, causal: bool =
     return dq, dk, dv
 
 
+@_on_stream
 def combine(o_parts, lse_parts, *, out=None, lse=None, return_lse: bool = True, stream=None):
     """Merge partial results over disjoint key sets: o_parts fp32 [n, rows, d], lse_parts fp32 [n, rows]."""
     import torch

@@ -548,6 +548,10 @@ attn_status attn_fwd_decode_paged(const attn_decode_paged_args *a, void *workspa
   if (ps < 16 || (ps & (ps - 1)) != 0 || ps > a->split_size || a->split_size / ps > 64)
     return fail(ATTN_ERR_SHAPE,
                 "page_size must be a power of two in [16, split_size] with at most 64 pages per split (got %d)", ps);
+  // Every split must start on a page boundary: the kernel maps key j of a
+  // split to slot j % page_size of the split's (j / page_size)-th page.
+  if (a->split_size % ps != 0)
+    return fail(ATTN_ERR_SHAPE, "split_size (%d) must be a multiple of page_size (%d)", a->split_size, ps);
   if (a->n_pages < 1) return fail(ATTN_ERR_SHAPE, "n_pages must be >= 1");
   const int64_t max_pages = ((int64_t)a->max_kv_len + ps - 1) / ps;
   if (a->bt_stride < max_pages)

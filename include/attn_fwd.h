@@ -165,7 +165,8 @@ typedef struct {
  *       indices in [0, n_pages); entries past those are not read.  A page index
  *       outside [0, n_pages) is never dereferenced: its tokens read as zeros
  *       (a wrong result, not a fault).
- * page_size: a power of two in [16, split_size] with split_size/page_size <= 64;
+ * page_size: a power of two in [16, split_size] that divides split_size, with
+ *       split_size/page_size <= 64 (so every split starts on a page boundary);
  *       bt_stride >= ceil(max_kv_len/page_size).
  * Other fields, the workspace (attn_fwd_decode_workspace_size with the same
  * sizes), its ownership and the supported sizes are those of attn_fwd_decode.

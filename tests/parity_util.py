@@ -6,6 +6,9 @@ and max |LSE_gpu - LSE_oracle| <= 1e-3, with -inf LSE required to match exactly.
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -44,28 +47,33 @@ def cosine(a, b):
     return float(a @ b / max(np.linalg.norm(a) * np.linalg.norm(b), 1e-300))
 
 
-def oracle_rows(q, k, v, scale, causal, window, sinks, picks):
-    """Oracle O and LSE of selected query rows (b, h, i) of a prefill problem.
+def oracle_full(q, k, v, scale, causal, window, sinks, workers=None):
+    """Oracle O and LSE of every row of a prefill problem, one (batch, head) slice per task.
 
-    A row's result only depends on its own visible keys, so each picked row is
-    an s_q = 1 problem over the keys up to its (bottom-right) diagonal; with
-    s_q = 1 the causal/window rule then keeps exactly the row's visible keys.
+    The slices are independent problems, so each is handed to
+    ``oracle.attention_ref`` unchanged; the tasks run on a thread pool (numpy
+    releases the interpreter lock inside its kernels) with one BLAS thread per
+    worker.
     """
+    from threadpoolctl import threadpool_limits
+
     b, h_q, s_q, d = q.shape
-    h_kv, s_k = k.shape[1], k.shape[2]
-    ratio = h_q // h_kv
-    off = s_k - s_q
-    o_out = np.zeros((len(picks), d))
-    l_out = np.zeros(len(picks))
-    sig_all = None if sinks is None else sinks.detach().cpu().double().numpy()
-    for n, (bi, h, i) in enumerate(picks):
+    ratio = h_q // k.shape[1]
+    qn, kn, vn = (t.detach().cpu().to(torch.float64).numpy() for t in (q, k, v))
+    sig = None if sinks is None else sinks.detach().cpu().double().numpy()
+    o_out = np.empty((b, h_q, s_q, d))
+    l_out = np.empty((b, h_q, s_q))
+
+    def one(bh):
+        bi, h = divmod(bh, h_q)
         g = h // ratio
-        hi = s_k if not causal else max(0, min(s_k, i + off + 1))
-        qi = q[bi, h, i:i + 1][None, None]
-        kk = k[bi, g, :hi][None, None]
-        vv = v[bi, g, :hi][None, None]
-        sig = None if sig_all is None else sig_all[h:h + 1]
-        o, l = oracle.attention_ref(qi, kk, vv, scale, causal=causal, window=window, sinks=sig)
-        o_out[n] = o[0, 0, 0]
-        l_out[n] = l[0, 0, 0]
+        o, l = oracle.attention_ref(qn[bi:bi + 1, h:h + 1], kn[bi:bi + 1, g:g + 1], vn[bi:bi + 1, g:g + 1],
+                                    scale, causal=causal, window=window,
+                                    sinks=None if sig is None else sig[h:h + 1])
+        o_out[bi, h] = o[0, 0]
+        l_out[bi, h] = l[0, 0]
+
+    workers = workers or min(16, os.cpu_count() or 1)
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, range(b * h_q)))
     return o_out, l_out

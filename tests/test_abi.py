@@ -281,6 +281,8 @@ PAGED_BAD = [
     ("page 48", dict(page_size=48), 2),
     ("page above split", dict(page_size=1024), 2),
     ("65 pages per split", dict(split_size=1024 + 64, page_size=16), 2),
+    ("split 384, page 256", dict(split_size=384, page_size=256), 2),  # splits would start mid-page
+    ("split 192, page 128", dict(split_size=192, page_size=128), 2),
     ("no pages", dict(n_pages=0), 2),
     ("table too narrow", dict(bt_stride=127), 3),
     ("odd page stride", dict(k_ps=12), 3),

@@ -157,6 +157,7 @@ PAGED = [
     (4, 8, 8, 128, 0, 300, 256, 256),      # empty sequences possible
     (3, 256, 2, 128, 100, 1030, 128, 1024),
     (2, 32, 1, 128, 200, 2100, 16, 1024),  # 64 pages per split
+    (3, 64, 1, 128, 1, 1500, 128, 384),    # three pages per split (split not a power of two)
 ]
 
 
