@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     combine,
     decode,
     decode_fp8,
+    decode_noalloc,
     decode_paged,
     decode_workspace_size,
     load_library,

@@ -144,6 +144,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_void_p]
     lib.attn_fwd_decode.restype = ctypes.c_int
+    lib.attn_fwd_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+    lib.attn_fwd_decode_noalloc.restype = ctypes.c_int
     lib.attn_fwd_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p]
     lib.attn_fwd_decode_paged.restype = ctypes.c_int
@@ -307,20 +309,10 @@ def decode_workspace_size(B: int, h_q: int, d: int, max_kv_len: int, split_size:
     return int(load_library().attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
 
 
-@_on_stream
-def decode(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = None, sinks=None,
-           split_size: int = 512, workspace=None, out=None, lse=None, return_lse: bool = True,
-           stream=None):
-    """Single-token decode over a per-sequence contiguous KV cache (split-KV + LSE merge).
-
-    q: bf16 [B, h_q, d]; k, v: bf16 [T, h_kv, d] (token-major cache; any token
-    and head strides with a unit head-dim stride); kv_start: int64 [B];
-    kv_len: int32 [B]; max_kv_len: host upper bound on kv_len.
-    Returns (O bf16 [B, h_q, d], LSE fp32 [B, h_q] or None).
-    """
+def _decode_args(q, k, v, kv_start, kv_len, max_kv_len, scale, sinks, split_size, out, lse, return_lse):
+    """Check the tensors of a contiguous-cache decode and fill the C argument struct (and outputs)."""
     import torch
 
-    lib = load_library()
     _require_cuda_bf16("q", q, 3)
     _require_cuda_bf16("k", k, 3)
     _require_cuda_bf16("v", v, 3)
@@ -330,9 +322,6 @@ def decode(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = 
     h_kv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = int(lib.attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, h_q, d), dtype=torch.bfloat16, device=q.device)
     if lse is None and return_lse:
@@ -353,8 +342,45 @@ def decode(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = 
     a.o_sb, a.o_sh = out.stride(0), out.stride(1)
     a.lse_sb = lse.stride(0) if lse is not None else 0
     a.scale = scale
+    return a, out, lse
+
+
+@_on_stream
+def decode(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = None, sinks=None,
+           split_size: int = 512, workspace=None, out=None, lse=None, return_lse: bool = True,
+           stream=None):
+    """Single-token decode over a per-sequence contiguous KV cache (split-KV + LSE merge).
+
+    q: bf16 [B, h_q, d]; k, v: bf16 [T, h_kv, d] (token-major cache; any token
+    and head strides with a unit head-dim stride); kv_start: int64 [B];
+    kv_len: int32 [B]; max_kv_len: host upper bound on kv_len.
+    Returns (O bf16 [B, h_q, d], LSE fp32 [B, h_q] or None).
+    """
+    import torch
+
+    lib = load_library()
+    a, out, lse = _decode_args(q, k, v, kv_start, kv_len, max_kv_len, scale, sinks, split_size, out, lse,
+                               return_lse)
+    need = int(lib.attn_fwd_decode_workspace_size(a.B, a.h_q, a.d, a.max_kv_len, a.split_size))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check(lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+@_on_stream
+def decode_noalloc(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = None, sinks=None,
+                   split_size: int = 512, out=None, lse=None, return_lse: bool = True, stream=None):
+    """decode() through attn_fwd_decode_noalloc: no workspace, the library's fixed scratch region.
+
+    Calls that may overlap on one GPU race (they share the region).  The
+    outputs are allocated here unless ``out`` (and ``lse``) are given.
+    """
+    lib = load_library()
+    a, out, lse = _decode_args(q, k, v, kv_start, kv_len, max_kv_len, scale, sinks, split_size, out, lse,
+                               return_lse)
+    _check(lib.attn_fwd_decode_noalloc(ctypes.byref(a), _stream(stream)))
     return out, lse
 
 

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/attn_fwd.h"
 #include "kernels.hpp"
@@ -438,8 +439,12 @@ size_t attn_fwd_decode_workspace_size(int32_t B, int32_t h_q, int32_t d, int32_t
   return (size_t)(o_aligned + parts * 4);
 }
 
-attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t workspace_bytes,
-                            void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a contiguous-cache decode call, everything but the workspace.
+attn_status check_decode_args(const attn_decode_args *a) {
   if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
   if (a->B < 1 || a->h_q < 1 || a->h_kv < 1)
     return fail(ATTN_ERR_SHAPE, "need B, h_q, h_kv >= 1");
@@ -465,12 +470,11 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
   if (a->lse && a->lse_sb < 0) return fail(ATTN_ERR_STRIDE, "lse_sb must be >= 0");
   if (a->k_st >= kMaxRowStride || a->v_st >= kMaxRowStride)
     return fail(ATTN_ERR_STRIDE, "k/v token strides must be below 2^24 elements");
-  const size_t need = attn_fwd_decode_workspace_size(a->B, a->h_q, a->d, a->max_kv_len, a->split_size);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
-                workspace ? "" : ", NULL");
-  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return ATTN_OK;
+}
 
+// Split kernel + combine of a checked contiguous-cache decode call, partials in `workspace`.
+attn_status launch_decode(const attn_decode_args *a, void *workspace, void *stream) {
   attn::DecodeParams p{};
   p.q = static_cast<const uint16_t *>(a->q);
   p.k = static_cast<const uint16_t *>(a->k);
@@ -481,6 +485,68 @@ attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t w
   return run_decode(p, a->kv_len, a->sinks, a->o, a->lse, a->B, a->h_q, a->h_kv, a->d, a->max_kv_len,
                     a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, 0, workspace,
                     stream);
+}
+
+}  // namespace
+
+// Device memory of attn_fwd_decode_noalloc: the split partials of every call
+// on a GPU go here.  Each GPU the library runs on holds its own copy from
+// module load until the process ends.  In host code this name is only a
+// handle for hipGetSymbolAddress, never a device address.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+attn_status scratch_address(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxDevices - 1);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], "hipGetSymbolAddress(scratch)");
+  *ptr = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_decode(const attn_decode_args *a, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  const attn_status st = check_decode_args(a);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_fwd_decode_workspace_size(a->B, a->h_q, a->d, a->max_kv_len, a->split_size);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return launch_decode(a, workspace, stream);
+}
+
+attn_status attn_fwd_decode_noalloc(const attn_decode_args *a, void *stream) {
+  const attn_status st = check_decode_args(a);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_fwd_decode_workspace_size(a->B, a->h_q, a->d, a->max_kv_len, a->split_size);
+  if (need > ATTN_DECODE_SCRATCH_BYTES)
+    return fail(ATTN_ERR_WORKSPACE, "these sizes need %zu bytes of partials, above the %zu-byte scratch of "
+                "attn_fwd_decode_noalloc (use attn_fwd_decode with a workspace)", need,
+                (size_t)ATTN_DECODE_SCRATCH_BYTES);
+  void *ptr = nullptr;
+  const attn_status sst = scratch_address(&ptr);
+  if (sst != ATTN_OK) return sst;
+  return launch_decode(a, ptr, stream);
 }
 
 attn_status attn_fwd_decode_fp8(const attn_decode_fp8_args *a, void *workspace, size_t workspace_bytes,

@@ -354,6 +354,27 @@ attn_status attn_fwd_prefill_chunked(const attn_prefill_args *args, void *worksp
 
 attn_status attn_fwd_decode(const attn_decode_args *args, void *workspace, size_t workspace_bytes,
                             void *stream);
+/*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory or take a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The same operation, kernels and
+ * results as attn_fwd_decode; the split partials go to a fixed region of
+ * ATTN_DECODE_SCRATCH_BYTES that the library holds in device memory on every
+ * GPU it runs on, from the moment the library's device code is loaded until
+ * the process ends.  Sizes whose partials need more
+ * (attn_fwd_decode_workspace_size above ATTN_DECODE_SCRATCH_BYTES) are
+ * rejected with ATTN_ERR_WORKSPACE; 72 MiB holds B = 64 sequences of up to
+ * 8192 keys with h_q = 128 and d = 256 in 512-key splits.  The caller still
+ * owns q, k, v, kv_start, kv_len, o, lse and sinks.  All calls on one GPU
+ * share its region: calls that may overlap on one GPU (on different streams,
+ * or from different host threads without ordering) race and give wrong
+ * results; calls ordered on one stream are safe.  Nothing in the region needs
+ * to start at any value.  The first call on a device looks up the region's
+ * address with that device current (hipGetSymbolAddress; ATTN_ERR_HIP if it
+ * fails).
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)72 << 20)
+attn_status attn_fwd_decode_noalloc(const attn_decode_args *args, void *stream);
 attn_status attn_fwd_decode_paged(const attn_decode_paged_args *args, void *workspace,
                                   size_t workspace_bytes, void *stream);
 attn_status attn_fwd_decode_fp8(const attn_decode_fp8_args *args, void *workspace, size_t workspace_bytes,

@@ -33,8 +33,8 @@ def test_header_declares_the_boundary():
     for want in ("attn_fwd_prefill", "attn_fwd_prefill_chunked", "attn_fwd_prefill_chunked_workspace_size",
                  "attn_fwd_decode", "attn_fwd_decode_paged", "attn_fwd_decode_fp8",
                  "attn_combine", "attn_bwd", "attn_bwd_workspace_size",
-                 "attn_fwd_decode_workspace_size", "attn_status_str", "attn_last_error",
-                 "attn_abi_version"):
+                 "attn_fwd_decode_workspace_size", "attn_fwd_decode_noalloc", "attn_status_str",
+                 "attn_last_error", "attn_abi_version"):
         assert want in names
 
 
@@ -249,6 +249,27 @@ def test_decode_rejects(name, over, code):
     a = good_decode(**over)
     st = lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None)
     assert st == code, (st, lib.attn_last_error())
+
+
+@pytest.mark.parametrize("name,over,code", DECODE_BAD, ids=[c[0] for c in DECODE_BAD])
+def test_decode_noalloc_rejects(name, over, code):
+    """The no-allocation decode checks its arguments like attn_fwd_decode, before any HIP call."""
+    lib = afa.load_library()
+    a = good_decode(**over)
+    st = lib.attn_fwd_decode_noalloc(ctypes.byref(a), None)
+    assert st == code, (st, lib.attn_last_error())
+
+
+def test_decode_noalloc_rejects_sizes_beyond_its_scratch():
+    lib = afa.load_library()
+    # B = 64, h_q = 128, d = 256, 16384 keys in 512-key splits: 128 MiB of partials
+    a = good_decode(B=64, h_q=128, d=256, max_kv_len=16384)
+    need = lib.attn_fwd_decode_workspace_size(64, 128, 256, 16384, 512)
+    assert need > 72 << 20
+    assert lib.attn_fwd_decode_noalloc(ctypes.byref(a), None) == 6
+    assert b"scratch" in lib.attn_last_error()
+    # the largest decode workload (d = 256, 8192 keys) fits
+    assert lib.attn_fwd_decode_workspace_size(64, 128, 256, 8192, 512) <= 72 << 20
 
 
 def good_paged(**over):
