@@ -225,17 +225,21 @@ def cpu_model() -> str:
 def timed(cases, steps: int, warmup: int, start: int = 0):
     """Run warmup + steps; return (per-case mean ms per launch, wall ms per step).
 
-    The timed region runs the K steps case by case: K launches of the first
-    case back to back, then K of the next, each block between two HIP events
-    on the launch stream (torch's current stream), so a per-launch average
-    carries no event overhead of its own.  Every launch takes the next input
+    The W warm-up steps run case by case, last case first; the timed region
+    then runs the K steps case by case: K launches of the first case back to
+    back, then K of the next, each block between two HIP events on the launch
+    stream (torch's current stream), so a per-launch average carries no event
+    overhead of its own.  Every launch takes the next input
     set of its case's rotation, as a step would.  The region is bracketed by
     torch.cuda.synchronize() on both sides.
     """
     import torch
 
-    for i in range(warmup):
-        for c in cases:
+    # warm-up in blocks, last case first, so that each timed block follows warm
+    # launches of its own kind (a memory-bound decode block leaves the clock
+    # in another state than a compute-bound prefill block)
+    for c in reversed(cases):
+        for i in range(warmup):
             c.run(start + i)
     torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(cases) + 1)]
@@ -504,9 +508,9 @@ def recorded_traffic(*profiles: str):
                    + ", ".join(f"profiles/{n}" for n in profiles) + " (current kernel sources)")
 
 
-PREFILL_PROFILE = ("prefill_d128_causal_b1_h16_s8192.md",)
-DECODE_PROFILES = {"mqa_decode_B64_hq128_d128": ("decode_d128_B64_hq128.md",),
-                   "mqa_decode_B64_hq128_d256": ("decode_d256_B64_hq128.md",)}
+PREFILL_PROFILE = ("prefill_d128_mha_b1_h16_s8192_d128_causal.md",)
+DECODE_PROFILES = {"mqa_decode_B64_hq128_d128": ("decode_d128_mqa_decode_B64_hq128_d128.md",),
+                   "mqa_decode_B64_hq128_d256": ("decode_d256_mqa_decode_B64_hq128_d256.md",)}
 
 
 def roofline_prefill(flops: int, ms: float, traffic=(None, None)):
@@ -653,13 +657,13 @@ def make_case(w, dev):
     return kind(w, n_sets_beyond_mall(decode_set_bytes(w)), dev)
 
 
-def bench_one(name: str, steps: int, warmup: int, dev):
+def bench_one(name: str, steps: int, warmup: int, dev, settle_s: float = 1.0):
     """One JSON line for one named workload alone (settle pass, warm-up, timed block)."""
     from attention_forward_attn_amd.inputs import WORKLOADS
 
     w = WORKLOADS[name]
     c = make_case(w, dev)
-    st = settle(c, 0)
+    st = settle(c, 0, min_s=settle_s) if settle_s > 0 else {"seconds": 0.0, "launches": 0}
     (ms,), wall = timed([c], steps, warmup, start=st["launches"])
     base = {"workload": name, "kind": w.kind, "ms": round(ms, 4), "input_sets": len(c.sets), "settle": st}
     if w.kind in ("prefill", "backward"):
@@ -677,6 +681,9 @@ def main():
     ap.add_argument("--workload", default=None, help="bench one named workload alone")
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="least duration of the clock-settle pass before the warm-up (0: no settle pass, e.g. "
+                         "under a counter profiler, which serialises every launch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy 3 times (a known-size reference for "
                          "HBM byte counters)")
@@ -707,7 +714,7 @@ def main():
     if args.workload or args.all:
         names = [args.workload] if args.workload else list(WORKLOADS)
         for n in names:
-            print(json.dumps(bench_one(n, args.steps, args.warmup, dev)), flush=True)
+            print(json.dumps(bench_one(n, args.steps, args.warmup, dev, args.settle_seconds)), flush=True)
         return
 
     wp = WORKLOADS[HEADLINE_PREFILL]
@@ -715,7 +722,7 @@ def main():
     wd2 = WORKLOADS[SECOND_DECODE]
     pc, dc, dc2 = make_case(wp, dev), make_case(wd, dev), make_case(wd2, dev)
     # clock settle (time-based, before the warm-up steps), then warm-up and the timed steps
-    st = settle(pc, 0)
+    st = settle(pc, 0, min_s=args.settle_seconds) if args.settle_seconds > 0 else {"seconds": 0.0, "launches": 0}
     start = st["launches"]
     (pre_ms, dec_ms, dec2_ms), wall_ms = timed([pc, dc, dc2], args.steps, args.warmup, start=start)
     start += args.warmup + args.steps
