@@ -106,7 +106,8 @@ class BwdArgs(ctypes.Structure):
         ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_ss", ctypes.c_int64),
         ("k_sb", ctypes.c_int64), ("k_sh", ctypes.c_int64), ("k_ss", ctypes.c_int64),
         ("lse_sb", ctypes.c_int64), ("lse_sh", ctypes.c_int64),
-        ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("sinks", ctypes.c_void_p), ("d_sinks", ctypes.c_void_p),
     ]
 
 
@@ -504,13 +505,15 @@ def backward_workspace_size(b: int, h_q: int, s_q: int) -> int:
 
 
 @_on_stream
-def backward(q, k, v, o, d_o, lse, *, scale: float | None = None, causal: bool = False, dq=None, dk=None,
-             dv=None, workspace=None, stream=None):
+def backward(q, k, v, o, d_o, lse, *, scale: float | None = None, causal: bool = False, window: int = 0,
+             sinks=None, dq=None, dk=None, dv=None, d_sinks=None, workspace=None, stream=None):
     """dQ, dK, dV of the prefill for an incoming gradient d_o, from the forward's o and lse.
 
     q, o, d_o: bf16 [b, h_q, s_q, d] with identical strides; k, v: bf16
     [b, h_kv, s_k, d] with identical strides; lse: fp32 [b, h_q, s_q] (unit
-    stride along s).  Returns (dq, dk, dv) laid out like q, k and v.
+    stride along s); causal and window as in the forward.  Returns (dq, dk, dv)
+    laid out like q, k and v; with ``sinks`` (the forward's fp32 [h_q] sink
+    logits) also d_sinks, the sink gradient summed over the batch.
     """
     import torch
 
@@ -535,6 +538,10 @@ def backward(q, k, v, o, d_o, lse, *, scale: float | None = None, causal: bool =
         dv = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=q.device)
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != k.stride():
         raise ValueError("dq must have q's strides, dk and dv k's strides")
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
+        raise ValueError("sinks must be a contiguous float32 device tensor")
+    if sinks is not None and d_sinks is None:
+        d_sinks = torch.empty(h_q, dtype=torch.float32, device=q.device)
     need = int(lib.attn_bwd_workspace_size(b, h_q, s_q))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -548,8 +555,13 @@ def backward(q, k, v, o, d_o, lse, *, scale: float | None = None, causal: bool =
     a.lse_sb, a.lse_sh = lse.stride(0), lse.stride(1)
     a.scale = scale
     a.causal = 1 if causal else 0
+    a.window = int(window)
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.d_sinks = d_sinks.data_ptr() if d_sinks is not None else None
     _check(lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                         workspace.numel() * workspace.element_size(), _stream(stream)))
+    if sinks is not None:
+        return dq, dk, dv, d_sinks
     return dq, dk, dv
 
 

@@ -659,9 +659,14 @@ attn_status attn_fwd_decode_paged(const attn_decode_paged_args *a, void *workspa
                     stream);
 }
 
+// Backward workspace: D = rowsum(dO * O) [b][h_q][s_q] fp32, then (256-byte
+// aligned) the sink-gradient partials [b][h_q][query tiles of the dQ kernel].
 size_t attn_bwd_workspace_size(int32_t b, int32_t h_q, int32_t s_q) {
   if (b < 1 || h_q < 1 || s_q < 0) return 0;
-  return (size_t)b * h_q * (size_t)(s_q > 0 ? s_q : 1) * 4;
+  const size_t rows = (size_t)b * h_q * (size_t)(s_q > 0 ? s_q : 1);
+  const size_t br = (size_t)attn::backward_block_rows();
+  const size_t tiles = (size_t)b * h_q * (((size_t)s_q + br - 1) / br);
+  return (rows * 4 + 255) / 256 * 256 + tiles * 4;
 }
 
 attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
@@ -672,10 +677,18 @@ attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_b
     return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
   if (a->d != 64 && a->d != 128) return fail(ATTN_ERR_SHAPE, "backward supports d = 64 or 128 (got %d)", a->d);
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1");
+  if (a->window < 0) return fail(ATTN_ERR_SHAPE, "window must be >= 0");
+  if (a->window > 0 && !a->causal) return fail(ATTN_ERR_SHAPE, "a window requires causal = 1");
   if (!(std::isfinite(a->scale) && a->scale > 0.0f))
     return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
-  if (!a->q || !a->k || !a->v || !a->o || !a->d_o || !a->lse || !a->dq || !a->dk || !a->dv)
-    return fail(ATTN_ERR_NULL, "q, k, v, o, d_o, lse, dq, dk and dv must be non-NULL");
+  // A tensor with no element may be NULL (a zero-length torch tensor has no storage).
+  if (a->s_q > 0 && (!a->q || !a->o || !a->d_o || !a->lse || !a->dq))
+    return fail(ATTN_ERR_NULL, "q, o, d_o, lse and dq must be non-NULL when s_q > 0");
+  if (a->s_k > 0 && (!a->k || !a->v || !a->dk || !a->dv))
+    return fail(ATTN_ERR_NULL, "k, v, dk and dv must be non-NULL when s_k > 0");
+  if (a->d_sinks && !a->sinks) return fail(ATTN_ERR_NULL, "d_sinks needs sinks");
+  if ((a->sinks && !aligned4(a->sinks)) || (a->d_sinks && !aligned4(a->d_sinks)))
+    return fail(ATTN_ERR_ALIGN, "sinks and d_sinks must be 4-byte aligned");
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) || !aligned16(a->d_o) ||
       !aligned16(a->dq) || !aligned16(a->dk) || !aligned16(a->dv) || !aligned4(a->lse))
     return fail(ATTN_ERR_ALIGN, "bf16 tensors must be 16-byte aligned, lse 4-byte aligned");
@@ -693,7 +706,7 @@ attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_b
     return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", NULL");
   if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
-  if (a->s_q == 0 && a->s_k == 0) return ok();
+  if (a->s_q == 0 && a->s_k == 0 && a->d_sinks == nullptr) return ok();
 
   attn::BwdParams p;
   p.q = static_cast<const uint16_t *>(a->q);
@@ -706,6 +719,12 @@ attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_b
   p.dk = static_cast<uint16_t *>(a->dk);
   p.dv = static_cast<uint16_t *>(a->dv);
   p.dsum = static_cast<float *>(workspace);
+  const size_t rows = (size_t)a->b * a->h_q * (size_t)(a->s_q > 0 ? a->s_q : 1);
+  p.window = a->window;
+  p.sinks = a->sinks;
+  p.d_sinks = a->d_sinks;
+  p.dsink_part = a->d_sinks ? reinterpret_cast<float *>(static_cast<char *>(workspace) + (rows * 4 + 255) / 256 * 256)
+                            : nullptr;
   p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_ss = a->q_ss;
   p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_ss = a->k_ss;
   p.lse_sb = a->lse_sb; p.lse_sh = a->lse_sh;

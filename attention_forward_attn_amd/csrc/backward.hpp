@@ -1,5 +1,11 @@
 // Attention backward at head dims 64 and 128: dQ, dK, dV for an incoming dO, from the
-// forward's O and LSE (no window, no sink), deterministic (no atomics).
+// forward's O and LSE, under no mask, a causal mask or a causal sliding window,
+// deterministic (no atomics).  A sink only enters through the forward's LSE
+// (P = exp(scale*S - LSE) already carries its share of the normalisation), so
+// dQ, dK and dV need nothing more; the sink logit's own gradient,
+// d sigma_h = -sum_{b,i} exp(sigma_h - LSE_i) D_i, is summed per query tile by
+// the dQ kernel and over the tiles and the batch, in a fixed order, by a small
+// third kernel.
 //
 // Two kernels, both built from the forward's tile engine:
 //   * dQ (one workgroup per NW x 32 query rows, NW waves x 32 rows): the forward
@@ -70,13 +76,14 @@ __device__ __forceinline__ void store_rows(uint16_t *op, const f32x16 (&a)[NDB],
 
 // ---------------------------------------------------------------------------
 // dQ (and D).
-template <int D, int BN, bool CAUSAL, int NW>
+template <int D, int BN, bool CAUSAL, bool WINDOW, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dq_kernel(BwdParams p) {
   using T = Tile<D, NW, BN>;
   constexpr int BM = 32 * NW;
   constexpr int STAGE = 3 * T::TILE_BYTES;  // [K, row swizzle][K, transpose swizzle][V, row swizzle]
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE / 2];
+  __shared__ float s_red[NW];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -93,6 +100,8 @@ void bwd_dq_kernel(BwdParams p) {
   const int i_last = min(p.s_q, q0 + BM) - 1;
   const int kend = CAUSAL ? max(0, min(p.s_k, i_last + off + 1)) : p.s_k;
   const int n_tiles = (kend + BN - 1) / BN;
+  // A window: the first key any row of the tile sees.
+  const int t0 = WINDOW ? min(n_tiles, max(0, q0 + off - p.window + 1) / BN) : 0;
 
   const int w_lo = q0 + wave * 32;
   const int w_hi = min(w_lo + 31, p.s_q - 1);
@@ -140,25 +149,27 @@ void bwd_dq_kernel(BwdParams p) {
     T::dma1(ln, true, st + T::TILE_ELEMS, kbase, p.k_ss, t * BN, p.s_k, wave);
     T::dma1(ln, false, st + 2 * T::TILE_ELEMS, vbase, p.k_ss, t * BN, p.s_k, wave);
   };
-  if (n_tiles > 0) load(0, 0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int cur = t & 1;
+  if (t0 < n_tiles) load(0, t0);
+  for (int t = t0; t < n_tiles; ++t) {
+    const int cur = (t - t0) & 1;
     wait_vmcnt<0>();
     __syncthreads();
     if (t + 1 < n_tiles) load(cur ^ 1, t + 1);
     const int j0 = t * BN;
-    if (w_lo < p.s_q && (!CAUSAL || j0 <= w_hi + off)) {
+    if (w_lo < p.s_q && (!CAUSAL || j0 <= w_hi + off) &&
+        (!WINDOW || j0 + BN - 1 >= w_lo + off - p.window + 1)) {
       const uint32_t so = cur * STAGE;
       f32x16 s[T::NKB], dp[T::NKB];
       T::scores(s, qreg, ln, so);
       T::scores(dp, dreg, ln, so + 2 * T::TILE_BYTES);
       const int lim = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
+      const int lo = WINDOW ? row + off - p.window + 1 : 0;
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int j = j0 + T::key_of(kb, i, hi);
-          const float pv = j > lim ? 0.0f : fast_exp2(fmaf(s[kb][i], p.c, -lse2));
+          const float pv = (j > lim || j < lo) ? 0.0f : fast_exp2(fmaf(s[kb][i], p.c, -lse2));
           s[kb][i] = pv * (dp[kb][i] - dd);  // dS
         }
       u32x4 pk[T::NPV];
@@ -167,11 +178,36 @@ void bwd_dq_kernel(BwdParams p) {
     }
   }
   if (row_ok) store_rows(p.dq + qrow0 + (int64_t)row * p.q_ss + 4 * hi, acc, p.scale);
+  if (p.dsink_part != nullptr) {
+    // this tile's share of d sigma_h: -sum over its rows of exp(sigma_h - LSE_i) D_i
+    float cs = (row_ok && hi == 0 && lse != kNegInf) ? -__expf(p.sinks[h] - lse) * dd : 0.0f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cs += __shfl_xor(cs, o);
+    if (lane == 0) s_red[wave] = cs;
+    __syncthreads();
+    if (tid == 0) {
+      float tot = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += s_red[w];
+      p.dsink_part[(int64_t)bh * n_qt + qt] = tot;
+    }
+  }
+}
+
+// d sigma_h = sum over the batch and the query tiles of the dQ kernel's
+// partials, in a fixed order (one thread per query head).
+__global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdParams p, int n_qt) {
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  if (h >= p.h_q) return;
+  float tot = 0.0f;
+  for (int bi = 0; bi < p.b; ++bi)
+    for (int qt = 0; qt < n_qt; ++qt) tot += p.dsink_part[((int64_t)bi * p.h_q + h) * n_qt + qt];
+  p.d_sinks[h] = tot;
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV.  Reads D written by bwd_dq_kernel.
-template <int D, int BN, bool CAUSAL, int NW>
+template <int D, int BN, bool CAUSAL, bool WINDOW, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dkdv_kernel(BwdParams p) {
   using T = Tile<D, NW, BN>;  // here the streamed "keys" of the engine are query rows
@@ -204,8 +240,10 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   // Query rows that see any key of this workgroup: i + off >= first key.
   const int r_begin = CAUSAL ? max(0, kt * BK - off) : 0;
+  // A window: rows past k1 - off + W - 1 (k1 the workgroup's last key) see none of its keys.
+  const int r_end = WINDOW ? max(0, min(p.s_q, kt * BK + BK - 1 - off + p.window)) : p.s_q;
   const int t_begin = r_begin / BN;
-  const int t_end = (p.s_q + BN - 1) / BN;
+  const int t_end = (r_end + BN - 1) / BN;
   const int n_tiles = t_begin < t_end ? t_end - t_begin : 0;
 
   typename T::Lane ln;
@@ -243,7 +281,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       if (n + 1 < n_tiles) load(cur ^ 1, t + 1);
       const int i0 = t * BN;
       // this wave has keys, and (causal) the tile's last row reaches its first key
-      if (w_key0 < p.s_k && (!CAUSAL || min(i0 + BN, p.s_q) - 1 + off >= w_key0)) {
+      if (w_key0 < p.s_k && (!CAUSAL || min(i0 + BN, p.s_q) - 1 + off >= w_key0) &&
+          (!WINDOW || i0 <= min(w_key0 + 31, p.s_k - 1) - off + p.window - 1)) {
         {
           const uint32_t so = cur * STAGE;
           f32x16 s[T::NKB], dp[T::NKB];
@@ -267,7 +306,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = r4 + e;
-                const bool vis = r < p.s_q && key_ok && (!CAUSAL || key <= r + off);
+                const bool vis = r < p.s_q && key_ok && (!CAUSAL || key <= r + off) &&
+                                 (!WINDOW || key >= r + off - p.window + 1);
                 float pv = 0.0f, dsv = 0.0f;
                 if (vis) {
                   const float l = l4[e];
@@ -295,17 +335,22 @@ void bwd_dkdv_kernel(BwdParams p) {
 
 // NWQ waves per dQ workgroup (NWQ x 32 query rows), NWK per dK/dV workgroup
 // (NWK x 32 keys).
-template <int D, int BN, bool CAUSAL, int NWQ, int NWK>
+template <int D, int BN, bool CAUSAL, bool WINDOW, int NWQ, int NWK>
 hipError_t launch_backward(const BwdParams &p, hipStream_t stream) {
   const int n_qt = (p.s_q + 32 * NWQ - 1) / (32 * NWQ), n_kt = (p.s_k + 32 * NWK - 1) / (32 * NWK);
-  if (n_qt > 0) {  // dQ (zero when there are no keys) and D
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL, NWQ>), dim3(p.b * p.h_q * n_qt), dim3(NWQ * 64), 0, stream,
-                       p);
+  if (n_qt > 0) {  // dQ (zero when there are no keys), D and the sink partials
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL, WINDOW, NWQ>), dim3(p.b * p.h_q * n_qt), dim3(NWQ * 64), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.d_sinks != nullptr) {  // zero when there are no query rows
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3((p.h_q + 255) / 256), dim3(256), 0, stream, p, n_qt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (n_kt > 0) {  // dK, dV (zero when there are no rows)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BN, CAUSAL, NWK>), dim3(p.b * p.h_kv * n_kt), dim3(NWK * 64), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BN, CAUSAL, WINDOW, NWK>), dim3(p.b * p.h_kv * n_kt), dim3(NWK * 64), 0,
                        stream, p);
     return hipGetLastError();
   }

@@ -65,6 +65,10 @@ struct BwdParams {
   int32_t b, h_q, h_kv, s_q, s_k, ratio;
   float c;      // scale * log2(e)
   float scale;
+  int32_t window;        // 0 = none (a window requires the causal mask)
+  const float *sinks;    // [h_q] sink logits, read only when d_sinks is set
+  float *dsink_part;     // [b][h_q][query tiles of the dQ kernel] partial sink gradients
+  float *d_sinks;        // [h_q] sink gradient summed over the batch; NULL = not wanted
 };
 
 // Device-side parameters of the split-KV decode kernel.

@@ -33,7 +33,11 @@ hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s);
 // The same over an FP8 (E4M3) cache with per-kv-head scales (p.k_scale, p.v_scale); d = 128.
 hipError_t decode_split_fp8(int d, const DecodeParams &p, hipStream_t s);
 
-// Attention backward (dQ, dK, dV) at head dim 64 or 128; p.dsum is scratch of b*h_q*s_q floats.
+// Attention backward (dQ, dK, dV, and the sink gradient when p.d_sinks is set) at
+// head dim 64 or 128; p.dsum is scratch of b*h_q*s_q floats, p.dsink_part of
+// b*h_q*ceil(s_q / backward_block_rows()) floats.  A window (p.window > 0)
+// requires causal.
+int backward_block_rows();
 hipError_t backward(int d, const BwdParams &p, bool causal, hipStream_t s);
 
 // LSE merge of fp32 partials (public entry point) / of bf16 partials (decode).

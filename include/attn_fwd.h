@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 6
+#define ATTN_FWD_ABI_VERSION 7
 
 typedef enum {
   ATTN_OK = 0,
@@ -241,17 +241,27 @@ typedef struct {
  * the one taken here is the chain rule through the softmax, with
  * P = exp(scale*QK^T - LSE), D_i = sum_t dO[i,t] O[i,t], dS = P*(dP - D),
  * dQ = scale*dS K, dK = scale*dS^T Q, dV = P^T dO (dK and dV summed over the
- * query heads of each kv head).  No window and no sink; the LSE gets no
- * gradient.  Deterministic: no atomics, every output element is written by
- * exactly one thread in a fixed order.
+ * query heads of each kv head), under the forward's masks: none, causal, or a
+ * causal sliding window of `window` keys (status page rows D3/D4).  A sink
+ * (row D5c) enters only through the forward's LSE, which must be the one
+ * computed with the same sinks; its logit's own gradient,
+ * d_sinks[h] = -sum over the batch and rows of exp(sinks[h] - LSE_i) * D_i, is
+ * written when d_sinks is not NULL.  The LSE gets no gradient.  Deterministic:
+ * no atomics, every output element is written by exactly one thread in a fixed
+ * order.
  *
  * q, o, d_o, dq: bf16 [b, h_q, s_q, d], one shared stride set (q_sb, q_sh,
  *       q_ss); k, v, dk, dv: bf16 [b, h_kv, s_k, d], one shared stride set
  *       (k_*); lse: fp32 (bi, h, i) at lse + bi*lse_sb + h*lse_sh + i.
+ * q, o, d_o, lse and dq may be NULL when s_q = 0, k, v, dk and dv when s_k = 0.
+ * window: 0 = none; W > 0 (only with causal) keeps keys j >= i + s_k - s_q - W + 1.
+ * sinks: fp32 [h_q], the forward's sink logits (read only for d_sinks);
+ * d_sinks: fp32 [h_q] output, NULL = not wanted (then sinks may be NULL).
  * workspace: attn_bwd_workspace_size(b, h_q, s_q) bytes, 16-byte aligned,
- *       caller-owned (row sums D between the two kernels).
- * Two kernels run on `stream` (dQ and D, then dK/dV).  Supported: d = 64 or 128;
- * causal (bottom-right) or not; h_q % h_kv == 0.
+ *       caller-owned (row sums D between the kernels, and the sink gradient's
+ *       per-tile partials).
+ * Kernels run on `stream`: dQ and D, the sink gradient (if wanted), then dK/dV.
+ * Supported: d = 64 or 128; causal (bottom-right) or not; h_q % h_kv == 0.
  */
 typedef struct {
   const void *q, *k, *v, *o, *d_o;
@@ -263,6 +273,9 @@ typedef struct {
   int64_t lse_sb, lse_sh;
   float scale;
   int32_t causal;
+  int32_t window;
+  const float *sinks;
+  float *d_sinks;
 } attn_bwd_args;
 
 /* Bytes of device workspace attn_bwd needs (0 on invalid sizes). */

@@ -395,15 +395,16 @@ def decode_fp8_ref(q, k_codes, v_codes, k_scale, v_scale, kv_start, kv_len, scal
     return decode_ref(q, k, v, kv_start, kv_len, scale, sinks=sinks)
 
 
-def attention_backward_ref(q, k, v, d_o, scale: float, causal: bool = False):
+def attention_backward_ref(q, k, v, d_o, scale: float, causal: bool = False, window: int = 0, sinks=None):
     """Gradients of the attention output: (dQ, dK, dV) in float64, shapes of q, k, v.
 
     The pages name the backward kernels and ask for a deterministic one (SM120
     research page, feature-parity and tuning notes) but define no algorithm
     beyond the forward; the planner page says a backward needs its own design.
     Reading used: the gradients of L = sum(dO * O) for O of attention_ref
-    (no incoming gradient on the LSE, no window, no sink), by the chain rule
-    through the softmax, per batch b and query head h (kv head g):
+    (no incoming gradient on the LSE), by the chain rule through the softmax,
+    per batch b and query head h (kv head g), with the visible keys of
+    ``visible_keys`` (causal and sliding-window masks):
 
         P    = softmax_j(scale * Q K^T + mask)          (rows that see no key: 0)
         dV_g = sum_{h in g} P^T dO
@@ -411,6 +412,13 @@ def attention_backward_ref(q, k, v, d_o, scale: float, causal: bool = False):
         D_i  = sum_t dO[i,t] O[i,t]   (= sum_j P_ij dP_ij)
         dS   = P * (dP - D)
         dQ   = scale * dS K,   dK_g = sum_{h in g} scale * dS^T Q
+
+    A sink sigma_h (DSV4 status page row D5c: one more softmax column per query
+    head, logit taken as is, zero value row) enters the normalisation of P, so
+    the formulas above hold with P over the real keys only; its own column has
+    dP = 0, hence d sigma_h = sum_{b,i} P_i,sink * (0 - D_i), summed over the
+    batch because the sink is shared by every sequence.  With ``sinks`` the
+    result is (dQ, dK, dV, d_sinks [h_q]).
     """
     q = _as_f64(q)
     k = _as_f64(k)
@@ -419,19 +427,25 @@ def attention_backward_ref(q, k, v, d_o, scale: float, causal: bool = False):
     b, h_q, h_kv, s_k, d = _check_shapes(q, k, v)
     s_q = q.shape[2]
     ratio = h_q // h_kv
-    vis = visible_keys(s_q, s_k, causal, 0)
+    sig = None if sinks is None else _as_f64(sinks).reshape(-1)
+    vis = visible_keys(s_q, s_k, causal, window)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    dsig = np.zeros(h_q)
     for bi in range(b):
         for h in range(h_q):
             g = h // ratio
             s = scale * (q[bi, h] @ k[bi, g].T)
             s = np.where(vis, s, NEG_INF)
             m = s.max(axis=1) if s_k > 0 else np.full(s_q, NEG_INF)
+            if sig is not None:
+                m = np.maximum(m, sig[h])
             m_safe = np.where(np.isfinite(m), m, 0.0)
             num = np.exp(s - m_safe[:, None])
             z = num.sum(axis=1)
+            if sig is not None:
+                z = z + np.exp(sig[h] - m_safe)
             p = num / np.where(z > 0, z, 1.0)[:, None]
             o = p @ v[bi, g]
             dp = d_o[bi, h] @ v[bi, g].T
@@ -440,6 +454,11 @@ def attention_backward_ref(q, k, v, d_o, scale: float, causal: bool = False):
             dq[bi, h] = scale * (ds @ k[bi, g])
             dk[bi, g] += scale * (ds.T @ q[bi, h])
             dv[bi, g] += p.T @ d_o[bi, h]
+            if sig is not None:
+                p_sink = np.exp(sig[h] - m_safe) / np.where(z > 0, z, 1.0)
+                dsig[h] += (p_sink * (0.0 - dd)).sum()
+    if sig is not None:
+        return dq, dk, dv, dsig
     return dq, dk, dv
 
 

@@ -452,17 +452,23 @@ def pin_fp8_decode_matches_brute(orc):
 
 
 def pin_backward_matches_autograd(orc):
-    """dQ, dK, dV equal torch's fp64 autograd through its textbook attention (GQA by repeated heads)."""
+    """dQ, dK, dV (and the sink gradient) equal torch's fp64 autograd through its textbook
+    attention: GQA by repeated heads, the window as a band mask, the sink as a concatenated
+    column of zero value."""
     import torch
 
     rng = _rng(27)
-    for (b, h_q, h_kv, s_q, s_k, d, causal) in [(1, 2, 2, 5, 5, 4, False), (2, 4, 2, 6, 6, 3, True),
-                                                 (1, 4, 1, 4, 7, 5, True), (1, 2, 1, 7, 3, 2, True)]:
+    for (b, h_q, h_kv, s_q, s_k, d, causal, window, with_sink) in [
+            (1, 2, 2, 5, 5, 4, False, 0, False), (2, 4, 2, 6, 6, 3, True, 0, False),
+            (1, 4, 1, 4, 7, 5, True, 0, False), (1, 2, 1, 7, 3, 2, True, 0, False),
+            (2, 2, 1, 9, 9, 3, True, 3, False), (1, 2, 2, 6, 8, 4, True, 2, True),
+            (2, 4, 2, 5, 5, 3, False, 0, True), (1, 2, 1, 7, 3, 2, True, 0, True)]:
         q = rng.standard_normal((b, h_q, s_q, d))
         k = rng.standard_normal((b, h_kv, s_k, d))
         v = rng.standard_normal((b, h_kv, s_k, d))
         do = rng.standard_normal((b, h_q, s_q, d))
-        dq, dk, dv = orc.attention_backward_ref(q, k, v, do, 0.6, causal)
+        sig = rng.standard_normal(h_q) if with_sink else None
+        res = orc.attention_backward_ref(q, k, v, do, 0.6, causal, window, sig)
         tq = torch.tensor(q, requires_grad=True)
         tk = torch.tensor(k, requires_grad=True)
         tv = torch.tensor(v, requires_grad=True)
@@ -470,16 +476,28 @@ def pin_backward_matches_autograd(orc):
         kk = tk.repeat_interleave(r, dim=1)
         vv = tv.repeat_interleave(r, dim=1)
         s = 0.6 * tq @ kk.transpose(-1, -2)
+        off = s_k - s_q
+        keep = torch.ones(s_q, s_k, dtype=torch.bool)
         if causal:
-            off = s_k - s_q
-            mask = torch.arange(s_k)[None, :] <= torch.arange(s_q)[:, None] + off
-            s = s.masked_fill(~mask, float("-inf"))
-        p = torch.softmax(s, dim=-1).nan_to_num(0.0)  # rows that see no key: zero
+            keep &= torch.arange(s_k)[None, :] <= torch.arange(s_q)[:, None] + off
+        if window:
+            keep &= torch.arange(s_k)[None, :] >= torch.arange(s_q)[:, None] + off - window + 1
+        s = s.masked_fill(~keep, float("-inf"))
+        if with_sink:
+            ts = torch.tensor(sig, requires_grad=True)
+            col = ts[None, :, None, None].expand(b, h_q, s_q, 1)
+            p = torch.softmax(torch.cat([s, col], dim=-1), dim=-1)[..., :s_k]
+        else:
+            p = torch.softmax(s, dim=-1).nan_to_num(0.0)  # rows that see no key: zero
         o = p @ vv
         (o * torch.tensor(do)).sum().backward()
-        _close(dq, tq.grad.numpy(), 1e-10, "dQ")
-        _close(dk, tk.grad.numpy(), 1e-10, "dK")
-        _close(dv, tv.grad.numpy(), 1e-10, "dV")
+        _close(res[0], tq.grad.numpy(), 1e-10, "dQ")
+        _close(res[1], tk.grad.numpy(), 1e-10, "dK")
+        _close(res[2], tv.grad.numpy(), 1e-10, "dV")
+        if with_sink:
+            _close(res[3], ts.grad.numpy(), 1e-10, "d sinks")
+        else:
+            assert len(res) == 3
 
 
 def pin_split_merge_equals_unsplit(orc):

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     lib = afa.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
-    assert lib.attn_abi_version() == 6
+    assert lib.attn_abi_version() == 7
 
 
 def test_status_strings():
@@ -458,6 +458,12 @@ BWD_BAD = [
     ("huge row stride", dict(k_ss=1 << 24), 3),
     ("misaligned dq", dict(dq=FAKE + 8), 4),
     ("misaligned lse", dict(lse=FAKE + 2), 4),
+    ("window without causal", dict(causal=0, window=16), 2),
+    ("negative window", dict(window=-1), 2),
+    ("d_sinks without sinks", dict(d_sinks=FAKE), 1),
+    ("null q with rows", dict(q=None), 1),
+    ("null dk with keys", dict(dk=None), 1),
+    ("misaligned d_sinks", dict(sinks=FAKE, d_sinks=FAKE + 2), 4),
 ]
 
 
@@ -469,11 +475,19 @@ def test_bwd_rejects(name, over, code):
     assert st == code, (st, lib.attn_last_error())
 
 
+def test_bwd_empty_sides_may_be_null():
+    """s_q = 0 and s_k = 0: nothing to compute and no pointer needed, returns before any HIP call."""
+    lib = afa.load_library()
+    a = good_bwd(s_q=0, s_k=0, q=None, o=None, d_o=None, lse=None, dq=None, k=None, v=None, dk=None, dv=None)
+    assert lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 20, None) == 0, lib.attn_last_error()
+
+
 def test_bwd_workspace_checks():
     lib = afa.load_library()
     a = good_bwd()
     need = lib.attn_bwd_workspace_size(2, 16, 4096)
-    assert need == 2 * 16 * 4096 * 4
+    # D per row, then the sink-gradient partials per 256-row query tile of the dQ kernel
+    assert need == 2 * 16 * 4096 * 4 + 2 * 16 * (4096 // 256) * 4
     assert lib.attn_bwd(ctypes.byref(a), None, need, None) == 6
     assert lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
     assert lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4

@@ -30,8 +30,9 @@ MUTATIONS = [
     ("Q K^T transposed", "s = scale * (q[bi, h, i0:i1] @ kg.T)", "s = scale * (kg[i0:i1] @ q[bi, h].T)"),
     ("GQA interleaved mapping", "            g = h // ratio\n            kg = k[bi, g]",
      "            g = h % h_kv\n            kg = k[bi, g]"),
-    ("sink scaled", "z = z + np.exp(sig[h] - m_safe)", "z = z + np.exp(scale * sig[h] - m_safe)"),
-    ("sink dropped from Z", "z = z + np.exp(sig[h] - m_safe)", "z = z"),
+    ("sink scaled", "z = z + np.exp(sig[h] - m_safe)\n                num = e @ vg",
+     "z = z + np.exp(scale * sig[h] - m_safe)\n                num = e @ vg"),
+    ("sink dropped from Z", "z = z + np.exp(sig[h] - m_safe)\n                num = e @ vg", "z = z\n                num = e @ vg"),
     ("LSE without max", "lse[bi, h, i0:i1] = np.where(nonempty, m_safe + np.log(",
      "lse[bi, h, i0:i1] = np.where(nonempty, 0.0 + np.log("),
     ("not normalised", "num / np.where(nonempty, z, 1.0)[:, None]", "num"),
@@ -64,6 +65,9 @@ MUTATIONS = [
     ("bwd: dK without scale", "dk[bi, g] += scale * (ds.T @ q[bi, h])", "dk[bi, g] += (ds.T @ q[bi, h])"),
     ("bwd: dV transposed P", "dv[bi, g] += p.T @ d_o[bi, h]", "dv[bi, g] += p[:, :v.shape[2]].T @ d_o[bi, h][:p.shape[1]]"),
     ("bwd: dQ from V", "dq[bi, h] = scale * (ds @ k[bi, g])", "dq[bi, h] = scale * (ds @ v[bi, g])"),
+    ("bwd: sink gradient sign", "dsig[h] += (p_sink * (0.0 - dd)).sum()", "dsig[h] += (p_sink * dd).sum()"),
+    ("bwd: sink left out of P", "                z = z + np.exp(sig[h] - m_safe)\n            p = num",
+     "                z = z\n            p = num"),
     ("flops count 2d per pair", "return 4 * d * pairs * b * h_q", "return 2 * d * pairs * b * h_q"),
 ]
 
