@@ -7,6 +7,7 @@ library; the first call does, and raises if the library has not been built.
 """
 
 from ._binding import (  # noqa: F401
+    DECODE_WORKSPACE_HEADER,
     LIB_PATH,
     AttnError,
     backward,
@@ -18,5 +19,6 @@ from ._binding import (  # noqa: F401
     decode_paged,
     decode_workspace_size,
     load_library,
+    new_decode_workspace,
     prefill,
 )

@@ -306,8 +306,22 @@ def prefill(q, k, v, *, scale: float | None = None, causal: bool = False, window
 
 
 
+# ATTN_DECODE_WORKSPACE_HEADER: the leading bytes of a decode workspace that
+# hold the merge's arrival counters (zero before the first call, left zero).
+DECODE_WORKSPACE_HEADER = 64 << 10
+
+
 def decode_workspace_size(B: int, h_q: int, d: int, max_kv_len: int, split_size: int = 512) -> int:
     return int(load_library().attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
+
+
+def new_decode_workspace(nbytes: int, device):
+    """A decode workspace of nbytes with its counter header zeroed (the rest is left as allocated)."""
+    import torch
+
+    ws = torch.empty(max(nbytes, DECODE_WORKSPACE_HEADER), dtype=torch.uint8, device=device)
+    ws[:DECODE_WORKSPACE_HEADER].zero_()
+    return ws
 
 
 def _decode_args(q, k, v, kv_start, kv_len, max_kv_len, scale, sinks, split_size, out, lse, return_lse):
@@ -364,7 +378,7 @@ def decode(q, k, v, kv_start, kv_len, max_kv_len: int, *, scale: float | None = 
                                return_lse)
     need = int(lib.attn_fwd_decode_workspace_size(a.B, a.h_q, a.d, a.max_kv_len, a.split_size))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = new_decode_workspace(need, q.device)
     _check(lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
@@ -415,7 +429,7 @@ def decode_paged(q, k_cache, v_cache, block_table, kv_len, max_kv_len: int, *, s
         scale = 1.0 / math.sqrt(d)
     need = int(lib.attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = new_decode_workspace(need, q.device)
     if out is None:
         out = torch.empty((B, h_q, d), dtype=torch.bfloat16, device=q.device)
     if lse is None and return_lse:
@@ -472,7 +486,7 @@ def decode_fp8(q, k8, v8, k_scale, v_scale, kv_start, kv_len, max_kv_len: int, *
         scale = 1.0 / math.sqrt(d)
     need = int(lib.attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = new_decode_workspace(need, q.device)
     if out is None:
         out = torch.empty((B, h_q, d), dtype=torch.bfloat16, device=q.device)
     if lse is None and return_lse:

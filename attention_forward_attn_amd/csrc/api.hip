@@ -53,10 +53,10 @@ attn_status hip_fail(hipError_t e, const char *what) {
   return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Shared tail of the dense and paged decode entry points (arguments already
-// validated; p carries the K/V addressing; kind 0 = contiguous bf16 cache,
-// 1 = paged, 2 = FP8): grid check, workspace layout, the split kernel and the
-// combine kernel.
+// Shared tail of the dense, paged and FP8 decode entry points (arguments
+// already validated; p carries the K/V addressing; kind 0 = contiguous bf16
+// cache, 1 = paged, 2 = FP8): grid check, workspace layout and the one launch
+// of the split kernel with its merge.
 attn_status run_decode(attn::DecodeParams &p, const int32_t *kv_len, const float *sinks, void *o, float *lse,
                        int32_t B, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_kv_len, int32_t split_size,
                        int64_t q_sb, int64_t q_sh, int64_t o_sb, int64_t o_sh, int64_t lse_sb, float scale,
@@ -65,34 +65,51 @@ attn_status run_decode(attn::DecodeParams &p, const int32_t *kv_len, const float
   const int ratio = h_q / h_kv;
   const int64_t n_split = max_kv_len > 0 ? (max_kv_len + split_size - 1) / split_size : 1;
   const int64_t n_hblk = (ratio + bm - 1) / bm;
-  if (attn::decode_grid_size(n_split, B, h_kv, n_hblk) > INT32_MAX)
+  const int64_t mh = attn::decode_merge_heads(d);
+  const int64_t n_mblk = (ratio + mh - 1) / mh;
+  const int64_t unit_grid = attn::decode_grid_size(n_split, B, h_kv, n_hblk);
+  if (unit_grid + (int64_t)B * h_kv * n_mblk > INT32_MAX)
     return fail(ATTN_ERR_SHAPE, "decode grid too large: splits x B x kv heads x head blocks must fit in int32");
+  // The kernels address one head block's partial rows through a 32-bit buffer range.
+  if ((int64_t)bm * n_split * d * 2 > (int64_t)UINT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "too many splits (%lld): 128 x splits x d x 2 must fit in 32 bits",
+                (long long)n_split);
 
   const int64_t parts = (int64_t)B * h_q * n_split;
-  const int64_t o_bytes = parts * d * 2;
-  uint16_t *o_part = static_cast<uint16_t *>(workspace);
-  float *lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + (o_bytes + 255) / 256 * 256);
-
+  char *ws = static_cast<char *>(workspace);
+  const int64_t header = (int64_t)ATTN_DECODE_WORKSPACE_HEADER;
+  // One arrival counter per merge workgroup in the fixed header; beyond that
+  // many, the splits are merged by a second kernel instead.
+  const int64_t n_merge = (int64_t)B * h_kv * n_mblk;
+  const bool fused = n_merge <= header / 4;
+  p.arrive = fused ? reinterpret_cast<uint32_t *>(ws) : nullptr;
+  p.arrive_stride = n_merge * 64 <= header ? 16 : 1;  // a 64-byte line per counter when they fit
+  p.o_part = reinterpret_cast<uint16_t *>(ws + header);
+  p.lse_part = reinterpret_cast<float *>(ws + header + (parts * d * 2 + 255) / 256 * 256);
   p.kv_len = kv_len;
   p.sinks = sinks;
-  p.o_part = o_part;
-  p.lse_part = lse_part;
   p.q_sb = q_sb; p.q_sh = q_sh;
   p.B = B; p.h_q = h_q; p.h_kv = h_kv; p.ratio = ratio;
   p.n_split = (int32_t)n_split;
   p.split = split_size;
   p.n_hblk = (int32_t)n_hblk;
   p.c = scale * attn::kLog2e;
+  p.o_out = static_cast<uint16_t *>(o);
+  p.lse_out = lse;
+  p.o_sb = o_sb; p.o_sh = o_sh; p.lse_sb = lse_sb;
+  p.n_mblk = fused ? (int32_t)n_mblk : 0;  // no merge workgroups when the combine kernel merges
+  p.unit_grid = (int32_t)unit_grid;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = kind == 1   ? attn::decode_split_paged(d, p, s)
                  : kind == 2 ? attn::decode_split_fp8(d, p, s)
                              : attn::decode_split(d, p, s);
-  if (e != hipSuccess) return hip_fail(e, "decode split launch");
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (fused) return ok();
 
   attn::CombineParams c;
-  c.o_parts = o_part;
-  c.lse_parts = lse_part;
+  c.o_parts = p.o_part;
+  c.lse_parts = p.lse_part;
   c.o_out = static_cast<uint16_t *>(o);
   c.lse_out = lse;
   c.n_parts = (int32_t)n_split;
@@ -436,7 +453,7 @@ size_t attn_fwd_decode_workspace_size(int32_t B, int32_t h_q, int32_t d, int32_t
   const int64_t parts = (int64_t)B * h_q * n_split;
   const int64_t o_bytes = parts * d * 2;  // bf16 partial outputs
   const int64_t o_aligned = (o_bytes + 255) / 256 * 256;
-  return (size_t)(o_aligned + parts * 4);
+  return ATTN_DECODE_WORKSPACE_HEADER + (size_t)(o_aligned + parts * 4);
 }
 
 }  // extern "C"

@@ -36,16 +36,16 @@ struct Vec8<uint16_t> {
   }
 };
 
-// Merge of one 8-column chunk of one row over n parts (LSE at lp[i*ls], vector
-// at op[i*os]); writes 8 bf16 to out and, if lse_out is not NULL, the LSE.
-// Parts are taken PB at a time.  The partial vectors of a batch are loaded
-// together with their LSEs (not after them: a part's LSE only decides whether
-// its vector is used), so a batch costs one memory round trip; the running
-// (max, weight sum, accumulator) is rescaled once per batch to the batch's
-// new maximum.
-template <typename PT, int PB>
-__device__ __forceinline__ void merge_chunk(const float *lp, int64_t ls, const PT *op, int64_t os, int n,
-                                            uint16_t *out, float *lse_out) {
+// Merge of one 8-column chunk of one row over n parts: lse_at(i) gives part
+// i's LSE and vec_at(i) its 8-column vector (a Vec8); writes 8 bf16 to out
+// and, if lse_out is not NULL, the LSE.  Parts are taken PB at a time.  The
+// partial vectors of a batch are loaded together with their LSEs (not after
+// them: a part's LSE only decides whether its vector is used), so a batch
+// costs one memory round trip; the running (max, weight sum, accumulator) is
+// rescaled once per batch to the batch's new maximum.
+template <typename PT, int PB, typename LseAt, typename VecAt>
+__device__ __forceinline__ void merge_parts(int n, LseAt &&lse_at, VecAt &&vec_at, uint16_t *out,
+                                            float *lse_out) {
   float mx = kNegInf, wsum = 0.0f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < n; i += PB) {
@@ -55,8 +55,8 @@ __device__ __forceinline__ void merge_chunk(const float *lp, int64_t ls, const P
     for (int u = 0; u < PB; ++u) {
       li[u] = kNegInf;
       if (i + u < n) {
-        li[u] = lp[(i + u) * ls];
-        v[u].load(op + (int64_t)(i + u) * os);
+        li[u] = lse_at(i + u);
+        v[u] = vec_at(i + u);
       }
     }
     float bm = li[0];
@@ -84,6 +84,20 @@ __device__ __forceinline__ void merge_chunk(const float *lp, int64_t ls, const P
   for (int q = 0; q < 4; ++q) res[q] = pack_bf16x2(acc[2 * q] * inv, acc[2 * q + 1] * inv);
   *reinterpret_cast<u32x4 *>(out) = res;
   if (lse_out != nullptr) *lse_out = wsum > 0.0f ? mx + __logf(wsum) : kNegInf;
+}
+
+// The same with plain loads: LSE at lp[i*ls], vector at op[i*os].
+template <typename PT, int PB>
+__device__ __forceinline__ void merge_chunk(const float *lp, int64_t ls, const PT *op, int64_t os, int n,
+                                            uint16_t *out, float *lse_out) {
+  merge_parts<PT, PB>(
+      n, [&](int i) { return lp[i * ls]; },
+      [&](int i) {
+        Vec8<PT> v;
+        v.load(op + (int64_t)i * os);
+        return v;
+      },
+      out, lse_out);
 }
 
 // bf16 parts come 16 to a batch (every split of an 8192-key sequence at 512

@@ -95,7 +95,20 @@ struct DecodeParams {
   // FP8 cache only: E4M3 codes times these per-kv-head scales.
   const float *k_scale, *v_scale;
   float c;
+  // Merge in the same launch: workgroups from unit_grid on merge the splits
+  // of (sequence, kv head, slice of decode_merge_heads(D) heads) m once its
+  // arrival counter arrive[m * arrive_stride] (m = (b * h_kv + g) * n_mblk +
+  // slice) has counted every split, and write o_out / lse_out.
+  uint32_t *arrive;
+  uint16_t *o_out;
+  float *lse_out;
+  int64_t o_sb, o_sh, lse_sb;
+  int32_t n_mblk, unit_grid;
+  int32_t arrive_stride;  // 16 (one counter per 64-byte line) when they fit, else 1
 };
+
+// Query heads whose merge one 256-thread workgroup takes (8 columns a thread).
+__host__ __device__ constexpr int decode_merge_heads(int d) { return 2048 / d; }
 
 // Workgroups the split-KV decode launches for these sizes (its unit numbering
 // needs the slots in whole groups of 8): every (split, sequence, kv head) slot,

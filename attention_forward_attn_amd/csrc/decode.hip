@@ -1,4 +1,4 @@
-// Split-KV decode and LSE-merge instantiations.
+// Split-KV decode (with its in-launch merge) and LSE-merge instantiations.
 #include "combine.hpp"
 #include "decode.hpp"
 #include "kernels.hpp"
@@ -9,23 +9,23 @@ int decode_block_rows(int d) { return (d == 64 || d == 128 || d == 256) ? 128 : 
 
 hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s) {
   switch (d) {
-    case 64: return launch_decode_split<64, 4, 1, 64, 2, 4>(p, s);
-    case 128: return launch_decode_split<128, 4, 1, 32, 2, 3>(p, s);
-    default: return launch_decode_split<256, 4, 1, 32, 2, 2>(p, s);
+    case 64: return launch_decode_split<64, 4, 64, 2, 4>(p, s);
+    case 128: return launch_decode_split<128, 4, 32, 2, 3>(p, s);
+    default: return launch_decode_split<256, 4, 32, 2, 2>(p, s);
   }
 }
 
 hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s) {
   switch (d) {
-    case 64: return launch_decode_split<64, 4, 1, 64, 2, 4, true>(p, s);
-    case 128: return launch_decode_split<128, 4, 1, 32, 2, 3, true>(p, s);
-    default: return launch_decode_split<256, 4, 1, 32, 2, 2, true>(p, s);
+    case 64: return launch_decode_split<64, 4, 64, 2, 4, true>(p, s);
+    case 128: return launch_decode_split<128, 4, 32, 2, 3, true>(p, s);
+    default: return launch_decode_split<256, 4, 32, 2, 2, true>(p, s);
   }
 }
 
 hipError_t decode_split_fp8(int d, const DecodeParams &p, hipStream_t s) {
   if (d != 128) return hipErrorInvalidValue;
-  return launch_decode_split<128, 4, 1, 32, 2, 3, false, true>(p, s);
+  return launch_decode_split<128, 4, 32, 2, 3, false, true>(p, s);
 }
 
 hipError_t combine(const CombineParams &p, hipStream_t s) { return launch_combine<float>(p, s); }

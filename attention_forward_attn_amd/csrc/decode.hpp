@@ -1,5 +1,6 @@
 // Split-KV decode: one workgroup per unit (key split, sequence, kv head, head
-// block of HG*32 query heads).
+// block of HG*32 query heads), and the LSE merge of the splits in the same
+// launch.
 //
 // A decode step has one query token per sequence, so a single sequence gives
 // an MMA only one row -- unless the query heads that share a kv head are
@@ -7,9 +8,9 @@
 // heads of one kv group (all the heads of an MQA model), and every K/V tile is
 // read once from HBM and used by all of them (the DSV4 status page's
 // "head-packed MQA/GQA", row D2, with MQA as kv head stride 0).  Each split
-// covers a fixed run of keys; its normalised partial output (bf16) and LSE
-// (fp32) are merged afterwards by the combine kernel (the LSE merge of the
-// STAGE_D.md page).  With one query row the bottom-right causal mask admits
+// covers a fixed run of keys and writes its normalised partial output (bf16)
+// and LSE (fp32); the splits of a row are then merged by the LSE merge of the
+// STAGE_D.md page.  With one query row the bottom-right causal mask admits
 // every cached key, so only the tail of a split is masked.
 //
 // Work placement.  Sequence lengths live on the device, so the grid is sized
@@ -21,17 +22,30 @@
 // same number of units, and the same number of full 512-key splits up to one
 // per split level -- with lengths spread over a range, numbering units per
 // sequence instead leaves some XCDs with twice the bytes of others.  Empty
-// splits never launch; the combine kernel reads only the splits a sequence
-// has.
+// splits never launch; the merge reads only the splits a sequence has.
 //
 // Decode streams K/V once, so the kernel is built to keep bytes in flight:
 // an LDS ring of STAGES tiles of which STAGES-1 are being loaded while one is
 // consumed.  Every iteration issues exactly one tile's loads (tiles past the
 // end get an empty buffer descriptor and load nothing), so the wait count is a
-// constant.  With KG = 2 key groups, each wave takes half the keys of every
-// tile with its own running max/sum/O, and at the end the two key groups of
-// each head group are merged in LDS by their running maxima, exactly like two
-// disjoint key sets.
+// constant.
+//
+// Merge in the same launch.  The grid ends with one merge workgroup per
+// (sequence, kv head, slice of decode_merge_heads(D) query heads).  Workgroups
+// are dispatched in index order, so every unit is resident or done before a
+// merge workgroup takes a slot, and a merge workgroup only ever waits for
+// units.  A unit publishes its partial rows with device-coherent stores (sc1:
+// written through the XCD's L2, which other XCDs do not see), waits until they
+// are complete, and then counts itself in the arrival counter of each slice of
+// its head block (a device-scope atomic).  The merge workgroup of a slice
+// waits until its counter has counted every split of the sequence, resets it
+// to zero for the next call, reads the partials with device-coherent loads and
+// writes O and the LSE.  No cache-wide write-back or invalidate is involved.
+// The counters sit 64 bytes apart when the workspace header has room: polls
+// of many waiting workgroups on shared lines slowed the whole launch by 8 %
+// (they queue at the memory channel that holds the line).
+// The wait is bounded (kMergeSpin sleeps), so the launch always ends, even
+// over counters that were not zero when it started.
 #pragma once
 
 #include "fp8.hpp"
@@ -100,32 +114,81 @@ __device__ bool decode_unit(const DecodeParams &p, int u, int lane, int len0, in
   return false;  // not reached: r is below the count of level s
 }
 
-// HG head groups of 32 heads x KG key groups of BN/KG keys = HG*KG waves.
+// Sleeps a merge workgroup waits at most for its splits (s_sleep 2 is about
+// 128 clocks: tens of milliseconds in all, far beyond any unit's run time).
+constexpr int kMergeSpin = 1 << 20;
+
+// Merge workgroup m: the splits of (sequence b, kv head g, heads
+// [mb*MH, mb*MH + MH) of the group), one thread per 8 output columns of a head.
+template <int D>
+__device__ void decode_merge(const DecodeParams &p, int m) {
+  constexpr int MH = decode_merge_heads(D);
+  constexpr int CPR = D / 8;  // 8-column chunks per row
+  static_assert(MH * CPR == 256, "one chunk per thread");
+  const int per_b = p.h_kv * p.n_mblk;
+  const int b = m / per_b;
+  const int g = (m - b * per_b) / p.n_mblk;
+  const int mb = m - b * per_b - g * p.n_mblk;
+  const int n = decode_splits_of(p.kv_len, p.split, p.n_split, b);
+  if (threadIdx.x == 0) {
+    uint32_t *cnt = p.arrive + (int64_t)m * p.arrive_stride;
+    int it = 0;
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)n && ++it < kMergeSpin)
+      __builtin_amdgcn_s_sleep(2);
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const int h0 = mb * MH;  // first head of the slice inside the kv group
+  const int nh = min(MH, p.ratio - h0);
+  const int r = threadIdx.x / CPR, ch = threadIdx.x % CPR;
+  if (r >= nh) return;
+  const int64_t row0 = (int64_t)b * p.h_q + g * p.ratio + h0;  // partial row of the slice's first head
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(p.o_part + row0 * p.n_split * D, (uint32_t)((int64_t)nh * p.n_split * D * 2));
+  const uint32_t off = (uint32_t)(r * p.n_split * D * 2 + ch * 16);
+  const float *lp = p.lse_part + (row0 + r) * p.n_split;
+  const int head = g * p.ratio + h0 + r;
+  merge_parts<uint16_t, 16>(
+      n, [&](int i) { return __hip_atomic_load(lp + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
+      [&](int i) {
+        Vec8<uint16_t> v;
+        v.a = __builtin_amdgcn_raw_buffer_load_b128(rs, off + (uint32_t)(i * D * 2), 0, kDeviceCoherent);
+        return v;
+      },
+      p.o_out + b * p.o_sb + (int64_t)head * p.o_sh + ch * 8,
+      p.lse_out != nullptr && ch == 0 ? p.lse_out + b * p.lse_sb + head : nullptr);
+}
+
+// HG head groups of 32 heads = HG waves.
 // PAGED: K/V are read through the block table (one descriptor per DMA load,
 // see Tile::dma1_paged) instead of from a per-sequence contiguous range.
 // FP8: K/V are E4M3 codes with a per-kv-head scale (see fp8.hpp).
-template <int D, int HG, int KG, int BN, int STAGES, int OCC, bool PAGED = false, bool FP8 = false>
-__global__ __launch_bounds__(HG * KG * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+template <int D, int HG, int BN, int STAGES, int OCC, bool PAGED = false, bool FP8 = false>
+__global__ __launch_bounds__(HG * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_split_kernel(DecodeParams p) {
-  constexpr int NW = HG * KG;
-  using TD = Tile<D, NW, BN>;       // DMA geometry: all waves load one BN-key tile
-  using TC = Tile<D, NW, BN / KG>;  // MMA view: each wave computes on BN/KG keys of it
+  constexpr int NW = HG;
+  using TD = Tile<D, NW, BN>;  // DMA geometry: all waves load one BN-key tile
+  using TC = TD;               // MMA view: each wave computes on the whole tile for its heads
   using F8 = Fp8Tile<FP8 ? D : 128, NW, FP8 ? BN : 32>;
-  constexpr int BM = 32 * HG;       // query heads per workgroup
+  constexpr int BM = 32 * HG;  // query heads per workgroup
   constexpr int NDB = TC::NDB;
-  constexpr int MERGE_BYTES = KG > 1 ? HG * (NDB * 4 + 1) * 64 * 16 : 0;
   constexpr int RING_BYTES = STAGES * (FP8 ? F8::STAGE_BYTES : TD::STAGE_BYTES);
   constexpr int STORE_BYTES = BM * D * 2;  // partial tile staged for the whole-row stores
-  constexpr int SMEM_BYTES = RING_BYTES > MERGE_BYTES ? (RING_BYTES > STORE_BYTES ? RING_BYTES : STORE_BYTES)
-                                                      : MERGE_BYTES;
-  static_assert(STAGES >= 2 && (KG == 1 || KG == 2) && (BN / KG) % 32 == 0, "decode shape");
-  static_assert(!FP8 || (KG == 1 && !PAGED), "FP8 decode: one key group, contiguous cache");
+  constexpr int SMEM_BYTES = RING_BYTES > STORE_BYTES ? RING_BYTES : STORE_BYTES;
+  static_assert(STAGES >= 2 && BN % 32 == 0, "decode shape");
+  static_assert(!FP8 || !PAGED, "FP8 decode: contiguous cache");
+  static_assert(HG * 64 == 256 && BM % decode_merge_heads(D) == 0, "merge slices inside one head block");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_BYTES / 2];
+
+  if ((int)blockIdx.x >= p.unit_grid) {
+    decode_merge<D>(p, (int)blockIdx.x - p.unit_grid);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
-  const int hgrp = wave % HG, kgrp = wave / HG;
+  const int hgrp = wave;
 
   // Lengths and starts of the first 64 sequences are loaded once, side by
   // side, so the unit scan and this unit's key range wait for one load.
@@ -185,7 +248,7 @@ void decode_split_kernel(DecodeParams p) {
   if constexpr (FP8) {
     F8::init(fl, p.k_st, p.v_st, wave, lane, base, base + F8::TILE_BYTES);
   } else {
-    TC::init_mma(ml, base + kgrp * (BN / KG) * D * 2, base + TD::TILE_BYTES + kgrp * (BN / KG) * D * 2, lane);
+    TC::init_mma(ml, base, base + TD::TILE_BYTES, lane);
   }
 
   constexpr int STG = FP8 ? F8::STAGE_BYTES : TD::STAGE_BYTES;  // bytes per ring stage
@@ -202,7 +265,7 @@ void decode_split_kernel(DecodeParams p) {
   }
 
   float m = kNegInf, l = 0.0f;
-  if (p.sinks != nullptr && split == 0 && kgrp == 0) {  // the sink belongs to exactly one part
+  if (p.sinks != nullptr && split == 0) {  // the sink belongs to exactly one part
     m = p.sinks[head] * kLog2e;
     l = hi == 0 ? 1.0f : 0.0f;
   }
@@ -218,12 +281,12 @@ void decode_split_kernel(DecodeParams p) {
     const int nxt = t + STAGES - 1;
     load_tile(smem + (nxt % STAGES) * (STG / 2), nxt);
     const uint32_t stage_off = (t % STAGES) * STG;
-    const int j0 = t * BN + kgrp * (BN / KG);  // first key of this wave's part of the tile
-    if (wave_ok && j0 < n_keys) {
+    const int j0 = t * BN;  // first key of the tile
+    if (wave_ok) {
       f32x16 s[TC::NKB];
       if constexpr (FP8) F8::scores(s, qreg, fl, stage_off);
       else TC::scores(s, qreg, ml, stage_off);
-      if (j0 + BN / KG > n_keys) {
+      if (j0 + BN > n_keys) {
 #pragma unroll
         for (int kb = 0; kb < TC::NKB; ++kb)
 #pragma unroll
@@ -236,100 +299,72 @@ void decode_split_kernel(DecodeParams p) {
       else TC::values(o, pk, ml, stage_off);
     }
   }
-
-  // Merge the two key groups of each head group: (m, l, O) of key group 1
-  // goes through LDS to key group 0, which rescales both to the larger max.
   wait_vmcnt<0>();
-  if constexpr (KG > 1) {
-  __syncthreads();
-  f32x4 *xb = reinterpret_cast<f32x4 *>(smem) + hgrp * (NDB * 4 + 1) * 64;
-  if (kgrp == 1) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        xb[(db * 4 + q4) * 64 + lane] = f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2],
-                                               o[db][4 * q4 + 3]};
-    xb[NDB * 4 * 64 + lane] = f32x4{m, l, 0.0f, 0.0f};
-  }
-  __syncthreads();
-  if (kgrp == 1) return;
-  {
-    const f32x4 ml2 = xb[NDB * 4 * 64 + lane];
-    const float mb = ml2[0], lb = ml2[1];
-    const float mm = fmaxf(m, mb);
-    const float fa = (m == kNegInf) ? 0.0f : fast_exp2(m - mm);
-    const float fb = (mb == kNegInf) ? 0.0f : fast_exp2(mb - mm);
-    m = mm;
-    l = l * fa + lb * fb;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = xb[(db * 4 + q4) * 64 + lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[db][4 * q4 + e] = o[db][4 * q4 + e] * fa + v[e] * fb;
-      }
-  }
-  }
 
   const float lt = sum_across_halves(l);
   // FP8: the V scale multiplies every output column.
   const float inv = lt > 0.0f ? (FP8 ? p.v_scale[g] : 1.0f) / lt : 0.0f;
-  if (row_ok && hi == 0) p.lse_part[part] = lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  if (row_ok && hi == 0)
+    __hip_atomic_store(p.lse_part + part, lt > 0.0f ? (m + __log2f(lt)) * kLn2 : kNegInf, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   // Normalised partial output, bf16 (its rounding is far below the final bf16
   // rounding of O after the merge).  A lane holds pieces of one head's row,
   // so a store straight from the accumulators would touch 32 rows 8 bytes at
   // a time; the tile goes through the (now idle) K/V ring instead, with 16-byte
   // chunks XOR-swizzled by row, and every store then writes whole rows.
-  if constexpr (KG == 1) {
-    constexpr int NC = D / 8;              // 16-byte chunks per row
-    constexpr int SW = NC < 16 ? NC : 16;  // swizzle span
-    constexpr int RPI = 64 / NC;           // rows per store instruction
-    static_assert(STORE_BYTES <= SMEM_BYTES, "partial tile must fit in LDS");
-    __syncthreads();  // every wave is done with the last stage
-    char *xw = reinterpret_cast<char *>(smem) + hgrp * 32 * D * 2;
+  constexpr int NC = D / 8;              // 16-byte chunks per row
+  constexpr int SW = NC < 16 ? NC : 16;  // swizzle span
+  constexpr int RPI = 64 / NC;           // rows per store instruction
+  static_assert(STORE_BYTES <= SMEM_BYTES, "partial tile must fit in LDS");
+  __syncthreads();  // every wave is done with the last stage
+  char *xw = reinterpret_cast<char *>(smem) + hgrp * 32 * D * 2;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        u32x2 val;
-        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
-        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
-        const int chunk = db * 4 + gi;
-        *reinterpret_cast<u32x2 *>(xw + lr * D * 2 + (chunk ^ (lr % SW)) * 16 + 8 * hi) = val;
-      }
-    __syncthreads();
-    const int c = lane % NC;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = i * RPI + lane / NC;
-      const u32x4 val = *reinterpret_cast<const u32x4 *>(xw + r * D * 2 + (c ^ (r % SW)) * 16);
-      const int hr = hb * BM + hgrp * 32 + r;  // head inside the kv group
-      if (hr < p.ratio) {
-        const int64_t pr = ((int64_t)bi * p.h_q + g * p.ratio + hr) * p.n_split + split;
-        *reinterpret_cast<u32x4 *>(p.o_part + pr * D + c * 8) = val;
-      }
+    for (int gi = 0; gi < 4; ++gi) {
+      u32x2 val;
+      val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
+      val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
+      const int chunk = db * 4 + gi;
+      *reinterpret_cast<u32x2 *>(xw + lr * D * 2 + (chunk ^ (lr % SW)) * 16 + 8 * hi) = val;
     }
-  } else if (row_ok) {
-    uint16_t *op = p.o_part + part * D + 4 * hi;
+  __syncthreads();
+  // The head block's partial rows of this split, device-coherent: row h of
+  // the block at byte ((h * n_split) + split) * D * 2 of the descriptor.
+  const int64_t row0 = (int64_t)bi * p.h_q + g * p.ratio + hb * BM;
+  const int nh = min(BM, p.ratio - hb * BM);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(p.o_part + row0 * p.n_split * D, (uint32_t)((int64_t)nh * p.n_split * D * 2));
+  const int cc = lane % NC;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        u32x2 val;
-        val[0] = pack_bf16x2(o[db][4 * gi + 0] * inv, o[db][4 * gi + 1] * inv);
-        val[1] = pack_bf16x2(o[db][4 * gi + 2] * inv, o[db][4 * gi + 3] * inv);
-        *reinterpret_cast<u32x2 *>(op + db * 32 + 8 * gi) = val;
-      }
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / NC;
+    const u32x4 val = *reinterpret_cast<const u32x4 *>(xw + r * D * 2 + (cc ^ (r % SW)) * 16);
+    const int hr = hgrp * 32 + r;  // head inside the head block
+    if (hr < nh)
+      __builtin_amdgcn_raw_buffer_store_b128(val, rs, (uint32_t)((hr * p.n_split + split) * D * 2 + cc * 16), 0,
+                                             kDeviceCoherent);
+  }
+  // Arrival: once every wave's partial stores are complete, count this split
+  // in the counter of each merge slice of the head block.
+  if (p.arrive == nullptr) return;  // merged by a second kernel
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int SPB = BM / decode_merge_heads(D);  // merge slices per head block
+    const int mb0 = hb * SPB;
+    if (lane < SPB && mb0 + lane < p.n_mblk)
+      __hip_atomic_fetch_add(p.arrive + (((int64_t)bi * p.h_kv + g) * p.n_mblk + mb0 + lane) * p.arrive_stride, 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-template <int D, int HG, int KG, int BN, int STAGES, int OCC, bool PAGED = false, bool FP8 = false>
+// Grid: the units (decode_grid_size), then the merge workgroups.
+template <int D, int HG, int BN, int STAGES, int OCC, bool PAGED = false, bool FP8 = false>
 hipError_t launch_decode_split(const DecodeParams &p, hipStream_t stream) {
-  dim3 grid((unsigned)decode_grid_size(p.n_split, p.B, p.h_kv, p.n_hblk));
-  hipLaunchKernelGGL((decode_split_kernel<D, HG, KG, BN, STAGES, OCC, PAGED, FP8>), grid, dim3(HG * KG * 64), 0,
-                     stream, p);
+  const int64_t merges = (int64_t)p.B * p.h_kv * p.n_mblk;
+  dim3 grid((unsigned)(p.unit_grid + merges));
+  hipLaunchKernelGGL((decode_split_kernel<D, HG, BN, STAGES, OCC, PAGED, FP8>), grid, dim3(HG * 64), 0, stream, p);
   return hipGetLastError();
 }
 

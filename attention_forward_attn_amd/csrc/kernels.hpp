@@ -27,6 +27,11 @@ hipError_t prefill_d512_chunked(const PrefillParams &p, const PrefillChunks &ck,
 
 // Query heads per decode workgroup (0 if unsupported).
 int decode_block_rows(int d);
+// Split-KV decode and the merge of its splits, one launch: p.unit_grid unit
+// workgroups (decode_grid_size) then B * h_kv * n_mblk merge workgroups; the
+// p.arrive counters must be zero at launch and are left zero.  With
+// p.arrive = NULL and n_mblk = 0 only the partials are written (merged by
+// combine_bf16).
 hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s);
 // The same over a paged cache (p.block_table, p.page_shift, p.k_ps, p.v_ps set).
 hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s);
@@ -40,7 +45,8 @@ hipError_t decode_split_fp8(int d, const DecodeParams &p, hipStream_t s);
 int backward_block_rows();
 hipError_t backward(int d, const BwdParams &p, bool causal, hipStream_t s);
 
-// LSE merge of fp32 partials (public entry point) / of bf16 partials (decode).
+// LSE merge of fp32 partials (public entry point) / of bf16 partials (decode
+// shapes with more merge workgroups than the workspace header has counters).
 hipError_t combine(const CombineParams &p, hipStream_t s);
 hipError_t combine_bf16(const CombineParams &p, hipStream_t s);
 

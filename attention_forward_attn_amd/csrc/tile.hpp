@@ -90,6 +90,11 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   return (uint32_t)(uintptr_t)q;
 }
 
+// Cache-policy operand of the buffer load/store builtins that sets sc1: the
+// access is coherent at device scope (a store is written through the XCD's
+// L2, a load does not take a line another XCD may have changed from it).
+constexpr int kDeviceCoherent = 16;
+
 // Buffer descriptor over [base, base + bytes) (gfx9 raw buffer, stride 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);

@@ -151,8 +151,8 @@ class DecodeCase:
                               for n, t in self.sets[0].items()})
         self.sinks = base["sinks"].to(dev) if base["sinks"] is not None else None
         self.scale = 1.0 / math.sqrt(w.d)
-        self.ws = torch.empty(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
-                              dtype=torch.uint8, device=dev)
+        self.ws = afa.new_decode_workspace(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
+                                           dev)
         self.out = torch.empty((w.b, w.h_q, w.d), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((w.b, w.h_q), dtype=torch.float32, device=dev)
         self.bytes = decode_bytes(w, self.total)
@@ -553,8 +553,8 @@ class PagedDecodeCase(DecodeCase):
                               for n, t in self.sets[0].items()})
         self.sinks = base["sinks"].to(dev) if base["sinks"] is not None else None
         self.scale = 1.0 / math.sqrt(w.d)
-        self.ws = torch.empty(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
-                              dtype=torch.uint8, device=dev)
+        self.ws = afa.new_decode_workspace(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
+                                           dev)
         self.out = torch.empty((w.b, w.h_q, w.d), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((w.b, w.h_q), dtype=torch.float32, device=dev)
         self.bytes = decode_bytes(w, self.total)
@@ -597,8 +597,8 @@ class Fp8DecodeCase(DecodeCase):
             self.sets.append(st)
         self.sinks = base["sinks"].to(dev) if base["sinks"] is not None else None
         self.scale = 1.0 / math.sqrt(w.d)
-        self.ws = torch.empty(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
-                              dtype=torch.uint8, device=dev)
+        self.ws = afa.new_decode_workspace(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
+                                           dev)
         self.out = torch.empty((w.b, w.h_q, w.d), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((w.b, w.h_q), dtype=torch.float32, device=dev)
         self.bytes = decode_bytes(w, self.total)

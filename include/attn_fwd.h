@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 7
+#define ATTN_FWD_ABI_VERSION 8
 
 typedef enum {
   ATTN_OK = 0,
@@ -122,12 +122,22 @@ typedef struct {
  * split_size: keys per split (a multiple of 64, >= 64).  Split c of sequence
  *       bi covers keys [c*split_size, min((c+1)*split_size, kv_len[bi])).
  *
- * Two kernels run on `stream`: the split kernel writes normalised partial
- * outputs (rounded to bf16) and their fp32 LSE into the workspace, then the
- * combine kernel merges them in fp32 into o and lse.  The workspace is owned
- * by the caller, must stay allocated until the stream has run both kernels,
- * and must not be shared by calls that may overlap.  Supported: d in {64, 128, 256}; B, h_q, h_kv
- * >= 1, h_q % h_kv == 0.
+ * One kernel runs on `stream`: its split workgroups write normalised partial
+ * outputs (rounded to bf16) and their fp32 LSE into the workspace, and its
+ * merge workgroups, one per (sequence, kv head, slice of 2048/d query heads),
+ * wait until every split of their rows has arrived and merge them in fp32
+ * into o and lse.  The arrival counters sit in the first
+ * ATTN_DECODE_WORKSPACE_HEADER bytes of the workspace, at fixed places for
+ * every size: that header must be zero before the first call that uses the
+ * workspace, and every call leaves it zero, so one zeroed workspace serves any
+ * sequence of calls of any sizes that fit it.  (Over a header that is not
+ * zero the merge may read splits that have not arrived; its wait is bounded,
+ * so the kernel still ends.)  Shapes with more than ATTN_DECODE_WORKSPACE_HEADER
+ * / 4 merge workgroups (B * h_kv * ceil((h_q / h_kv) / (2048 / d))) are merged
+ * by a second kernel instead and do not use the header.  The workspace is
+ * owned by the caller, must be 16-byte aligned, must stay allocated until the
+ * stream has run the call's kernels, and must not be shared by calls that may
+ * overlap.  Supported: d in {64, 128, 256}; B, h_q, h_kv >= 1, h_q % h_kv == 0.
  */
 typedef struct {
   const void *q;
@@ -311,7 +321,9 @@ typedef struct {
   int64_t o_out_row_stride;
 } attn_combine_args;
 
-/* Bytes of device workspace attn_fwd_decode needs for these sizes (0 on invalid sizes). */
+/* Bytes of device workspace attn_fwd_decode needs for these sizes (0 on invalid
+ * sizes), the ATTN_DECODE_WORKSPACE_HEADER bytes of arrival counters included. */
+#define ATTN_DECODE_WORKSPACE_HEADER ((size_t)64 << 10)
 size_t attn_fwd_decode_workspace_size(int32_t B, int32_t h_q, int32_t d, int32_t max_kv_len,
                                       int32_t split_size);
 
@@ -371,18 +383,19 @@ attn_status attn_fwd_decode(const attn_decode_args *args, void *workspace, size_
  * Decode that allocates nothing, for callers that cannot allocate device
  * memory or take a workspace: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  The same operation, kernels and
- * results as attn_fwd_decode; the split partials go to a fixed region of
- * ATTN_DECODE_SCRATCH_BYTES that the library holds in device memory on every
- * GPU it runs on, from the moment the library's device code is loaded until
- * the process ends.  Sizes whose partials need more
+ * results as attn_fwd_decode; the workspace (arrival counters and split
+ * partials) is a fixed region of ATTN_DECODE_SCRATCH_BYTES that the library
+ * holds in device memory on every GPU it runs on, from the moment the
+ * library's device code is loaded until the process ends.  Sizes whose partials need more
  * (attn_fwd_decode_workspace_size above ATTN_DECODE_SCRATCH_BYTES) are
  * rejected with ATTN_ERR_WORKSPACE; 72 MiB holds B = 64 sequences of up to
  * 8192 keys with h_q = 128 and d = 256 in 512-key splits.  The caller still
  * owns q, k, v, kv_start, kv_len, o, lse and sinks.  All calls on one GPU
  * share its region: calls that may overlap on one GPU (on different streams,
  * or from different host threads without ordering) race and give wrong
- * results; calls ordered on one stream are safe.  Nothing in the region needs
- * to start at any value.  The first call on a device looks up the region's
+ * results; calls ordered on one stream are safe.  The region starts zeroed
+ * (static storage) and every call leaves its arrival counters zero.  The
+ * first call on a device looks up the region's
  * address with that device current (hipGetSymbolAddress; ATTN_ERR_HIP if it
  * fails).
  */

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     lib = afa.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
-    assert lib.attn_abi_version() == 7
+    assert lib.attn_abi_version() == 8
 
 
 def test_status_strings():
@@ -381,12 +381,18 @@ def test_decode_fp8_workspace_checks():
     assert lib.attn_fwd_decode_fp8(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4
 
 
+def test_decode_workspace_header_constant_matches_c_header():
+    text = open(os.path.join(ROOT, "include", "attn_fwd.h")).read()
+    m = re.search(r"#define ATTN_DECODE_WORKSPACE_HEADER \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == afa.DECODE_WORKSPACE_HEADER
+
+
 def test_decode_workspace_checks():
     lib = afa.load_library()
     a = good_decode()
     need = lib.attn_fwd_decode_workspace_size(4, 128, 128, 8192, 512)
-    # 4 sequences x 128 heads x 16 splits x (128 bf16 outputs + 1 fp32 LSE)
-    assert need >= 4 * 128 * 16 * (128 * 2 + 4)
+    # the counter header, then 4 sequences x 128 heads x 16 splits x (128 bf16 outputs + 1 fp32 LSE)
+    assert need == afa.DECODE_WORKSPACE_HEADER + 4 * 128 * 16 * (128 * 2 + 4)
     assert lib.attn_fwd_decode(ctypes.byref(a), None, need, None) == 6
     assert lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
     assert lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4

@@ -16,17 +16,29 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def run_decode(inp, max_len, split=512, sinks=None, d=None):
+def poisoned_ws(nbytes):
+    """A decode workspace of NaN bytes (partials) behind the zeroed counter header."""
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device=DEV)
+    ws[: afa.DECODE_WORKSPACE_HEADER].zero_()
+    return ws
+
+
+def header_left_zero(ws):
+    return not bool(ws[: afa.DECODE_WORKSPACE_HEADER].any())
+
+
+def run_decode(inp, max_len, split=512, sinks=None, d=None, ws=None):
     q, k, v = inp["q"].to(DEV), inp["k"].to(DEV), inp["v"].to(DEV)
     ks, kl = inp["kv_start"].to(DEV), inp["kv_len"].to(DEV)
     d = q.shape[-1]
-    ws = torch.full((afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split),),
-                    255, dtype=torch.uint8, device=DEV)  # NaN-poisoned partials
+    if ws is None:
+        ws = poisoned_ws(afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split))
     out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
     lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
     sd = None if sinks is None else sinks.to(DEV)
     afa.decode(q, k, v, ks, kl, max_len, sinks=sd, split_size=split, workspace=ws, out=out, lse=lse)
     torch.cuda.synchronize()
+    assert header_left_zero(ws)
     return out, lse
 
 
@@ -79,7 +91,8 @@ def test_decode_head_stride_zero_matches_mqa():
 
 
 @pytest.mark.parametrize("B,h_q,h_kv,d,split", [(70, 16, 2, 128, 256), (133, 8, 1, 64, 128),
-                                                (65, 32, 1, 256, 512)])
+                                                (65, 32, 1, 256, 512),
+                                                (300, 16, 4, 128, 256)])  # 1200 merges: counters 4 bytes apart
 def test_decode_many_sequences(B, h_q, h_kv, d, split):
     # more sequences than a wave has lanes, empty sequences, and a max_kv_len
     # above every length (trailing splits hold no keys)
@@ -93,6 +106,36 @@ def test_decode_many_sequences(B, h_q, h_kv, d, split):
     o_ref, l_ref = oracle.decode_ref(inp["q"], inp["k"], inp["v"], inp["kv_start"], inp["kv_len"],
                                      1 / math.sqrt(d))
     check(out, lse, o_ref, l_ref, f"B={B}")
+
+
+def test_decode_workspace_reused_across_sizes():
+    # one workspace, calls of different sizes in turn: the arrival counters sit
+    # at fixed places, so every call finds them zero and leaves them zero
+    big = make(70, 16, 2, 128, np.random.default_rng(5).integers(0, 2048, size=70).tolist(), 25)
+    small = make(3, 128, 1, 256, [700, 1, 1500], 26)
+    nbytes = max(afa.decode_workspace_size(70, 16, 128, 2048, 256), afa.decode_workspace_size(3, 128, 256, 1500, 256))
+    ws = poisoned_ws(nbytes)
+    for inp, max_len in ((big, 2048), (small, 1500), (big, 2048)):
+        d = inp["q"].shape[-1]
+        print(f"reused workspace B={inp['q'].shape[0]} d={d}", flush=True)
+        out, lse = run_decode(inp, max_len, 256, ws=ws)
+        o_ref, l_ref = oracle.decode_ref(inp["q"], inp["k"], inp["v"], inp["kv_start"], inp["kv_len"],
+                                         1 / math.sqrt(d))
+        check(out, lse, o_ref, l_ref, f"B={inp['q'].shape[0]}")
+
+
+def test_decode_more_merges_than_counters():
+    # B * h_kv merge workgroups above the header's 16384 counters: the splits
+    # are merged by the second kernel instead
+    B, h = 1040, 16
+    assert B * h > afa.DECODE_WORKSPACE_HEADER // 4
+    lens = np.random.default_rng(6).integers(0, 200, size=B)
+    lens[::9] = 0
+    inp = make(B, h, h, 64, lens.tolist(), 27)
+    print("decode with the combine kernel, B=1040 h=16 d=64", flush=True)
+    out, lse = run_decode(inp, 200, 64)
+    o_ref, l_ref = oracle.decode_ref(inp["q"], inp["k"], inp["v"], inp["kv_start"], inp["kv_len"], 1 / 8.0)
+    check(out, lse, o_ref, l_ref, "B=1040")
 
 
 def test_decode_split_size_invariance():
@@ -139,13 +182,13 @@ def run_paged(inp, max_len, split=512, sinks=None, table=None):
     bt = (inp["block_table"] if table is None else table).to(DEV)
     kl = inp["kv_len"].to(DEV)
     d = q.shape[-1]
-    ws = torch.full((afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split),),
-                    255, dtype=torch.uint8, device=DEV)  # NaN-poisoned partials
+    ws = poisoned_ws(afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split))
     out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
     lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
     sd = None if sinks is None else sinks.to(DEV)
     afa.decode_paged(q, kc, vc, bt, kl, max_len, sinks=sd, split_size=split, workspace=ws, out=out, lse=lse)
     torch.cuda.synchronize()
+    assert header_left_zero(ws)
     return out, lse
 
 
@@ -219,13 +262,13 @@ def run_fp8(inp, max_len, split=512, sinks=None):
     ksc, vsc = inp["k_scale"].to(DEV), inp["v_scale"].to(DEV)
     ks, kl = inp["kv_start"].to(DEV), inp["kv_len"].to(DEV)
     d = q.shape[-1]
-    ws = torch.full((afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split),),
-                    255, dtype=torch.uint8, device=DEV)  # NaN-poisoned partials
+    ws = poisoned_ws(afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split))
     out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
     lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
     sd = None if sinks is None else sinks.to(DEV)
     afa.decode_fp8(q, k8, v8, ksc, vsc, ks, kl, max_len, sinks=sd, split_size=split, workspace=ws, out=out, lse=lse)
     torch.cuda.synchronize()
+    assert header_left_zero(ws)
     return out, lse
 
 
