@@ -59,6 +59,25 @@ __device__ __forceinline__ void lds_row4(f32x4 (&v)[8], uint32_t addr) {
   if constexpr (I + 1 < 8) lds_row4<I + 1>(v, addr);
 }
 
+// Hooks that run element-wise work between the MMAs of a score product
+// (step<KK>, after k-step KK) or of a value product (vstep<T>, after k-step
+// T): that vector work then executes while the MMAs just issued are in
+// flight.  G groups of work are spread evenly over the N steps.
+template <int G, int N, typename F>
+struct GroupHook {
+  F &f;
+  template <int K>
+  __device__ __forceinline__ void run() {
+    static_assert(G % N == 0, "whole groups per step");
+#pragma unroll
+    for (int g = K * (G / N); g < (K + 1) * (G / N); ++g) f(g);
+  }
+  template <int KK>
+  __device__ __forceinline__ void step() { run<KK>(); }
+  template <int T_>
+  __device__ __forceinline__ void vstep() { run<T_>(); }
+};
+
 // Stores a transposed accumulator (lane = row, registers = head-dim columns)
 // times f as bf16 rows.
 template <int NDB>
@@ -285,44 +304,48 @@ void bwd_dkdv_kernel(BwdParams p) {
           (!WINDOW || i0 <= min(w_key0 + 31, p.s_k - 1) - off + p.window - 1)) {
         {
           const uint32_t so = cur * STAGE;
-          f32x16 s[T::NKB], dp[T::NKB];
-          T::scores(s, kreg, ln, so);                        // S = Q.K^T: rows in registers, keys in lanes
-          T::scores(dp, vreg, ln, so + 2 * T::TILE_BYTES);   // dP = dO.V^T
-          // LSE and D of the rows this lane's registers hold (4 consecutive rows per read)
-          const uint32_t aux = base + so + 4 * T::TILE_BYTES + (4 * hi) * 4;
-          f32x4 lv[4 * T::NKB], dv4[4 * T::NKB];  // index 4rb + q4: rows 32rb + 8q4 + 4hi .. +3
           static_assert(T::NKB == 2, "64-row tiles");
+          // LSE and D of the rows this lane's registers hold (4 consecutive
+          // rows per read; index 4rb + q4: rows 32rb + 8q4 + 4hi .. +3), read
+          // first: LDS reads complete in order, so they have landed once the
+          // score product's own operand waits have passed.
+          const uint32_t aux = base + so + 4 * T::TILE_BYTES + (4 * hi) * 4;
+          f32x4 lv[4 * T::NKB], dv4[4 * T::NKB];
           lds_row4<0>(lv, aux);
           lds_row4<0>(dv4, aux + BN * 4);
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          f32x16 s[T::NKB], dp[T::NKB];
+          T::scores(s, kreg, ln, so);  // S = Q.K^T: rows in registers, keys in lanes
+          tie8(lv, 8);                 // behind the last operand wait of the product above
+          tie8(dv4, 8);
+          // Group g = 4rb + q4 of a lane's values: rows i0 + 32rb + 8q4 + 4hi + e
+          // in registers 4q4 + e of block rb.
+          auto visible = [&](int r) {
+            return r < p.s_q && key_ok && (!CAUSAL || key <= r + off) && (!WINDOW || key >= r + off - p.window + 1);
+          };
+          auto p_group = [&](int g) {  // P = exp(scale*S - LSE) over the visible pairs, into s
+            const int rb = g >> 2, q4 = g & 3, r4 = i0 + 32 * rb + 8 * q4 + 4 * hi;
 #pragma unroll
-          for (int rb = 0; rb < T::NKB; ++rb)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              // rows i0 + 32rb + 8q4 + 4hi + 0..3 hold registers 4q4..4q4+3
-              const int r4 = i0 + 32 * rb + 8 * q4 + 4 * hi;
-              const f32x4 l4 = lv[4 * rb + q4];
-              const f32x4 d4 = dv4[4 * rb + q4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = r4 + e;
-                const bool vis = r < p.s_q && key_ok && (!CAUSAL || key <= r + off) &&
-                                 (!WINDOW || key >= r + off - p.window + 1);
-                float pv = 0.0f, dsv = 0.0f;
-                if (vis) {
-                  const float l = l4[e];
-                  pv = l == kNegInf ? 0.0f : fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -l * kLog2e));
-                  dsv = pv * (dp[rb][4 * q4 + e] - d4[e]);
-                }
-                s[rb][4 * q4 + e] = pv;
-                dp[rb][4 * q4 + e] = dsv;
-              }
+            for (int e = 0; e < 4; ++e) {
+              const float l = lv[g][e];
+              const float pv = fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -l * kLog2e));
+              s[rb][4 * q4 + e] = visible(r4 + e) && l != kNegInf ? pv : 0.0f;
             }
+          };
+          auto ds_group = [&](int g) {  // dS = P * (dP - D), into dp
+            const int rb = g >> 2, q4 = g & 3;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[rb][4 * q4 + e] = s[rb][4 * q4 + e] * (dp[rb][4 * q4 + e] - dv4[g][e]);
+          };
+          // dP = dO.V^T, with P computed between its MMAs
+          GroupHook<4 * T::NKB, T::NKK, decltype(p_group)> hp{p_group};
+          T::scores(dp, vreg, ln, so + 2 * T::TILE_BYTES, hp);
           u32x4 pp[T::NPV], pd[T::NPV];
           pack_operand(s, pp);
+          // dV^T += dO^T . P, with dS computed between its MMAs
+          GroupHook<4 * T::NKB, T::NPV, decltype(ds_group)> hd{ds_group};
+          T::values(dv, pp, ln, so + 2 * T::TILE_BYTES, hd);
           pack_operand(dp, pd);
-          T::values(dv, pp, ln, so + 2 * T::TILE_BYTES);  // dV^T += dO^T . P
-          T::values(dk, pd, ln, so);                        // dK^T += Q^T . dS
+          T::values(dk, pd, ln, so);  // dK^T += Q^T . dS
         }
       }
     }
