@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     decode_fp8,
     decode_noalloc,
     decode_paged,
+    decode_paged_fp8,
     decode_workspace_size,
     load_library,
     new_decode_workspace,

@@ -96,6 +96,25 @@ class DecodeFp8Args(ctypes.Structure):
     ]
 
 
+class DecodePagedFp8Args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("kv_len", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("sinks", ctypes.c_void_p),
+        ("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32), ("split_size", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+        ("bt_stride", ctypes.c_int64),
+        ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("k_ps", ctypes.c_int64), ("k_ts", ctypes.c_int64), ("k_sh", ctypes.c_int64),
+        ("v_ps", ctypes.c_int64), ("v_ts", ctypes.c_int64), ("v_sh", ctypes.c_int64),
+        ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("lse_sb", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+    ]
+
+
 class BwdArgs(ctypes.Structure):
     _fields_ = [
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
@@ -153,6 +172,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_fwd_decode_fp8.argtypes = [ctypes.POINTER(DecodeFp8Args), ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]
     lib.attn_fwd_decode_fp8.restype = ctypes.c_int
+    lib.attn_fwd_decode_paged_fp8.argtypes = [ctypes.POINTER(DecodePagedFp8Args), ctypes.c_void_p, ctypes.c_size_t,
+                                              ctypes.c_void_p]
+    lib.attn_fwd_decode_paged_fp8.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int32] * 3
@@ -510,6 +532,69 @@ def decode_fp8(q, k8, v8, k_scale, v_scale, kv_start, kv_len, max_kv_len: int, *
     a.scale = scale
     _check(lib.attn_fwd_decode_fp8(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+@_on_stream
+def decode_paged_fp8(q, k8_cache, v8_cache, k_scale, v_scale, block_table, kv_len, max_kv_len: int, *,
+                     scale: float | None = None, sinks=None, split_size: int = 512, workspace=None, out=None,
+                     lse=None, return_lse: bool = True, stream=None):
+    """Single-token decode over a paged FP8 (E4M3) KV cache with per-kv-head scales.
+
+    q: bf16 [B, h_q, d]; k8_cache, v8_cache: uint8 E4M3 codes [n_pages,
+    page_size, h_kv, d] (page, token and head strides multiples of 16 bytes,
+    unit head-dim stride); k_scale, v_scale: fp32 [h_kv]; block_table: int32
+    [B, max_pages]; kv_len: int32 [B].  Returns (O bf16 [B, h_q, d], LSE fp32
+    [B, h_q] or None).
+    """
+    import torch
+
+    lib = load_library()
+    _require_cuda_bf16("q", q, 3)
+    for name, t in (("k8_cache", k8_cache), ("v8_cache", v8_cache)):
+        if not t.is_cuda or t.dtype != torch.uint8 or t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be a uint8 device tensor [n_pages, page_size, h_kv, d] with unit last stride")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [B, max_pages] with unit column stride")
+    if kv_len.dtype != torch.int32:
+        raise ValueError("kv_len must be int32")
+    if k8_cache.shape != v8_cache.shape:
+        raise ValueError("k8_cache and v8_cache must have the same shape")
+    B, h_q, d = q.shape
+    n_pages, page_size, h_kv = k8_cache.shape[0], k8_cache.shape[1], k8_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = int(lib.attn_fwd_decode_workspace_size(B, h_q, d, max_kv_len, split_size))
+    if workspace is None:
+        workspace = new_decode_workspace(need, q.device)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, h_q), dtype=torch.float32, device=q.device)
+    if lse is not None and lse.stride(-1) != 1:
+        raise ValueError("lse must have unit stride along the heads")
+    a = DecodePagedFp8Args()
+    a.q, a.k, a.v = q.data_ptr(), k8_cache.data_ptr(), v8_cache.data_ptr()
+    a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    a.block_table, a.kv_len = block_table.data_ptr(), kv_len.data_ptr()
+    a.o = out.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.B, a.h_q, a.h_kv, a.d = B, h_q, h_kv, d
+    a.max_kv_len, a.split_size = int(max_kv_len), int(split_size)
+    a.page_size, a.n_pages = int(page_size), int(n_pages)
+    a.bt_stride = block_table.stride(0)
+    a.q_sb, a.q_sh = q.stride(0), q.stride(1)
+    a.k_ps, a.k_ts, a.k_sh = k8_cache.stride(0), k8_cache.stride(1), k8_cache.stride(2)
+    a.v_ps, a.v_ts, a.v_sh = v8_cache.stride(0), v8_cache.stride(1), v8_cache.stride(2)
+    a.o_sb, a.o_sh = out.stride(0), out.stride(1)
+    a.lse_sb = lse.stride(0) if lse is not None else 0
+    a.scale = scale
+    _check(lib.attn_fwd_decode_paged_fp8(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 

@@ -53,10 +53,28 @@ attn_status hip_fail(hipError_t e, const char *what) {
   return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Page geometry and block-table checks of the paged decode entry points
+// (split_size already checked).
+attn_status check_pages(int32_t ps, int32_t split_size, int32_t n_pages, int64_t bt_stride, int32_t max_kv_len) {
+  if (ps < 16 || (ps & (ps - 1)) != 0 || ps > split_size || split_size / ps > 64)
+    return fail(ATTN_ERR_SHAPE,
+                "page_size must be a power of two in [16, split_size] with at most 64 pages per split (got %d)", ps);
+  // Every split must start on a page boundary: the kernel maps key j of a
+  // split to slot j % page_size of the split's (j / page_size)-th page.
+  if (split_size % ps != 0)
+    return fail(ATTN_ERR_SHAPE, "split_size (%d) must be a multiple of page_size (%d)", split_size, ps);
+  if (n_pages < 1) return fail(ATTN_ERR_SHAPE, "n_pages must be >= 1");
+  const int64_t max_pages = ((int64_t)max_kv_len + ps - 1) / ps;
+  if (bt_stride < max_pages)
+    return fail(ATTN_ERR_STRIDE, "bt_stride (%lld) must be >= ceil(max_kv_len / page_size) = %lld",
+                (long long)bt_stride, (long long)max_pages);
+  return ATTN_OK;
+}
+
 // Shared tail of the dense, paged and FP8 decode entry points (arguments
 // already validated; p carries the K/V addressing; kind 0 = contiguous bf16
-// cache, 1 = paged, 2 = FP8): grid check, workspace layout and the one launch
-// of the split kernel with its merge.
+// cache, 1 = paged, 2 = FP8, 3 = paged FP8): grid check, workspace layout and
+// the one launch of the split kernel with its merge.
 attn_status run_decode(attn::DecodeParams &p, const int32_t *kv_len, const float *sinks, void *o, float *lse,
                        int32_t B, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_kv_len, int32_t split_size,
                        int64_t q_sb, int64_t q_sh, int64_t o_sb, int64_t o_sh, int64_t lse_sb, float scale,
@@ -103,6 +121,7 @@ attn_status run_decode(attn::DecodeParams &p, const int32_t *kv_len, const float
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = kind == 1   ? attn::decode_split_paged(d, p, s)
                  : kind == 2 ? attn::decode_split_fp8(d, p, s)
+                 : kind == 3 ? attn::decode_split_paged_fp8(d, p, s)
                              : attn::decode_split(d, p, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (fused) return ok();
@@ -573,7 +592,7 @@ attn_status attn_fwd_decode_fp8(const attn_decode_fp8_args *a, void *workspace, 
     return fail(ATTN_ERR_SHAPE, "need B, h_q, h_kv >= 1");
   if (a->h_q % a->h_kv != 0)
     return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
-  if (a->d != 128) return fail(ATTN_ERR_SHAPE, "FP8 decode supports d = 128 (got %d)", a->d);
+  if (a->d != 128 && a->d != 256) return fail(ATTN_ERR_SHAPE, "FP8 decode supports d = 128 or 256 (got %d)", a->d);
   if (a->max_kv_len < 0) return fail(ATTN_ERR_SHAPE, "max_kv_len must be >= 0");
   if (a->split_size < 64 || a->split_size % 64 != 0)
     return fail(ATTN_ERR_SHAPE, "split_size must be a positive multiple of 64 (got %d)", a->split_size);
@@ -628,18 +647,8 @@ attn_status attn_fwd_decode_paged(const attn_decode_paged_args *a, void *workspa
   if (a->split_size < 64 || a->split_size % 64 != 0)
     return fail(ATTN_ERR_SHAPE, "split_size must be a positive multiple of 64 (got %d)", a->split_size);
   const int ps = a->page_size;
-  if (ps < 16 || (ps & (ps - 1)) != 0 || ps > a->split_size || a->split_size / ps > 64)
-    return fail(ATTN_ERR_SHAPE,
-                "page_size must be a power of two in [16, split_size] with at most 64 pages per split (got %d)", ps);
-  // Every split must start on a page boundary: the kernel maps key j of a
-  // split to slot j % page_size of the split's (j / page_size)-th page.
-  if (a->split_size % ps != 0)
-    return fail(ATTN_ERR_SHAPE, "split_size (%d) must be a multiple of page_size (%d)", a->split_size, ps);
-  if (a->n_pages < 1) return fail(ATTN_ERR_SHAPE, "n_pages must be >= 1");
-  const int64_t max_pages = ((int64_t)a->max_kv_len + ps - 1) / ps;
-  if (a->bt_stride < max_pages)
-    return fail(ATTN_ERR_STRIDE, "bt_stride (%lld) must be >= ceil(max_kv_len / page_size) = %lld",
-                (long long)a->bt_stride, (long long)max_pages);
+  const attn_status pst = check_pages(ps, a->split_size, a->n_pages, a->bt_stride, a->max_kv_len);
+  if (pst != ATTN_OK) return pst;
   if (!(std::isfinite(a->scale) && a->scale > 0.0f))
     return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
   if (!a->q || !a->k || !a->v || !a->o || !a->block_table || !a->kv_len)
@@ -673,6 +682,61 @@ attn_status attn_fwd_decode_paged(const attn_decode_paged_args *a, void *workspa
   p.n_pages = a->n_pages;
   return run_decode(p, a->kv_len, a->sinks, a->o, a->lse, a->B, a->h_q, a->h_kv, a->d, a->max_kv_len,
                     a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, 1, workspace,
+                    stream);
+}
+
+attn_status attn_fwd_decode_paged_fp8(const attn_decode_paged_fp8_args *a, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  if (a == nullptr) return fail(ATTN_ERR_NULL, "args is NULL");
+  if (a->B < 1 || a->h_q < 1 || a->h_kv < 1)
+    return fail(ATTN_ERR_SHAPE, "need B, h_q, h_kv >= 1");
+  if (a->h_q % a->h_kv != 0)
+    return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
+  if (a->d != 128 && a->d != 256) return fail(ATTN_ERR_SHAPE, "FP8 decode supports d = 128 or 256 (got %d)", a->d);
+  if (a->max_kv_len < 0) return fail(ATTN_ERR_SHAPE, "max_kv_len must be >= 0");
+  if (a->split_size < 64 || a->split_size % 64 != 0)
+    return fail(ATTN_ERR_SHAPE, "split_size must be a positive multiple of 64 (got %d)", a->split_size);
+  const int ps = a->page_size;
+  const attn_status pst = check_pages(ps, a->split_size, a->n_pages, a->bt_stride, a->max_kv_len);
+  if (pst != ATTN_OK) return pst;
+  if (!(std::isfinite(a->scale) && a->scale > 0.0f))
+    return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+  if (!a->q || !a->k || !a->v || !a->o || !a->block_table || !a->kv_len || !a->k_scale || !a->v_scale)
+    return fail(ATTN_ERR_NULL, "q, k, v, o, block_table, kv_len, k_scale and v_scale must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(ATTN_ERR_ALIGN, "q, k, v, o must be 16-byte aligned");
+  if (!aligned4(a->block_table) || !aligned4(a->kv_len) || !aligned4(a->k_scale) || !aligned4(a->v_scale) ||
+      (a->lse && !aligned4(a->lse)) || (a->sinks && !aligned4(a->sinks)))
+    return fail(ATTN_ERR_ALIGN, "block_table, kv_len, scales, lse and sinks must be 4-byte aligned");
+  const int64_t st[] = {a->q_sb, a->q_sh, a->o_sb, a->o_sh};
+  for (int64_t s : st)
+    if (!bf16_stride_ok(s)) return fail(ATTN_ERR_STRIDE, "bf16 strides must be non-negative multiples of 8 elements");
+  const int64_t cst[] = {a->k_ps, a->k_ts, a->k_sh, a->v_ps, a->v_ts, a->v_sh};
+  for (int64_t s : cst)
+    if (s < 0 || s % 16 != 0) return fail(ATTN_ERR_STRIDE, "FP8 cache strides must be non-negative multiples of 16 bytes");
+  if (a->lse && a->lse_sb < 0) return fail(ATTN_ERR_STRIDE, "lse_sb must be >= 0");
+  if (a->k_ts >= kMaxRowStride || a->v_ts >= kMaxRowStride)
+    return fail(ATTN_ERR_STRIDE, "k/v token strides must be below 2^24 bytes");
+  const size_t need = attn_fwd_decode_workspace_size(a->B, a->h_q, a->d, a->max_kv_len, a->split_size);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+  attn::DecodeParams p{};
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k = reinterpret_cast<const uint16_t *>(a->k);  // byte addressing inside the kernel
+  p.v = reinterpret_cast<const uint16_t *>(a->v);
+  p.block_table = a->block_table;
+  p.bt_stride = a->bt_stride;
+  p.k_ps = a->k_ps; p.k_st = a->k_ts; p.k_sh = a->k_sh;
+  p.v_ps = a->v_ps; p.v_st = a->v_ts; p.v_sh = a->v_sh;
+  p.page_shift = __builtin_ctz((unsigned)ps);
+  p.n_pages = a->n_pages;
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  return run_decode(p, a->kv_len, a->sinks, a->o, a->lse, a->B, a->h_q, a->h_kv, a->d, a->max_kv_len,
+                    a->split_size, a->q_sb, a->q_sh, a->o_sb, a->o_sh, a->lse_sb, a->scale, 3, workspace,
                     stream);
 }
 

@@ -24,8 +24,19 @@ hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s) {
 }
 
 hipError_t decode_split_fp8(int d, const DecodeParams &p, hipStream_t s) {
-  if (d != 128) return hipErrorInvalidValue;
-  return launch_decode_split<128, 4, 32, 2, 3, false, true>(p, s);
+  switch (d) {
+    case 128: return launch_decode_split<128, 4, 32, 2, 3, false, true>(p, s);
+    case 256: return launch_decode_split<256, 4, 32, 2, 2, false, true>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t decode_split_paged_fp8(int d, const DecodeParams &p, hipStream_t s) {
+  switch (d) {
+    case 128: return launch_decode_split<128, 4, 32, 2, 3, true, true>(p, s);
+    case 256: return launch_decode_split<256, 4, 32, 2, 2, true, true>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t combine(const CombineParams &p, hipStream_t s) { return launch_combine<float>(p, s); }

@@ -162,7 +162,8 @@ __device__ void decode_merge(const DecodeParams &p, int m) {
 // HG head groups of 32 heads = HG waves.
 // PAGED: K/V are read through the block table (one descriptor per DMA load,
 // see Tile::dma1_paged) instead of from a per-sequence contiguous range.
-// FP8: K/V are E4M3 codes with a per-kv-head scale (see fp8.hpp).
+// FP8: K/V are E4M3 codes with a per-kv-head scale (see fp8.hpp); with PAGED
+// as well, the codes are read through the block table.
 template <int D, int HG, int BN, int STAGES, int OCC, bool PAGED = false, bool FP8 = false>
 __global__ __launch_bounds__(HG * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_split_kernel(DecodeParams p) {
@@ -176,7 +177,6 @@ void decode_split_kernel(DecodeParams p) {
   constexpr int STORE_BYTES = BM * D * 2;  // partial tile staged for the whole-row stores
   constexpr int SMEM_BYTES = RING_BYTES > STORE_BYTES ? RING_BYTES : STORE_BYTES;
   static_assert(STAGES >= 2 && BN % 32 == 0, "decode shape");
-  static_assert(!FP8 || !PAGED, "FP8 decode: contiguous cache");
   static_assert(HG * 64 == 256 && BM % decode_merge_heads(D) == 0, "merge slices inside one head block");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_BYTES / 2];
 
@@ -219,8 +219,8 @@ void decode_split_kernel(DecodeParams p) {
   const uint16_t *kbase = p.k + (PAGED ? 0 : (start + kbeg) * p.k_st) + g * p.k_sh;
   const uint16_t *vbase = p.v + (PAGED ? 0 : (start + kbeg) * p.v_st) + g * p.v_sh;
   // FP8: the cache is addressed in bytes (strides count bytes).
-  const uint8_t *kbase8 = reinterpret_cast<const uint8_t *>(p.k) + (start + kbeg) * p.k_st + g * p.k_sh;
-  const uint8_t *vbase8 = reinterpret_cast<const uint8_t *>(p.v) + (start + kbeg) * p.v_st + g * p.v_sh;
+  const uint8_t *kbase8 = reinterpret_cast<const uint8_t *>(p.k) + (PAGED ? 0 : (start + kbeg) * p.k_st) + g * p.k_sh;
+  const uint8_t *vbase8 = reinterpret_cast<const uint8_t *>(p.v) + (PAGED ? 0 : (start + kbeg) * p.v_st) + g * p.v_sh;
   const int n_keys = max(kend - kbeg, 0);
   int pg = 0;
   if constexpr (PAGED) {
@@ -235,7 +235,10 @@ void decode_split_kernel(DecodeParams p) {
   if constexpr (PAGED) TD::init_dma_paged(dl, p.k_st, p.v_st, wave, lane);
   else TD::init_dma(dl, p.k_st, p.v_st, wave, lane);
   auto load_tile = [&](uint16_t *stage, int t) {
-    if constexpr (FP8)
+    if constexpr (FP8 && PAGED)
+      F8::dma_paged(fl, reinterpret_cast<uint8_t *>(stage), kbase8, p.k_st, p.k_ps, vbase8, p.v_st, p.v_ps, pg,
+                    p.page_shift, p.n_pages, t * BN, n_keys, wave);
+    else if constexpr (FP8)
       F8::dma(fl, reinterpret_cast<uint8_t *>(stage), kbase8, p.k_st, vbase8, p.v_st, t * BN, n_keys, wave);
     else if constexpr (PAGED)
       TD::dma_paged(dl, stage, kbase, p.k_st, p.k_ps, vbase, p.v_st, p.v_ps, pg, p.page_shift, p.n_pages, t * BN,
@@ -247,6 +250,7 @@ void decode_split_kernel(DecodeParams p) {
   const uint32_t base = lds_offset(smem);
   if constexpr (FP8) {
     F8::init(fl, p.k_st, p.v_st, wave, lane, base, base + F8::TILE_BYTES);
+    if constexpr (PAGED) F8::init_dma_paged(fl, p.k_st, p.v_st, wave, lane);
   } else {
     TC::init_mma(ml, base, base + TD::TILE_BYTES, lane);
   }

@@ -1,9 +1,9 @@
-// FP8 (E4M3) K/V tiles for the split-KV decode at head dim 128.
+// FP8 (E4M3) K/V tiles for the split-KV decode at head dims 128 and 256.
 //
 // The cache holds 8-bit codes; a tile is BN keys x D bytes in LDS, rows of D
-// bytes whose 16-byte chunks are XOR-swizzled by row (chunk ^ ((r ^ r>>2) & 7),
-// which keeps both operand read patterns below at two LDS passes per
-// instruction, the minimum for 512 bytes).  Operands are widened to bf16 in
+// bytes whose 16-byte chunks are XOR-swizzled by row (chunk ^ ((r ^ r>>2) &
+// (D/16 - 1)), which keeps both operand read patterns below at two LDS passes
+// per instruction, the minimum for 512 bytes).  Operands are widened to bf16 in
 // registers after the LDS read (v_cvt_scalef32_pk_bf16_fp8 with scale 1;
 // every E4M3 value is exactly a bf16 value) and the MMAs are the bf16 ones of
 // the tile engine, so only the K/V byte traffic changes.  The per-kv-head
@@ -45,19 +45,27 @@ __device__ __forceinline__ u32x4 widen_fp8x8(u32x2 v) {
 
 template <int D, int NW, int BN>
 struct Fp8Tile {
-  static_assert(D == 128 && BN == 32, "FP8 tiles: head dim 128, 32-key tiles");
+  static_assert((D == 128 || D == 256) && BN == 32, "FP8 tiles: head dim 128 or 256, 32-key tiles");
   static constexpr int CH = D / 16;  // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * D;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K + V
   static constexpr int LOADS = TILE_BYTES / 1024 / NW;  // 1-KiB DMA loads per wave per tile
   static_assert(LOADS * 1024 * NW == TILE_BYTES, "tile must split into whole 1-KiB wave loads");
   static constexpr int NKB = BN / 32, NDB = D / 32, NKK = D / 16, NPV = BN / 16;
-  __device__ static __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 7; }
+  static constexpr int WIN = 8;  // LDS operand reads in flight
+  // Chunk swizzle of row r: both read patterns below then take two LDS passes
+  // per instruction, the minimum for 512 bytes (a CPU count of bank use over
+  // 64 banks of 4 bytes; at D = 256 a 3-bit swizzle would take four).
+  __device__ static __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & (CH - 1); }
 
+  // Operand addresses are formed per read from a row base and the row's
+  // swizzle (the chunk index kk ^ swizzle has no per-lane constant stride).
   struct Lane {
     uint32_t kg[LOADS], vg[LOADS];  // global byte offsets of this lane's DMA chunks (tile-relative)
-    uint32_t kl[NKK];               // LDS address of the K operand of k-step kk
-    uint32_t vl[NDB][2];            // LDS address of the V^T operand of block db, 16-key step parity
+    uint32_t krow;                  // LDS address of this lane's K row (half hi), chunk 0
+    uint32_t ksw;                   // its swizzle
+    uint32_t vrow[2], vsw[2];       // V^T operand: key row address and swizzle per 16-key step parity
+    uint32_t vcol;                  // 16-byte column group (g & 1) of this lane
   };
 
   // kbase/vbase: LDS byte addresses of the K and V tiles of stage 0.
@@ -72,8 +80,8 @@ struct Fp8Tile {
     }
     // K: lane (key lr, half hi) reads head-dim bytes 16kk + 8hi .. +7 of key lr.
     const int lr = lane & 31, hi = lane >> 5;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) ln.kl[kk] = kbase + lr * D + ((kk ^ swz(lr)) * 16) + 8 * hi;
+    ln.krow = kbase + lr * D + 8 * hi;
+    ln.ksw = (uint32_t)swz(lr);
     // V: in 16-lane group g, lane 2e+h points at half h of the 16 bytes of
     // head-dim columns 32db + 16(g&1) .. +15 of the key that the P operand
     // holds in k slot 8(g>>1) + e: 16T + 8(e>>2) + 4(g>>1) + (e&3).
@@ -81,10 +89,16 @@ struct Fp8Tile {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int key = 16 * p + 8 * (e >> 2) + 4 * (g >> 1) + (e & 3);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        ln.vl[db][p] = vbase + key * D + (((2 * db + (g & 1)) ^ swz(key)) * 16) + 8 * h;
+      ln.vrow[p] = vbase + key * D + 8 * h;
+      ln.vsw[p] = (uint32_t)swz(key);
     }
+    ln.vcol = (uint32_t)(g & 1);
+  }
+  __device__ static __forceinline__ uint32_t kaddr(const Lane &ln, int kk, uint32_t stage_off) {
+    return ln.krow + ((((uint32_t)kk ^ ln.ksw)) << 4) + stage_off;
+  }
+  __device__ static __forceinline__ uint32_t vaddr(const Lane &ln, int db, int t, uint32_t stage_off) {
+    return ln.vrow[t & 1] + ((((uint32_t)(2 * db) + ln.vcol) ^ ln.vsw[t & 1]) << 4) + stage_off;
   }
 
   // This wave's DMA share of the tile of keys [j0, j0 + BN) into `stage`
@@ -105,41 +119,86 @@ struct Fp8Tile {
                                                ln.vg[u], 0, 0, 0);
   }
 
-  // S^T = K . Q^T for the staged tile (all reads issued, then consumed in order).
+  // Paged caches: a 1-KiB load holds RPL whole rows, which always sit in one
+  // page (pages hold at least 16 rows), so each load gets its own descriptor
+  // and the lane offsets count from the load's first row.
+  static constexpr int RPL = 1024 / D;  // rows per load
+  __device__ static __forceinline__ void init_dma_paged(Lane &ln, int64_t k_rs, int64_t v_rs, int w, int lane) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int pch = (u * NW + w) * 64 + lane;
+      const int r = pch / CH, rl = lane / CH;  // row in the tile, row in the load
+      const int c = (pch % CH) ^ swz(r);
+      ln.kg[u] = (uint32_t)(rl * k_rs) + (uint32_t)(c * 16);
+      ln.vg[u] = (uint32_t)(rl * v_rs) + (uint32_t)(c * 16);
+    }
+  }
+  // This wave's loads of the tile whose first key is jt (keys counted from
+  // the start of a run of pages): key j of the run is row j % 2^shift of page
+  // readlane(pg, j >> shift), at head + page * page_rs + row * rs (bytes).
+  // Rows at or past nkeys, and pages outside [0, n_pages), read as zero
+  // without touching memory.
+  __device__ static __forceinline__ void dma_paged(const Lane &ln, uint8_t *stage, const uint8_t *khead,
+                                                   int64_t k_rs, int64_t k_page_rs, const uint8_t *vhead,
+                                                   int64_t v_rs, int64_t v_page_rs, int pg, int shift, int n_pages,
+                                                   int jt, int nkeys, int w) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int key = jt + (u * NW + w) * RPL;
+      const int nv = min(nkeys - key, RPL);
+      const int page = __builtin_amdgcn_readlane(pg, min(key >> shift, 63));
+      const bool ok = nv > 0 && (uint32_t)page < (uint32_t)n_pages;
+      const int64_t slot = key & ((1 << shift) - 1);
+      const uint8_t *kb = khead + (int64_t)page * k_page_rs + slot * k_rs;
+      const uint8_t *vb = vhead + (int64_t)page * v_page_rs + slot * v_rs;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(ok ? kb : khead, ok ? (uint32_t)((nv - 1) * k_rs + D) : 0u),
+                                               (lds_void *)(stage + (u * NW + w) * 1024), 16, ln.kg[u], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(ok ? vb : vhead, ok ? (uint32_t)((nv - 1) * v_rs + D) : 0u),
+                                               (lds_void *)(stage + TILE_BYTES + (u * NW + w) * 1024), 16,
+                                               ln.vg[u], 0, 0, 0);
+    }
+  }
+
+  // S^T = K . Q^T for the staged tile; WIN operand reads stay in flight.
   __device__ static __forceinline__ void scores(f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK], const Lane &ln,
                                                 uint32_t stage_off) {
     u32x2 a[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) a[kk] = ds_read_b64<0>(ln.kl[kk] + stage_off);
+    for (int kk = 0; kk < (NKK < WIN ? NKK : WIN); ++kk) a[kk] = ds_read_b64<0>(kaddr(ln, kk, stage_off));
     s[0] = f32x16{};
-    score_step<0>(s, qreg, a);
+    score_step<0>(s, qreg, a, ln, stage_off);
   }
   template <int KK>
-  __device__ static __forceinline__ void score_step(f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK], u32x2 (&a)[NKK]) {
-    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(NKK - 1 - KK));
+  __device__ static __forceinline__ void score_step(f32x16 (&s)[NKB], const u32x4 (&qreg)[NKK], u32x2 (&a)[NKK],
+                                                    const Lane &ln, uint32_t stage_off) {
+    constexpr int ISSUED = KK + WIN < NKK ? KK + WIN : NKK;  // reads issued before this step's wait
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(ISSUED - 1 - KK));
     asm volatile("" : "+v"(a[KK]));
+    if constexpr (KK + WIN < NKK) a[KK + WIN] = ds_read_b64<0>(kaddr(ln, KK + WIN, stage_off));
     s[0] = mfma32(widen_fp8x8(a[KK]), qreg[KK], s[0]);
-    if constexpr (KK + 1 < NKK) score_step<KK + 1>(s, qreg, a);
+    if constexpr (KK + 1 < NKK) score_step<KK + 1>(s, qreg, a, ln, stage_off);
   }
 
-  // O^T += V^T . P^T for the staged tile.
+  // O^T += V^T . P^T for the staged tile; read U serves head-dim block U % NDB
+  // of value k-step U / NDB.
+  static constexpr int NVR = NPV * NDB;
   __device__ static __forceinline__ void values(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV], const Lane &ln,
                                                 uint32_t stage_off) {
-    u32x2 v[NPV * NDB];
+    u32x2 v[NVR];
 #pragma unroll
-    for (int t = 0; t < NPV; ++t)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        v[t * NDB + db] = ds_read_tr8<0>(ln.vl[db][t & 1] + stage_off + (t >> 1) * 32 * D);
-    value_step<0>(o, pk, v);
+    for (int u = 0; u < (NVR < WIN ? NVR : WIN); ++u) v[u] = ds_read_tr8<0>(vaddr(ln, u % NDB, u / NDB, stage_off));
+    value_step<0>(o, pk, v, ln, stage_off);
   }
   template <int U>
-  __device__ static __forceinline__ void value_step(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV],
-                                                    u32x2 (&v)[NPV * NDB]) {
-    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(NPV * NDB - 1 - U));
+  __device__ static __forceinline__ void value_step(f32x16 (&o)[NDB], const u32x4 (&pk)[NPV], u32x2 (&v)[NVR],
+                                                    const Lane &ln, uint32_t stage_off) {
+    constexpr int ISSUED = U + WIN < NVR ? U + WIN : NVR;
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(ISSUED - 1 - U));
     asm volatile("" : "+v"(v[U]));
+    if constexpr (U + WIN < NVR)
+      v[U + WIN] = ds_read_tr8<0>(vaddr(ln, (U + WIN) % NDB, (U + WIN) / NDB, stage_off));
     o[U % NDB] = mfma32(widen_fp8x8(v[U]), pk[U / NDB], o[U % NDB]);
-    if constexpr (U + 1 < NPV * NDB) value_step<U + 1>(o, pk, v);
+    if constexpr (U + 1 < NVR) value_step<U + 1>(o, pk, v, ln, stage_off);
   }
 };
 

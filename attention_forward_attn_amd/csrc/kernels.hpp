@@ -35,8 +35,10 @@ int decode_block_rows(int d);
 hipError_t decode_split(int d, const DecodeParams &p, hipStream_t s);
 // The same over a paged cache (p.block_table, p.page_shift, p.k_ps, p.v_ps set).
 hipError_t decode_split_paged(int d, const DecodeParams &p, hipStream_t s);
-// The same over an FP8 (E4M3) cache with per-kv-head scales (p.k_scale, p.v_scale); d = 128.
+// The same over an FP8 (E4M3) cache with per-kv-head scales (p.k_scale, p.v_scale); d = 128 or 256.
 hipError_t decode_split_fp8(int d, const DecodeParams &p, hipStream_t s);
+// The same over a paged FP8 cache (paged addressing in bytes); d = 128 or 256.
+hipError_t decode_split_paged_fp8(int d, const DecodeParams &p, hipStream_t s);
 
 // Attention backward (dQ, dK, dV, and the sink gradient when p.d_sinks is set) at
 // head dim 64 or 128; p.dsum is scratch of b*h_q*s_q floats, p.dsink_part of

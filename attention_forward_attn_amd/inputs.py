@@ -84,9 +84,14 @@ WORKLOADS = {
         # the same draw quantized to an FP8 (E4M3) cache
         _w("mqa_decode_fp8_B64_hq128_d128", "decode", BASE_SEED + 3, 128, 128, 1, b=64,
            len_lo=1024, len_hi=8192, fp8=True),
+        _w("mqa_decode_fp8_B64_hq128_d256", "decode", BASE_SEED + 3, 256, 128, 1, b=64,
+           len_lo=1024, len_hi=8192, fp8=True),
         # the same draw held in a paged cache of 64-token pages
         _w("mqa_decode_paged_B64_hq128_d128_p64", "decode", BASE_SEED + 3, 128, 128, 1, b=64,
            len_lo=1024, len_hi=8192, page_size=64),
+        # the FP8 codes of that draw in the same pages
+        _w("mqa_decode_paged_fp8_B64_hq128_d128_p64", "decode", BASE_SEED + 3, 128, 128, 1, b=64,
+           len_lo=1024, len_hi=8192, page_size=64, fp8=True),
         # backward of the dense causal MHA prefill (incoming dO ~ N(0,1), drawn after Q, K, V)
         _w("bwd_mha_b2_h16_s4096_d128_causal", "backward", BASE_SEED + 1, 128, 16, 16, b=2, s_q=4096,
            s_k=4096, causal=True),
@@ -141,6 +146,8 @@ def workload_inputs(w: Workload):
         return prefill_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed, w.sinks)
     if w.kind == "backward":
         return backward_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed)
+    if w.fp8 and w.page_size:
+        return paged_fp8_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.page_size, w.seed, w.sinks)
     if w.fp8:
         return fp8_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed, w.sinks)
     if w.page_size:
@@ -196,6 +203,38 @@ def fp8_decode_inputs(B: int, h_q: int, h_kv: int, d: int, len_lo: int, len_hi: 
         codes = (x / sc[None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
         inp[name + "8"] = codes.contiguous()
         inp[name + "_scale"] = sc
+    return inp
+
+
+def paged_fp8_decode_inputs(B: int, h_q: int, h_kv: int, d: int, len_lo: int, len_hi: int, page_size: int,
+                            seed: int, with_sinks: bool = False, spare: int = 0):
+    """The codes and scales of fp8_decode_inputs laid out in a paged cache.
+
+    Returns fp8_decode_inputs' dict plus k8_cache, v8_cache (uint8 [n_pages,
+    page_size, h_kv, d]), block_table and page_size, with the page order of
+    paged_decode_inputs for the same seed; slots that hold no token are 0xff
+    (an E4M3 NaN, so that reading one shows).
+    """
+    inp = fp8_decode_inputs(B, h_q, h_kv, d, len_lo, len_hi, seed, with_sinks)
+    lens = [int(x) for x in inp["kv_len"]]
+    starts = [int(x) for x in inp["kv_start"]]
+    n_used = sum(-(-L // page_size) for L in lens)
+    n_pages = max(1, n_used + spare)
+    perm = torch.randperm(n_pages, generator=torch.Generator("cpu").manual_seed(seed + 7919))
+    kc = torch.full((n_pages, page_size, h_kv, d), 255, dtype=torch.uint8)
+    vc = torch.full((n_pages, page_size, h_kv, d), 255, dtype=torch.uint8)
+    max_pages = max(1, -(-len_hi // page_size))
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    used = 0
+    for b, (s0, L) in enumerate(zip(starts, lens)):
+        for pg in range(-(-L // page_size)):
+            phys = int(perm[used])
+            used += 1
+            table[b, pg] = phys
+            n = min(page_size, L - pg * page_size)
+            kc[phys, :n] = inp["k8"][s0 + pg * page_size:s0 + pg * page_size + n]
+            vc[phys, :n] = inp["v8"][s0 + pg * page_size:s0 + pg * page_size + n]
+    inp.update(k8_cache=kc, v8_cache=vc, block_table=table, page_size=page_size)
     return inp
 
 

@@ -612,6 +612,50 @@ class Fp8DecodeCase(DecodeCase):
                        workspace=self.ws, out=self.out, lse=self.lse)
 
 
+class PagedFp8DecodeCase(DecodeCase):
+    """The FP8 decode workload held in a paged cache (block table of page_size-token pages)."""
+
+    def __init__(self, w, n_sets: int, dev):
+        import torch
+
+        import attention_forward_attn_amd as afa
+        from attention_forward_attn_amd.inputs import paged_fp8_decode_inputs
+
+        self.w = w
+        base = paged_fp8_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.page_size, w.seed, w.sinks)
+        self.total = int(base["kv_len"].sum())
+        self.max_len = int(base["kv_len"].max())
+        self.kv_len = base["kv_len"].to(dev)
+        self.table = base["block_table"].to(dev)
+        self.k_scale = base["k_scale"].to(dev)
+        self.v_scale = base["v_scale"].to(dev)
+        self.sets = [{"q": base["q"].to(dev), "k": base["k8_cache"].to(dev), "v": base["v8_cache"].to(dev)}]
+        gen = torch.Generator(device=dev).manual_seed(w.seed + 1)
+        for _ in range(1, n_sets):  # further sets: fresh codes of the same shapes (no NaN codes)
+            st = {"q": torch.randn(self.sets[0]["q"].shape, generator=gen, device=dev).to(torch.bfloat16)}
+            for n in ("k", "v"):
+                st[n] = torch.randint(0, 0x7f, self.sets[0][n].shape, generator=gen, device=dev,
+                                      dtype=torch.int32).to(torch.uint8) | (
+                    torch.randint(0, 2, self.sets[0][n].shape, generator=gen, device=dev,
+                                  dtype=torch.int32).to(torch.uint8) << 7)
+            self.sets.append(st)
+        self.sinks = base["sinks"].to(dev) if base["sinks"] is not None else None
+        self.scale = 1.0 / math.sqrt(w.d)
+        self.ws = afa.new_decode_workspace(afa.decode_workspace_size(w.b, w.h_q, w.d, self.max_len, w.split),
+                                           dev)
+        self.out = torch.empty((w.b, w.h_q, w.d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.b, w.h_q), dtype=torch.float32, device=dev)
+        self.bytes = decode_bytes(w, self.total)
+
+    def run(self, i: int):
+        import attention_forward_attn_amd as afa
+
+        s = self.sets[i % len(self.sets)]
+        afa.decode_paged_fp8(s["q"], s["k"], s["v"], self.k_scale, self.v_scale, self.table, self.kv_len,
+                             self.max_len, scale=self.scale, sinks=self.sinks, split_size=self.w.split,
+                             workspace=self.ws, out=self.out, lse=self.lse)
+
+
 class BackwardCase:
     """dQ, dK, dV of the prefill for an incoming dO; O and LSE come from one forward outside the timing."""
 
@@ -653,7 +697,8 @@ def make_case(w, dev):
         return BackwardCase(w, n_sets_beyond_mall(2 * prefill_set_bytes(w)), dev)
     if w.kind == "prefill":
         return PrefillCase(w, n_sets_beyond_mall(prefill_set_bytes(w)), dev)
-    kind = Fp8DecodeCase if w.fp8 else PagedDecodeCase if w.page_size else DecodeCase
+    kind = (PagedFp8DecodeCase if w.fp8 and w.page_size else Fp8DecodeCase if w.fp8
+            else PagedDecodeCase if w.page_size else DecodeCase)
     return kind(w, n_sets_beyond_mall(decode_set_bytes(w)), dev)
 
 

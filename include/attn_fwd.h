@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 8
+#define ATTN_FWD_ABI_VERSION 9
 
 typedef enum {
   ATTN_OK = 0,
@@ -218,7 +218,7 @@ typedef struct {
  *       k + (kv_start[bi] + tok)*k_st + g*k_sh bytes (v: v_st, v_sh); token
  *       and head strides multiples of 16 bytes (head stride 0 = MQA).
  * k_scale, v_scale: DEVICE fp32 [h_kv].
- * Supported: d = 128.  Other fields, the workspace (attn_fwd_decode_workspace_size)
+ * Supported: d = 128 or 256.  Other fields, the workspace (attn_fwd_decode_workspace_size)
  * and its ownership are those of attn_fwd_decode.
  */
 typedef struct {
@@ -242,6 +242,43 @@ typedef struct {
   int64_t lse_sb;
   float scale;
 } attn_decode_fp8_args;
+
+/*
+ * Decode over a paged FP8 KV cache: the paged addressing of
+ * attn_fwd_decode_paged (pages of page_size tokens, a block table per
+ * sequence, the same rules on page_size, n_pages, bt_stride and indices
+ * outside [0, n_pages)) over the E4M3 codes and per-kv-head scales of
+ * attn_fwd_decode_fp8.  Token tok of sequence bi, kv head g is at
+ *     k + block_table[bi*bt_stride + tok/page_size]*k_ps + (tok % page_size)*k_ts + g*k_sh
+ * bytes (v: v_ps, v_ts, v_sh); every cache stride a non-negative multiple of
+ * 16 bytes.  Supported: d = 128 or 256.  Other fields, the workspace
+ * (attn_fwd_decode_workspace_size) and its ownership are those of
+ * attn_fwd_decode.
+ */
+typedef struct {
+  const void *q;
+  const uint8_t *k;
+  const uint8_t *v;
+  const float *k_scale;
+  const float *v_scale;
+  const int32_t *block_table;
+  const int32_t *kv_len;
+  void *o;
+  float *lse;
+  const float *sinks;
+  int32_t B, h_q, h_kv, d;
+  int32_t max_kv_len;
+  int32_t split_size;
+  int32_t page_size;
+  int32_t n_pages;
+  int64_t bt_stride;
+  int64_t q_sb, q_sh;
+  int64_t k_ps, k_ts, k_sh;
+  int64_t v_ps, v_ts, v_sh;
+  int64_t o_sb, o_sh;
+  int64_t lse_sb;
+  float scale;
+} attn_decode_paged_fp8_args;
 
 /*
  * Backward of the prefill: dQ, dK, dV for an incoming gradient dO of O, from
@@ -405,6 +442,8 @@ attn_status attn_fwd_decode_paged(const attn_decode_paged_args *args, void *work
                                   size_t workspace_bytes, void *stream);
 attn_status attn_fwd_decode_fp8(const attn_decode_fp8_args *args, void *workspace, size_t workspace_bytes,
                                 void *stream);
+attn_status attn_fwd_decode_paged_fp8(const attn_decode_paged_fp8_args *args, void *workspace,
+                                      size_t workspace_bytes, void *stream);
 attn_status attn_combine(const attn_combine_args *args, void *stream);
 attn_status attn_bwd(const attn_bwd_args *args, void *workspace, size_t workspace_bytes, void *stream);
 

@@ -13,7 +13,7 @@ import pytest
 
 import attention_forward_attn_amd as afa
 from attention_forward_attn_amd._binding import (BwdArgs, CombineArgs, DecodeArgs, DecodeFp8Args,
-                                                 DecodePagedArgs, PrefillArgs)
+                                                 DecodePagedArgs, DecodePagedFp8Args, PrefillArgs)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     lib = afa.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
-    assert lib.attn_abi_version() == 8
+    assert lib.attn_abi_version() == 9
 
 
 def test_status_strings():
@@ -321,6 +321,63 @@ def test_decode_paged_rejects(name, over, code):
     assert st == code, (st, lib.attn_last_error())
 
 
+def good_paged_fp8(**over):
+    a = DecodePagedFp8Args()
+    a.q = a.k = a.v = a.o = FAKE
+    a.k_scale = a.v_scale = FAKE
+    a.block_table = a.kv_len = FAKE
+    a.lse = None
+    a.sinks = None
+    a.B, a.h_q, a.h_kv, a.d = 4, 128, 1, 128
+    a.max_kv_len, a.split_size = 8192, 512
+    a.page_size, a.n_pages = 64, 1000
+    a.bt_stride = 128
+    a.q_sb, a.q_sh = 128 * 128, 128
+    a.k_ps, a.k_ts, a.k_sh = 64 * 128, 128, 0  # bytes
+    a.v_ps, a.v_ts, a.v_sh = 64 * 128, 128, 0
+    a.o_sb, a.o_sh = 128 * 128, 128
+    a.lse_sb = 128
+    a.scale = 0.088
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+PAGED_FP8_BAD = [
+    ("null k_scale", dict(k_scale=None), 1),
+    ("null block table", dict(block_table=None), 1),
+    ("d=64", dict(d=64), 2),
+    ("d=512", dict(d=512), 2),
+    ("ratio", dict(h_q=6, h_kv=4), 2),
+    ("page 8", dict(page_size=8), 2),
+    ("split 384, page 256", dict(split_size=384, page_size=256), 2),
+    ("no pages", dict(n_pages=0), 2),
+    ("table too narrow", dict(bt_stride=127), 3),
+    ("page stride 8 bytes", dict(k_ps=8), 3),
+    ("token stride 24 bytes", dict(v_ts=24), 3),
+    ("huge token stride", dict(k_ts=1 << 24), 3),
+    ("misaligned v", dict(v=FAKE + 8), 4),
+    ("misaligned scale", dict(k_scale=FAKE + 2), 4),
+]
+
+
+@pytest.mark.parametrize("name,over,code", PAGED_FP8_BAD, ids=[c[0] for c in PAGED_FP8_BAD])
+def test_decode_paged_fp8_rejects(name, over, code):
+    lib = afa.load_library()
+    a = good_paged_fp8(**over)
+    st = lib.attn_fwd_decode_paged_fp8(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert st == code, (st, lib.attn_last_error())
+
+
+def test_decode_paged_fp8_workspace_checks():
+    lib = afa.load_library()
+    a = good_paged_fp8(d=256)
+    need = lib.attn_fwd_decode_workspace_size(4, 128, 256, 8192, 512)
+    assert lib.attn_fwd_decode_paged_fp8(ctypes.byref(a), None, need, None) == 6
+    assert lib.attn_fwd_decode_paged_fp8(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
+    assert lib.attn_fwd_decode_paged_fp8(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4
+
+
 def test_decode_paged_workspace_checks():
     lib = afa.load_library()
     a = good_paged()
@@ -353,7 +410,7 @@ FP8_BAD = [
     ("null k_scale", dict(k_scale=None), 1),
     ("null v_scale", dict(v_scale=None), 1),
     ("d=64", dict(d=64), 2),
-    ("d=256", dict(d=256), 2),
+    ("d=512", dict(d=512), 2),
     ("ratio", dict(h_q=6, h_kv=4), 2),
     ("split 100", dict(split_size=100), 2),
     ("token stride 8 bytes", dict(k_st=8), 3),

@@ -8,7 +8,8 @@ import torch
 
 import attention_forward_attn_amd as afa
 import oracle
-from attention_forward_attn_amd.inputs import WORKLOADS, decode_inputs, fp8_decode_inputs, paged_decode_inputs
+from attention_forward_attn_amd.inputs import (WORKLOADS, decode_inputs, fp8_decode_inputs, paged_decode_inputs,
+                                               paged_fp8_decode_inputs)
 from parity_util import check
 
 pytestmark = pytest.mark.gpu
@@ -273,31 +274,35 @@ def run_fp8(inp, max_len, split=512, sinks=None):
 
 
 FP8 = [
-    # B, h_q, h_kv, len_lo, len_hi, split
-    (4, 128, 1, 1, 1500, 512),
-    (5, 16, 4, 0, 700, 128),
-    (3, 256, 2, 100, 1030, 256),
-    (2, 8, 8, 1, 300, 64),
+    # B, h_q, h_kv, d, len_lo, len_hi, split
+    (4, 128, 1, 128, 1, 1500, 512),
+    (5, 16, 4, 128, 0, 700, 128),
+    (3, 256, 2, 128, 100, 1030, 256),
+    (2, 8, 8, 128, 1, 300, 64),
+    (4, 128, 1, 256, 1, 1500, 512),
+    (5, 16, 4, 256, 0, 700, 128),
+    (2, 8, 8, 256, 1, 300, 64),
 ]
 
 
 @pytest.mark.parametrize("case", FP8, ids=[str(c) for c in FP8])
 @pytest.mark.parametrize("with_sink", [False, True])
 def test_decode_fp8_small(case, with_sink):
-    B, h_q, h_kv, lo, hi, split = case
+    B, h_q, h_kv, d, lo, hi, split = case
     print(f"fp8 decode case {case} sink={with_sink}", flush=True)
-    inp = fp8_decode_inputs(B, h_q, h_kv, 128, lo, hi, 41, with_sink)
+    inp = fp8_decode_inputs(B, h_q, h_kv, d, lo, hi, 41, with_sink)
     out, lse = run_fp8(inp, hi, split, inp["sinks"])
     o_ref, l_ref = oracle.decode_fp8_ref(inp["q"], inp["k8"].numpy(), inp["v8"].numpy(), inp["k_scale"],
-                                         inp["v_scale"], inp["kv_start"], inp["kv_len"], 1 / math.sqrt(128),
+                                         inp["v_scale"], inp["kv_start"], inp["kv_len"], 1 / math.sqrt(d),
                                          sinks=inp["sinks"])
     check(out, lse, o_ref, l_ref, str(case))
 
 
-def test_decode_fp8_equals_bf16_on_exact_values():
+@pytest.mark.parametrize("d", [128, 256])
+def test_decode_fp8_equals_bf16_on_exact_values(d):
     """Power-of-two scales make every dequantized value a bf16 value: the FP8 path
     then matches the bf16 decode on the dequantized cache bit for bit."""
-    inp = fp8_decode_inputs(5, 64, 2, 128, 1, 1500, 42, True)
+    inp = fp8_decode_inputs(5, 64, 2, d, 1, 1500, 42, True)
     inp["k_scale"] = torch.tensor([2.0 ** -6, 2.0 ** -7])
     inp["v_scale"] = torch.tensor([2.0 ** -5, 2.0 ** -8])
     for n in ("k", "v"):
@@ -309,8 +314,10 @@ def test_decode_fp8_equals_bf16_on_exact_values():
     assert torch.equal(out8, outb) and torch.equal(lse8, lseb)
 
 
-def test_decode_fp8_full_size():
-    w = WORKLOADS["mqa_decode_fp8_B64_hq128_d128"]
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items()
+                                  if w.kind == "decode" and w.fp8 and not w.page_size])
+def test_decode_fp8_full_size(name):
+    w = WORKLOADS[name]
     print(f"full-size fp8 decode {w.name}", flush=True)
     inp = fp8_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.seed)
     out, lse = run_fp8(inp, w.len_hi, w.split)
@@ -318,3 +325,87 @@ def test_decode_fp8_full_size():
                                          inp["v_scale"], inp["kv_start"], inp["kv_len"], 1 / math.sqrt(w.d))
     check(out, lse, o_ref, l_ref, w.name)
 
+
+
+# --- paged FP8 KV cache ----------------------------------------------------
+
+def run_paged_fp8(inp, max_len, split=512, sinks=None, table=None):
+    q = inp["q"].to(DEV)
+    kc, vc = inp["k8_cache"].to(DEV), inp["v8_cache"].to(DEV)
+    ksc, vsc = inp["k_scale"].to(DEV), inp["v_scale"].to(DEV)
+    bt = (inp["block_table"] if table is None else table).to(DEV)
+    kl = inp["kv_len"].to(DEV)
+    d = q.shape[-1]
+    ws = poisoned_ws(afa.decode_workspace_size(q.shape[0], q.shape[1], d, max_len, split))
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+    sd = None if sinks is None else sinks.to(DEV)
+    afa.decode_paged_fp8(q, kc, vc, ksc, vsc, bt, kl, max_len, sinks=sd, split_size=split, workspace=ws, out=out,
+                         lse=lse)
+    torch.cuda.synchronize()
+    assert header_left_zero(ws)
+    return out, lse
+
+
+PAGED_FP8 = [
+    # B, h_q, h_kv, d, len_lo, len_hi, page_size, split
+    (4, 128, 1, 128, 1, 1500, 16, 512),
+    (5, 16, 4, 128, 0, 700, 32, 128),      # empty sequences possible
+    (3, 64, 1, 128, 1, 1500, 128, 384),    # three pages per split
+    (4, 128, 1, 256, 1, 1500, 64, 512),
+    (3, 8, 8, 256, 1, 300, 16, 1024),      # 64 pages per split
+]
+
+
+@pytest.mark.parametrize("case", PAGED_FP8, ids=[str(c) for c in PAGED_FP8])
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_decode_paged_fp8_small(case, with_sink):
+    B, h_q, h_kv, d, lo, hi, page, split = case
+    print(f"paged fp8 decode case {case} sink={with_sink}", flush=True)
+    inp = paged_fp8_decode_inputs(B, h_q, h_kv, d, lo, hi, page, 43, with_sink, spare=3)
+    out, lse = run_paged_fp8(inp, hi, split, inp["sinks"])
+    # the pages hold the codes of the contiguous draw, token for token
+    o_ref, l_ref = oracle.decode_fp8_ref(inp["q"], inp["k8"].numpy(), inp["v8"].numpy(), inp["k_scale"],
+                                         inp["v_scale"], inp["kv_start"], inp["kv_len"], 1 / math.sqrt(d),
+                                         sinks=inp["sinks"])
+    check(out, lse, o_ref, l_ref, str(case))
+
+
+@pytest.mark.parametrize("d,page", [(128, 64), (256, 16)])
+def test_decode_paged_fp8_equals_contiguous_bitwise(d, page):
+    """The same codes read through a block table give bit-identical results."""
+    inp = paged_fp8_decode_inputs(6, 32, 2, d, 1, 1800, page, 44, True, spare=2)
+    out_p, lse_p = run_paged_fp8(inp, 1800, 512, inp["sinks"])
+    out_c, lse_c = run_fp8(inp, 1800, 512, inp["sinks"])
+    assert torch.equal(out_p, out_c) and torch.equal(lse_p, lse_c)
+
+
+def test_decode_paged_fp8_bad_page_reads_zero():
+    """A page index outside [0, n_pages) is not dereferenced: its tokens read as zero codes."""
+    inp = paged_fp8_decode_inputs(3, 16, 1, 128, 300, 600, 64, 45)
+    n_pages = inp["k8_cache"].shape[0]
+    table = inp["block_table"].clone()
+    table[0, 1] = n_pages       # one past the pool
+    table[2, 0] = -5
+    out, lse = run_paged_fp8(inp, 600, 256, table=table)
+    # expected: the contiguous codes with those two pages' tokens set to code 0 (+0.0)
+    k8, v8 = inp["k8"].clone(), inp["v8"].clone()
+    starts = inp["kv_start"]
+    for b, pg in ((0, 1), (2, 0)):
+        lo = int(starts[b]) + pg * 64
+        hi = min(int(starts[b]) + int(inp["kv_len"][b]), lo + 64)
+        k8[lo:hi] = 0
+        v8[lo:hi] = 0
+    o_ref, l_ref = oracle.decode_fp8_ref(inp["q"], k8.numpy(), v8.numpy(), inp["k_scale"], inp["v_scale"],
+                                         inp["kv_start"], inp["kv_len"], 1 / math.sqrt(128))
+    check(out, lse, o_ref, l_ref, "bad page")
+
+
+def test_decode_paged_fp8_full_size():
+    w = WORKLOADS["mqa_decode_paged_fp8_B64_hq128_d128_p64"]
+    print(f"full-size paged fp8 decode {w.name}", flush=True)
+    inp = paged_fp8_decode_inputs(w.b, w.h_q, w.h_kv, w.d, w.len_lo, w.len_hi, w.page_size, w.seed)
+    out, lse = run_paged_fp8(inp, w.len_hi, w.split)
+    o_ref, l_ref = oracle.decode_fp8_ref(inp["q"], inp["k8"].numpy(), inp["v8"].numpy(), inp["k_scale"],
+                                         inp["v_scale"], inp["kv_start"], inp["kv_len"], 1 / math.sqrt(w.d))
+    check(out, lse, o_ref, l_ref, w.name)
