@@ -741,13 +741,14 @@ attn_status attn_fwd_decode_paged_fp8(const attn_decode_paged_fp8_args *a, void 
 }
 
 // Backward workspace: D = rowsum(dO * O) [b][h_q][s_q] fp32, then (256-byte
-// aligned) the sink-gradient partials [b][h_q][query tiles of the dQ kernel].
+// aligned) LSE * log2(e) [b][h_q][s_q] fp32, then (256-byte aligned) the
+// sink-gradient partials [b][h_q][query tiles of the dQ kernel].
 size_t attn_bwd_workspace_size(int32_t b, int32_t h_q, int32_t s_q) {
   if (b < 1 || h_q < 1 || s_q < 0) return 0;
   const size_t rows = (size_t)b * h_q * (size_t)(s_q > 0 ? s_q : 1);
   const size_t br = (size_t)attn::backward_block_rows();
   const size_t tiles = (size_t)b * h_q * (((size_t)s_q + br - 1) / br);
-  return (rows * 4 + 255) / 256 * 256 + tiles * 4;
+  return 2 * ((rows * 4 + 255) / 256 * 256) + tiles * 4;
 }
 
 attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
@@ -801,11 +802,12 @@ attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_b
   p.dv = static_cast<uint16_t *>(a->dv);
   p.dsum = static_cast<float *>(workspace);
   const size_t rows = (size_t)a->b * a->h_q * (size_t)(a->s_q > 0 ? a->s_q : 1);
+  const size_t rows_bytes = (rows * 4 + 255) / 256 * 256;
+  p.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + rows_bytes);
   p.window = a->window;
   p.sinks = a->sinks;
   p.d_sinks = a->d_sinks;
-  p.dsink_part = a->d_sinks ? reinterpret_cast<float *>(static_cast<char *>(workspace) + (rows * 4 + 255) / 256 * 256)
-                            : nullptr;
+  p.dsink_part = a->d_sinks ? reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * rows_bytes) : nullptr;
   p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_ss = a->q_ss;
   p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_ss = a->k_ss;
   p.lse_sb = a->lse_sb; p.lse_sh = a->lse_sh;

@@ -11,7 +11,10 @@
 //   * dQ (one workgroup per NW x 32 query rows, NW waves x 32 rows): the forward
 //     layout S^T = K.Q^T (rows in lanes, keys in registers), plus
 //     dP^T = V.dO^T, then dQ^T += K^T.dS^T with dS = P * (dP - D).  It also
-//     writes D_i = sum_t dO[i,t] O[i,t] for the second kernel.
+//     writes D_i = sum_t dO[i,t] O[i,t] and the row's LSE in base 2 (+inf
+//     for a row with no key, so that P = exp2(S*c - L) needs no test) for
+//     the second kernel.  Tiles whose keys every row of a wave sees skip the
+//     per-key mask in both kernels.
 //   * dK/dV (one workgroup per NW x 32 keys of one kv head, NW waves x 32 keys):
 //     the same shapes with the roles of queries and keys swapped: S = Q.K^T
 //     and dP = dO.V^T with keys in lanes and query rows in registers, then
@@ -152,7 +155,10 @@ void bwd_dq_kernel(BwdParams p) {
   const float lse = row_ok ? p.lse[bi * p.lse_sb + h * p.lse_sh + row] : kNegInf;
   // A row that saw no key has P = 0: exp2(s*c - inf) = 0.
   const float lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
-  if (row_ok && hi == 0) p.dsum[(bi * p.h_q + h) * (int64_t)p.s_q + row] = dd;
+  if (row_ok && hi == 0) {
+    p.dsum[(bi * p.h_q + h) * (int64_t)p.s_q + row] = dd;
+    p.lse2[(bi * p.h_q + h) * (int64_t)p.s_q + row] = lse2;
+  }
 
   f32x16 acc[T::NDB];
 #pragma unroll
@@ -181,16 +187,26 @@ void bwd_dq_kernel(BwdParams p) {
       f32x16 s[T::NKB], dp[T::NKB];
       T::scores(s, qreg, ln, so);
       T::scores(dp, dreg, ln, so + 2 * T::TILE_BYTES);
-      const int lim = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
-      const int lo = WINDOW ? row + off - p.window + 1 : 0;
+      // Every key of the tile visible to every row of the wave: no per-key test.
+      const bool full = j0 + BN <= p.s_k && (!CAUSAL || j0 + BN - 1 <= w_lo + off) &&
+                        (!WINDOW || j0 >= w_hi + off - p.window + 1);
+      if (full) {
 #pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
+        for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = j0 + T::key_of(kb, i, hi);
-          const float pv = (j > lim || j < lo) ? 0.0f : fast_exp2(fmaf(s[kb][i], p.c, -lse2));
-          s[kb][i] = pv * (dp[kb][i] - dd);  // dS
-        }
+          for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], p.c, -lse2)) * (dp[kb][i] - dd);
+      } else {
+        const int lim = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
+        const int lo = WINDOW ? row + off - p.window + 1 : 0;
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + T::key_of(kb, i, hi);
+            const float pv = (j > lim || j < lo) ? 0.0f : fast_exp2(fmaf(s[kb][i], p.c, -lse2));
+            s[kb][i] = pv * (dp[kb][i] - dd);  // dS
+          }
+      }
       u32x4 pk[T::NPV];
       pack_operand(s, pk);
       T::values(acc, pk, ln, so);  // dQ^T += K^T . dS^T (K through the transpose-swizzled copy)
@@ -273,7 +289,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   for (int h = g * p.ratio; h < (g + 1) * p.ratio; ++h) {
     const int64_t qrow0 = bi * p.q_sb + h * p.q_sh;
     const uint16_t *qbase = p.q + qrow0, *dobase = p.d_o + qrow0;
-    const float *lse_h = p.lse + bi * p.lse_sb + h * p.lse_sh;
+    const float *lse_h = p.lse2 + (bi * p.h_q + h) * (int64_t)p.s_q;  // LSE * log2(e), +inf for no key
     const float *d_h = p.dsum + (bi * p.h_q + h) * (int64_t)p.s_q;
     auto load = [&](int buf, int t) {
       uint16_t *st = smem + buf * (STAGE / 2);
@@ -322,13 +338,20 @@ void bwd_dkdv_kernel(BwdParams p) {
           auto visible = [&](int r) {
             return r < p.s_q && key_ok && (!CAUSAL || key <= r + off) && (!WINDOW || key >= r + off - p.window + 1);
           };
+          // Every row of the tile sees every key of the wave: no per-pair test.
+          const bool full = i0 + BN <= p.s_q && w_key0 + 32 <= p.s_k && (!CAUSAL || w_key0 + 31 <= i0 + off) &&
+                            (!WINDOW || w_key0 >= i0 + BN - 1 + off - p.window + 1);
           auto p_group = [&](int g) {  // P = exp(scale*S - LSE) over the visible pairs, into s
             const int rb = g >> 2, q4 = g & 3, r4 = i0 + 32 * rb + 8 * q4 + 4 * hi;
+            if (full) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float l = lv[g][e];
-              const float pv = fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -l * kLog2e));
-              s[rb][4 * q4 + e] = visible(r4 + e) && l != kNegInf ? pv : 0.0f;
+              for (int e = 0; e < 4; ++e) s[rb][4 * q4 + e] = fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -lv[g][e]));
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float pv = fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -lv[g][e]));
+                s[rb][4 * q4 + e] = visible(r4 + e) ? pv : 0.0f;
+              }
             }
           };
           auto ds_group = [&](int g) {  // dS = P * (dP - D), into dp

@@ -53,12 +53,13 @@ struct PrefillChunks {
 
 // Device-side parameters of the backward kernels.  q, o, d_o and dq share one
 // [b, h_q, s_q, d] layout (q strides); k, v, dk and dv share one [b, h_kv,
-// s_k, d] layout (k strides); dsum is fp32 [b, h_q, s_q] scratch.
+// s_k, d] layout (k strides); dsum and lse2 are fp32 [b, h_q, s_q] scratch.
 struct BwdParams {
   const uint16_t *q, *k, *v, *o, *d_o;
   const float *lse;
   uint16_t *dq, *dk, *dv;
   float *dsum;
+  float *lse2;  // fp32 [b, h_q, s_q] scratch: LSE * log2(e), +inf for a row with no key
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t lse_sb, lse_sh;

@@ -305,8 +305,8 @@ typedef struct {
  * sinks: fp32 [h_q], the forward's sink logits (read only for d_sinks);
  * d_sinks: fp32 [h_q] output, NULL = not wanted (then sinks may be NULL).
  * workspace: attn_bwd_workspace_size(b, h_q, s_q) bytes, 16-byte aligned,
- *       caller-owned (row sums D between the kernels, and the sink gradient's
- *       per-tile partials).
+ *       caller-owned (row sums D and the rows' LSE in base 2 between the
+ *       kernels, and the sink gradient's per-tile partials).
  * Kernels run on `stream`: dQ and D, the sink gradient (if wanted), then dK/dV.
  * Supported: d = 64 or 128; causal (bottom-right) or not; h_q % h_kv == 0.
  */

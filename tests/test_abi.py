@@ -550,7 +550,7 @@ def test_bwd_workspace_checks():
     a = good_bwd()
     need = lib.attn_bwd_workspace_size(2, 16, 4096)
     # D per row, then the sink-gradient partials per 256-row query tile of the dQ kernel
-    assert need == 2 * 16 * 4096 * 4 + 2 * 16 * (4096 // 256) * 4
+    assert need == 2 * (2 * 16 * 4096 * 4) + 2 * 16 * (4096 // 256) * 4  # D and base-2 LSE, then sink partials
     assert lib.attn_bwd(ctypes.byref(a), None, need, None) == 6
     assert lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
     assert lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4
