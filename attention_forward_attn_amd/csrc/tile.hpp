@@ -52,9 +52,35 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Three-input maximum.  fmaxf on MMA results makes the compiler quiet possible
+// signalling NaNs first (an extra v_max_f32 x, x, x per input); the NaN-
+// propagating maximum needs no such step and becomes one v_maximum3_f32.  The
+// two differ only on NaN and on the order of -0 and +0, and the scores are
+// finite or -inf, where a signed zero maximum gives the same exponentials.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+// Maximum of N values by a tree of three-input maxima (N/2 instructions).
+template <int N>
+__device__ __forceinline__ float max_tree(const float *v) {
+  if constexpr (N == 1) {
+    return v[0];
+  } else if constexpr (N <= 3) {
+    return max3f(v[0], v[1], v[N - 1]);
+  } else {
+    constexpr int T3 = N / 3, M = T3 + N % 3;  // triples of this level, plus the leftovers
+    float w[M];
+#pragma unroll
+    for (int k = 0; k < T3; ++k) w[k] = max3f(v[3 * k], v[3 * k + 1], v[3 * k + 2]);
+#pragma unroll
+    for (int k = 0; k < N % 3; ++k) w[T3 + k] = v[3 * T3 + k];
+    return max_tree<M>(w);
+  }
+}
+
 __device__ __forceinline__ float max_across_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_across_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -679,14 +705,12 @@ struct Tile {
   // already masked to -inf), lazy rescale of l and O; returns the exponent base.
   __device__ static __forceinline__ float softmax_max(const f32x16 (&s)[NKB], f32x16 (&o)[NDB], float &m,
                                                       float &l, float c) {
-    // four independent chains, then a small tree
-    float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+    float v[16 * NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], s[kb][i]);
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    mx = max_across_halves(mx) * c;
+      for (int i = 0; i < 16; ++i) v[16 * kb + i] = s[kb][i];
+    const float mx = max_across_halves(max_tree<16 * NKB>(v)) * c;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {  // wave-uniform
       const float m_new = fmaxf(m, mx);
       const float alpha = (m == kNegInf) ? 0.0f : fast_exp2(m - m_new);
