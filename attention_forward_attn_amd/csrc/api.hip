@@ -757,7 +757,8 @@ attn_status attn_bwd(const attn_bwd_args *a, void *workspace, size_t workspace_b
     return fail(ATTN_ERR_SHAPE, "need b, h_q, h_kv >= 1 and s_q, s_k >= 0");
   if (a->h_q % a->h_kv != 0)
     return fail(ATTN_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
-  if (a->d != 64 && a->d != 128) return fail(ATTN_ERR_SHAPE, "backward supports d = 64 or 128 (got %d)", a->d);
+  if (a->d != 64 && a->d != 128 && a->d != 256)
+    return fail(ATTN_ERR_SHAPE, "backward supports d = 64, 128 or 256 (got %d)", a->d);
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1");
   if (a->window < 0) return fail(ATTN_ERR_SHAPE, "window must be >= 0");
   if (a->window > 0 && !a->causal) return fail(ATTN_ERR_SHAPE, "a window requires causal = 1");

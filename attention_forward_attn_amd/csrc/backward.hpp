@@ -1,4 +1,4 @@
-// Attention backward at head dims 64 and 128: dQ, dK, dV for an incoming dO, from the
+// Attention backward at head dims 64, 128 and 256: dQ, dK, dV for an incoming dO, from the
 // forward's O and LSE, under no mask, a causal mask or a causal sliding window,
 // deterministic (no atomics).  A sink only enters through the forward's LSE
 // (P = exp(scale*S - LSE) already carries its share of the normalisation), so
@@ -21,9 +21,9 @@
 //     dV^T += dO^T.P and dK^T += Q^T.dS, summed over every query head of the
 //     kv group (a workgroup owns its keys, so no atomics are needed).
 // A streamed tile is needed both row-wise (score-like MMA, A operand from
-// 16-byte row segments) and transposed (value-like MMA, transpose reads), and
-// the two read patterns want different LDS chunk swizzles, so each such tile
-// is staged twice, once per swizzle.
+// 16-byte row segments) and transposed (value-like MMA, transpose reads); the
+// tile engine's shared swizzle serves both read patterns without bank
+// conflicts, so each tile is staged once.
 #pragma once
 
 #include "tile.hpp"
@@ -55,31 +55,49 @@ __device__ __forceinline__ void load_b_rows(u32x4 (&reg)[NKK], const uint16_t *b
   for (int kk = 0; kk < NKK; ++kk) reg[kk] = *reinterpret_cast<const u32x4 *>(pr + kk * 16);
 }
 
-// Eight 16-byte LDS reads at addr + 32*I (I = 0..7) into f32x4 values.
-template <int I>
-__device__ __forceinline__ void lds_row4(f32x4 (&v)[8], uint32_t addr) {
+// N 16-byte LDS reads at addr + 32*I (I = 0..N-1) into f32x4 values.
+template <int I, int N>
+__device__ __forceinline__ void lds_row4(f32x4 (&v)[N], uint32_t addr) {
   v[I] = __builtin_bit_cast(f32x4, ds_read_b128<32 * I>(addr));
-  if constexpr (I + 1 < 8) lds_row4<I + 1>(v, addr);
+  if constexpr (I + 1 < N) lds_row4<I + 1>(v, addr);
 }
 
 // Hooks that run element-wise work between the MMAs of a score product
 // (step<KK>, after k-step KK) or of a value product (vstep<T>, after k-step
 // T): that vector work then executes while the MMAs just issued are in
-// flight.  G groups of work are spread evenly over the N steps.
+// flight.  G groups of work are spread evenly over the N steps: step K runs
+// groups ceil(K G / N) .. ceil((K+1) G / N) - 1 (G / N each when N divides G,
+// one every N / G steps when G divides N).
 template <int G, int N, typename F>
 struct GroupHook {
   F &f;
   template <int K>
   __device__ __forceinline__ void run() {
-    static_assert(G % N == 0, "whole groups per step");
+    constexpr int lo = (K * G + N - 1) / N, hi = ((K + 1) * G + N - 1) / N;
 #pragma unroll
-    for (int g = K * (G / N); g < (K + 1) * (G / N); ++g) f(g);
+    for (int g = lo; g < hi; ++g) f(g);
   }
   template <int KK>
   __device__ __forceinline__ void step() { run<KK>(); }
   template <int T_>
   __device__ __forceinline__ void vstep() { run<T_>(); }
 };
+
+// Wait before consuming tile n of a ring of NS stages, whose loads run NS - 1
+// tiles ahead (LPT loads per tile issued by this wave): when the NS - 2 tiles
+// after n are all in flight, only n's own loads need to have landed; near the
+// end, with fewer in flight, everything is waited for.
+template <int NS, int LPT>
+__device__ __forceinline__ void ring_wait(bool later_in_flight) {
+  if constexpr (NS <= 2) {
+    wait_vmcnt<0>();
+  } else {
+    if (later_in_flight)
+      wait_vmcnt<(NS - 2) * LPT>();
+    else
+      wait_vmcnt<0>();
+  }
+}
 
 // Stores a transposed accumulator (lane = row, registers = head-dim columns)
 // times f as bf16 rows.
@@ -97,14 +115,14 @@ __device__ __forceinline__ void store_rows(uint16_t *op, const f32x16 (&a)[NDB],
 }
 
 // ---------------------------------------------------------------------------
-// dQ (and D).
-template <int D, int BN, bool CAUSAL, bool WINDOW, int NW>
+// dQ (and D).  NS: stages of the K/V ring.
+template <int D, int BN, bool CAUSAL, bool WINDOW, int NW, int NS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dq_kernel(BwdParams p) {
-  using T = Tile<D, NW, BN>;
+  using T = Tile<D, NW, BN, D, true>;
   constexpr int BM = 32 * NW;
-  constexpr int STAGE = 3 * T::TILE_BYTES;  // [K, row swizzle][K, transpose swizzle][V, row swizzle]
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE / 2];
+  constexpr int STAGE = 2 * T::TILE_BYTES;  // [K][V]
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE / 2];
   __shared__ float s_red[NW];
 
   const int tid = threadIdx.x;
@@ -167,26 +185,27 @@ void bwd_dq_kernel(BwdParams p) {
   typename T::Lane ln;
   T::init_dma(ln, p.k_ss, p.k_ss, wave, lane);  // K and V share the row stride (checked on the host)
   const uint32_t base = lds_offset(smem);
-  T::init_mma(ln, base, base + T::TILE_BYTES, lane);
+  T::init_mma(ln, base, base, lane);  // K read row-wise and transposed from one copy
   auto load = [&](int buf, int t) {
     uint16_t *st = smem + buf * (STAGE / 2);
     T::dma1(ln, false, st, kbase, p.k_ss, t * BN, p.s_k, wave);
-    T::dma1(ln, true, st + T::TILE_ELEMS, kbase, p.k_ss, t * BN, p.s_k, wave);
-    T::dma1(ln, false, st + 2 * T::TILE_ELEMS, vbase, p.k_ss, t * BN, p.s_k, wave);
+    T::dma1(ln, false, st + T::TILE_ELEMS, vbase, p.k_ss, t * BN, p.s_k, wave);
   };
-  if (t0 < n_tiles) load(0, t0);
-  for (int t = t0; t < n_tiles; ++t) {
-    const int cur = (t - t0) & 1;
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (t + 1 < n_tiles) load(cur ^ 1, t + 1);
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k)
+    if (t0 + k < n_tiles) load(k, t0 + k);
+  int cur = 0;  // stage of tile t
+  for (int t = t0; t < n_tiles; ++t, cur = cur + 1 == NS ? 0 : cur + 1) {
+    ring_wait<NS, 2 * T::LOADS>(t + NS - 2 < n_tiles);
+    __syncthreads();  // also: every wave is done with tile t - 1, whose stage is refilled next
+    if (t + NS - 1 < n_tiles) load(cur == 0 ? NS - 1 : cur - 1, t + NS - 1);
     const int j0 = t * BN;
     if (w_lo < p.s_q && (!CAUSAL || j0 <= w_hi + off) &&
         (!WINDOW || j0 + BN - 1 >= w_lo + off - p.window + 1)) {
       const uint32_t so = cur * STAGE;
       f32x16 s[T::NKB], dp[T::NKB];
       T::scores(s, qreg, ln, so);
-      T::scores(dp, dreg, ln, so + 2 * T::TILE_BYTES);
+      T::scores(dp, dreg, ln, so + T::TILE_BYTES);
       // Every key of the tile visible to every row of the wave: no per-key test.
       const bool full = j0 + BN <= p.s_k && (!CAUSAL || j0 + BN - 1 <= w_lo + off) &&
                         (!WINDOW || j0 >= w_hi + off - p.window + 1);
@@ -209,7 +228,7 @@ void bwd_dq_kernel(BwdParams p) {
       }
       u32x4 pk[T::NPV];
       pack_operand(s, pk);
-      T::values(acc, pk, ln, so);  // dQ^T += K^T . dS^T (K through the transpose-swizzled copy)
+      T::values(acc, pk, ln, so);  // dQ^T += K^T . dS^T (K read transposed)
     }
   }
   if (row_ok) store_rows(p.dq + qrow0 + (int64_t)row * p.q_ss + 4 * hi, acc, p.scale);
@@ -241,15 +260,15 @@ __global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdParams p, int n_qt) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Reads D written by bwd_dq_kernel.
-template <int D, int BN, bool CAUSAL, bool WINDOW, int NW>
+// dK, dV.  Reads D written by bwd_dq_kernel.  NS: stages of the Q/dO ring.
+template <int D, int BN, bool CAUSAL, bool WINDOW, int NW, int NS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dkdv_kernel(BwdParams p) {
-  using T = Tile<D, NW, BN>;  // here the streamed "keys" of the engine are query rows
+  using T = Tile<D, NW, BN, D, true>;  // here the streamed "keys" of the engine are query rows
   constexpr int BK = 32 * NW;  // keys per workgroup
-  // [Q row][Q transpose][dO row][dO transpose][LSE of the BN rows][D of the BN rows]
-  constexpr int STAGE = 4 * T::TILE_BYTES + 2 * BN * 4;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE / 2];
+  // [Q][dO][LSE of the BN rows][D of the BN rows]
+  constexpr int STAGE = 2 * T::TILE_BYTES + 2 * BN * 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE / 2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -284,7 +303,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   typename T::Lane ln;
   T::init_dma(ln, p.q_ss, p.q_ss, wave, lane);  // Q and dO share the row stride (checked on the host)
   const uint32_t base = lds_offset(smem);
-  T::init_mma(ln, base, base + T::TILE_BYTES, lane);
+  T::init_mma(ln, base, base, lane);  // each tile read row-wise and transposed from one copy
 
   for (int h = g * p.ratio; h < (g + 1) * p.ratio; ++h) {
     const int64_t qrow0 = bi * p.q_sb + h * p.q_sh;
@@ -294,12 +313,14 @@ void bwd_dkdv_kernel(BwdParams p) {
     auto load = [&](int buf, int t) {
       uint16_t *st = smem + buf * (STAGE / 2);
       T::dma1(ln, false, st, qbase, p.q_ss, t * BN, p.s_q, wave);
-      T::dma1(ln, true, st + T::TILE_ELEMS, qbase, p.q_ss, t * BN, p.s_q, wave);
-      T::dma1(ln, false, st + 2 * T::TILE_ELEMS, dobase, p.q_ss, t * BN, p.s_q, wave);
-      T::dma1(ln, true, st + 3 * T::TILE_ELEMS, dobase, p.q_ss, t * BN, p.s_q, wave);
-      if (wave == 0) {  // LSE and D of the tile's rows, 4 bytes per lane; rows past s_q read as zero
+      T::dma1(ln, false, st + T::TILE_ELEMS, dobase, p.q_ss, t * BN, p.s_q, wave);
+      // LSE and D of the tile's rows, 4 bytes per lane; rows past s_q read as
+      // zero.  A direct-to-LDS load writes at lane * 4 for every active lane,
+      // so with tiles shorter than a wave only the first BN lanes take part.
+      static_assert(BN <= 64, "one LSE and one D load per tile");
+      if (wave == 0 && lane < BN) {
         const int r0 = t * BN, nr = max(0, min(BN, p.s_q - r0));
-        uint16_t *aux = st + 4 * T::TILE_ELEMS;
+        uint16_t *aux = st + 2 * T::TILE_ELEMS;
         const uint32_t bytes = (uint32_t)(nr * 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(nr > 0 ? lse_h + r0 : lse_h, bytes), (lds_void *)aux, 4,
                                                  lane * 4, 0, 0, 0);
@@ -308,31 +329,37 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
     };
     __syncthreads();  // the previous head's last tile is consumed
-    if (n_tiles > 0) load(0, t_begin);
-    for (int n = 0; n < n_tiles; ++n) {
-      const int t = t_begin + n, cur = n & 1;
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (n + 1 < n_tiles) load(cur ^ 1, t + 1);
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k)
+      if (k < n_tiles) load(k, t_begin + k);
+    int cur = 0;  // stage of tile n
+    for (int n = 0; n < n_tiles; ++n, cur = cur + 1 == NS ? 0 : cur + 1) {
+      const int t = t_begin + n;
+      // wave 0 also loads the tile's LSE and D
+      if (wave == 0)
+        ring_wait<NS, 2 * T::LOADS + 2>(n + NS - 2 < n_tiles);
+      else
+        ring_wait<NS, 2 * T::LOADS>(n + NS - 2 < n_tiles);
+      __syncthreads();  // also: every wave is done with tile n - 1, whose stage is refilled next
+      if (n + NS - 1 < n_tiles) load(cur == 0 ? NS - 1 : cur - 1, t + NS - 1);
       const int i0 = t * BN;
       // this wave has keys, and (causal) the tile's last row reaches its first key
       if (w_key0 < p.s_k && (!CAUSAL || min(i0 + BN, p.s_q) - 1 + off >= w_key0) &&
           (!WINDOW || i0 <= min(w_key0 + 31, p.s_k - 1) - off + p.window - 1)) {
         {
           const uint32_t so = cur * STAGE;
-          static_assert(T::NKB == 2, "64-row tiles");
           // LSE and D of the rows this lane's registers hold (4 consecutive
           // rows per read; index 4rb + q4: rows 32rb + 8q4 + 4hi .. +3), read
           // first: LDS reads complete in order, so they have landed once the
           // score product's own operand waits have passed.
-          const uint32_t aux = base + so + 4 * T::TILE_BYTES + (4 * hi) * 4;
+          const uint32_t aux = base + so + 2 * T::TILE_BYTES + (4 * hi) * 4;
           f32x4 lv[4 * T::NKB], dv4[4 * T::NKB];
           lds_row4<0>(lv, aux);
           lds_row4<0>(dv4, aux + BN * 4);
           f32x16 s[T::NKB], dp[T::NKB];
           T::scores(s, kreg, ln, so);  // S = Q.K^T: rows in registers, keys in lanes
-          tie8(lv, 8);                 // behind the last operand wait of the product above
-          tie8(dv4, 8);
+          tie8(lv, 4 * T::NKB);        // behind the last operand wait of the product above
+          tie8(dv4, 4 * T::NKB);
           // Group g = 4rb + q4 of a lane's values: rows i0 + 32rb + 8q4 + 4hi + e
           // in registers 4q4 + e of block rb.
           auto visible = [&](int r) {
@@ -361,12 +388,12 @@ void bwd_dkdv_kernel(BwdParams p) {
           };
           // dP = dO.V^T, with P computed between its MMAs
           GroupHook<4 * T::NKB, T::NKK, decltype(p_group)> hp{p_group};
-          T::scores(dp, vreg, ln, so + 2 * T::TILE_BYTES, hp);
+          T::scores(dp, vreg, ln, so + T::TILE_BYTES, hp);
           u32x4 pp[T::NPV], pd[T::NPV];
           pack_operand(s, pp);
           // dV^T += dO^T . P, with dS computed between its MMAs
           GroupHook<4 * T::NKB, T::NPV, decltype(ds_group)> hd{ds_group};
-          T::values(dv, pp, ln, so + 2 * T::TILE_BYTES, hd);
+          T::values(dv, pp, ln, so + T::TILE_BYTES, hd);
           pack_operand(dp, pd);
           T::values(dk, pd, ln, so);  // dK^T += Q^T . dS
         }
@@ -380,12 +407,12 @@ void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // NWQ waves per dQ workgroup (NWQ x 32 query rows), NWK per dK/dV workgroup
-// (NWK x 32 keys).
-template <int D, int BN, bool CAUSAL, bool WINDOW, int NWQ, int NWK>
+// (NWK x 32 keys); NSQ and NSK stages in their rings.
+template <int D, int BN, bool CAUSAL, bool WINDOW, int NWQ, int NWK, int NSQ, int NSK>
 hipError_t launch_backward(const BwdParams &p, hipStream_t stream) {
   const int n_qt = (p.s_q + 32 * NWQ - 1) / (32 * NWQ), n_kt = (p.s_k + 32 * NWK - 1) / (32 * NWK);
   if (n_qt > 0) {  // dQ (zero when there are no keys), D and the sink partials
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL, WINDOW, NWQ>), dim3(p.b * p.h_q * n_qt), dim3(NWQ * 64), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL, WINDOW, NWQ, NSQ>), dim3(p.b * p.h_q * n_qt), dim3(NWQ * 64), 0,
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -396,7 +423,7 @@ hipError_t launch_backward(const BwdParams &p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (n_kt > 0) {  // dK, dV (zero when there are no rows)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BN, CAUSAL, WINDOW, NWK>), dim3(p.b * p.h_kv * n_kt), dim3(NWK * 64), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BN, CAUSAL, WINDOW, NWK, NSK>), dim3(p.b * p.h_kv * n_kt), dim3(NWK * 64), 0,
                        stream, p);
     return hipGetLastError();
   }

@@ -175,7 +175,9 @@ __device__ __forceinline__ void lds_wait(V (&a)[M]) {
 // DS is the head-dim slice a wave works on: DS = D normally; for D = 512 two
 // waves share the same query rows and each takes one 256-wide half, for the
 // partial scores as well as for the output columns (see prefill.hpp).
-template <int D, int NW, int BN, int DS = D>
+// XS: one swizzle for both read patterns, so that a tile read row-wise (score
+// MMA) and transposed (value MMA) is staged once (the backward's tiles).
+template <int D, int NW, int BN, int DS = D, bool XS = false>
 struct Tile {
   static constexpr int NT = NW * 64;   // threads per workgroup
   static constexpr int SPLIT = D / DS; // waves sharing one block of query rows
@@ -194,13 +196,32 @@ struct Tile {
   static constexpr float kLazy = 8.0f;  // log2 of the growth that forces a rescale
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(STAGE_BYTES <= 65536, "LDS immediate offsets must stay below 64 KiB");
+  static_assert(!XS || CH >= 8, "the shared swizzle needs rows of at least 8 chunks");
 
   // Chunk swizzle for the score MMA's K reads: 16 lanes read one chunk of 16
   // consecutive rows.
-  __device__ static __forceinline__ int kswz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+  __device__ static __forceinline__ int kswz(int r) {
+    if constexpr (XS) return xswz(r);
+    return D == 64 ? ((r >> 1) & 7) : (r & 15);
+  }
   // Chunk swizzle for the value MMA's transposed V reads: 16 lanes read 4
   // chunks of 4 consecutive rows.
-  __device__ static __forceinline__ int vswz(int r) { return 4 * ((r / ROWS_PER_256) & 3) & (CH - 1); }
+  __device__ static __forceinline__ int vswz(int r) {
+    if constexpr (XS) return xswz(r);
+    return 4 * ((r / ROWS_PER_256) & 3) & (CH - 1);
+  }
+  // The shared swizzle.  Rows of 256 bytes or more start on bank 0: the
+  // row-wise reads want 16 distinct values over any 16 aligned rows, the
+  // transposed reads 4 distinct values of swz >> 2 over any 4 aligned rows;
+  // 4 (r mod 4) + (r / 4 mod 4) gives both.  At D = 64 two rows share the 64
+  // banks: the row-wise reads want 8 distinct values over the even rows of 16
+  // aligned ones (and over the odd ones), the transposed reads distinct swz >> 2
+  // for rows 4m and 4m + 2; 4 (r / 2 mod 2) + (r / 4 mod 4) gives both.  Either
+  // way rows r and r + 8 differ by 2 (bit 5 of the byte address) and rows r and
+  // r + 16 not at all.
+  __device__ static __forceinline__ int xswz(int r) {
+    return D == 64 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : 4 * (r & 3) + ((r >> 2) & 3);
+  }
 
   // Per-lane constants: global byte offsets of this lane's DMA chunks inside a
   // tile, and LDS byte addresses (stage 0) of its MMA operands.
@@ -467,8 +488,11 @@ struct Tile {
   __device__ static __forceinline__ void vread_blocks(u32x2 (&v)[2 * VG], const Lane &ln, uint32_t stage_off) {
     constexpr int DB = DB0 + I;
     constexpr int XO = (DB / NVL) * 256;
-    v[2 * I] = ds_read_tr16<OFF_LO + XO>(ln.vl[DB % NVL] + stage_off);
-    v[2 * I + 1] = ds_read_tr16<OFF_HI + XO>(ln.vl[DB % NVL] + stage_off);
+    const uint32_t a = ln.vl[DB % NVL] + stage_off;
+    v[2 * I] = ds_read_tr16<OFF_LO + XO>(a);
+    // under the shared swizzle the rows 8 further sit at chunk ^ 2: address bit 5
+    // (stage offsets are multiples of 64 bytes, row strides of 256)
+    v[2 * I + 1] = ds_read_tr16<OFF_HI + XO>(XS ? (a ^ 32u) : a);
     if constexpr (I + 1 < VG) vread_blocks<OFF_LO, OFF_HI, DB0, I + 1>(v, ln, stage_off);
   }
   // After the MMAs of the last unit of k-step T are issued, hook.vstep<T>() runs.

@@ -100,6 +100,9 @@ WORKLOADS = {
            s_q=16384, s_k=16384, causal=True),
         _w("wide_b1_h4_s4096_d512_causal", "prefill", BASE_SEED + 4, 512, 4, 4, b=1,
            s_q=4096, s_k=4096, causal=True),
+        # backward at d = 256: the d = 128 backward's shape with half the heads (same flops)
+        _w("bwd_mha_b2_h8_s4096_d256_causal", "backward", BASE_SEED + 4, 256, 8, 8, b=2, s_q=4096,
+           s_k=4096, causal=True),
     ]
 }
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 9
+#define ATTN_FWD_ABI_VERSION 10
 
 typedef enum {
   ATTN_OK = 0,
@@ -308,7 +308,7 @@ typedef struct {
  *       caller-owned (row sums D and the rows' LSE in base 2 between the
  *       kernels, and the sink gradient's per-tile partials).
  * Kernels run on `stream`: dQ and D, the sink gradient (if wanted), then dK/dV.
- * Supported: d = 64 or 128; causal (bottom-right) or not; h_q % h_kv == 0.
+ * Supported: d = 64, 128 or 256; causal (bottom-right) or not; h_q % h_kv == 0.
  */
 typedef struct {
   const void *q, *k, *v, *o, *d_o;
@@ -325,7 +325,9 @@ typedef struct {
   float *d_sinks;
 } attn_bwd_args;
 
-/* Bytes of device workspace attn_bwd needs (0 on invalid sizes). */
+/* Bytes of device workspace attn_bwd needs at any supported d (0 on invalid
+ * sizes): two fp32 values per query row, each array 256-byte aligned, then one
+ * fp32 sink-gradient partial per 128 query rows of each (batch, head). */
 size_t attn_bwd_workspace_size(int32_t b, int32_t h_q, int32_t s_q);
 
 /*

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     lib = afa.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
-    assert lib.attn_abi_version() == 9
+    assert lib.attn_abi_version() == 10
 
 
 def test_status_strings():
@@ -513,7 +513,8 @@ def good_bwd(**over):
 BWD_BAD = [
     ("null lse", dict(lse=None), 1),
     ("null dv", dict(dv=None), 1),
-    ("d=256", dict(d=256), 2),
+    ("d=512", dict(d=512), 2),
+    ("d=96", dict(d=96), 2),
     ("ratio", dict(h_q=6, h_kv=4), 2),
     ("causal 2", dict(causal=2), 2),
     ("zero scale", dict(scale=0.0), 2),
@@ -549,8 +550,10 @@ def test_bwd_workspace_checks():
     lib = afa.load_library()
     a = good_bwd()
     need = lib.attn_bwd_workspace_size(2, 16, 4096)
-    # D per row, then the sink-gradient partials per 256-row query tile of the dQ kernel
-    assert need == 2 * (2 * 16 * 4096 * 4) + 2 * 16 * (4096 // 256) * 4  # D and base-2 LSE, then sink partials
+    # D and the base-2 LSE per row, then the sink-gradient partials per 128 query rows (the
+    # dQ kernel's shortest query tile, at d = 256)
+    assert need == 2 * (2 * 16 * 4096 * 4) + 2 * 16 * (4096 // 128) * 4
+    assert lib.attn_bwd_workspace_size(1, 1, 129) == 2 * 768 + 2 * 4  # 516 bytes of rows aligned to 768
     assert lib.attn_bwd(ctypes.byref(a), None, need, None) == 6
     assert lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE), need - 1, None) == 6
     assert lib.attn_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), need, None) == 4

@@ -31,7 +31,7 @@ import torch
 
 import attention_forward_attn_amd as afa
 import oracle
-from attention_forward_attn_amd.inputs import prefill_inputs
+from attention_forward_attn_amd.inputs import WORKLOADS, backward_inputs, prefill_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -110,7 +110,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_backward_small(case, d):
     print(f"backward case {case} d={d}", flush=True)
     got, want, ed = run_case(*case, seed=51, d=d)
@@ -128,7 +128,7 @@ WINDOWED = [
 
 
 @pytest.mark.parametrize("case", WINDOWED, ids=[str(c) for c in WINDOWED])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_backward_window_and_sink(case, d):
     """Sliding window and sink: dQ, dK, dV and the sink gradient against the oracle."""
     b, h_q, h_kv, s_q, s_k, window, sink = case
@@ -168,17 +168,47 @@ def test_backward_sink_gradient_without_rows():
     assert torch.equal(got[1], torch.zeros_like(k)) and torch.equal(got[2], torch.zeros_like(k))
 
 
-def test_backward_long_heads():
+@pytest.mark.parametrize("d", [128, 256])
+def test_backward_long_heads(d):
     """Two heads at 2048 tokens: many key and row tiles, every output compared."""
-    print("backward b1 h2 s2048 causal", flush=True)
-    got, want, ed = run_case(1, 2, 2, 2048, 2048, True, seed=52)
+    print(f"backward b1 h2 s2048 causal d={d}", flush=True)
+    got, want, ed = run_case(1, 2, 2, 2048, 2048, True, seed=52, d=d)
     for name, g, w, e in zip(("dQ", "dK", "dV"), got, want, ed):
-        grad_check(g, w, name, e)
+        grad_check(g, w, f"d={d} {name}", e)
 
 
-def test_backward_deterministic():
-    inp = prefill_inputs(1, 4, 2, 300, 300, 128, 53)
-    d_o = torch.randn(1, 4, 300, 128).to(torch.bfloat16).to(DEV)
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.kind == "backward"])
+def test_backward_workload_full_size(name):
+    """A backward workload at its full size, in the bench's call: outputs pre-filled with NaN (a
+    row never written fails), every element finite, and every element of two whole heads (the
+    first of the first batch, the last of the last) against the oracle, which sees the same
+    bf16 inputs for that head alone (MHA: a kv head's gradients come from its one query head)."""
+    w = WORKLOADS[name]
+    assert w.h_q == w.h_kv, "one query head per kv head"
+    print(f"backward workload {name}", flush=True)
+    inp = backward_inputs(w.b, w.h_q, w.h_kv, w.s_q, w.s_k, w.d, w.seed)
+    q, k, v, d_o = (inp[n].to(DEV) for n in ("q", "k", "v", "d_o"))
+    o, lse = afa.prefill(q, k, v, causal=w.causal)
+    nan = float("nan")
+    dq, dk, dv = torch.full_like(q, nan), torch.full_like(k, nan), torch.full_like(k, nan)
+    afa.backward(q, k, v, o, d_o, lse, causal=w.causal, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for nm, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(t).all()), f"{name}: {nm} has unwritten or non-finite elements"
+    scale = 1 / math.sqrt(w.d)
+    for bi, h in ((0, 0), (w.b - 1, w.h_q - 1)):
+        one = {n: inp[n][bi:bi + 1, h:h + 1].contiguous() for n in ("q", "k", "v", "d_o")}
+        want = oracle.attention_backward_ref(one["q"], one["k"], one["v"], one["d_o"], scale, w.causal, 0, None)
+        eq, ek = d_error_terms(one, one["d_o"], scale, w.causal, 0, None)
+        got = (dq[bi:bi + 1, h:h + 1], dk[bi:bi + 1, h:h + 1], dv[bi:bi + 1, h:h + 1])
+        for nm, g, wt, e in zip(("dQ", "dK", "dV"), got, want, (eq, ek, 0.0)):
+            grad_check(g, wt, f"{name} b={bi} h={h} {nm}", e)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_backward_deterministic(d):
+    inp = prefill_inputs(1, 4, 2, 300, 300, d, 53)
+    d_o = torch.randn(1, 4, 300, d).to(torch.bfloat16).to(DEV)
     q, k, v = inp["q"].to(DEV), inp["k"].to(DEV), inp["v"].to(DEV)
     o, lse = afa.prefill(q, k, v, causal=True)
     r1 = afa.backward(q, k, v, o, d_o, lse, causal=True)
