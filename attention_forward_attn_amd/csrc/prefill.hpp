@@ -549,7 +549,7 @@ __device__ __forceinline__ void pp_unit(const PrefillParams &p, int bh, int qt, 
   auto softmax_phase = [&](int i) {
     if (i >= 0 && active(t_begin + i)) {
       mask(s, t_begin + i);
-      T::softmax_step(s, pk, o, m, l, p.c);
+      T::template softmax_step<true>(s, pk, o, m, l, p.c);
       if constexpr (T::PV_S_FUSED) T::values_issue0(vpre, ln, (i % STAGES) * T::STAGE_BYTES);
     }
   };

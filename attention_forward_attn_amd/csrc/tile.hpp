@@ -95,21 +95,6 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 // including the prefetch of later tiles.
 __device__ __forceinline__ void barrier_nofence() { __builtin_amdgcn_s_barrier(); }
 
-// Eight independent 2^x (v_exp_f32, the instruction behind fast_exp2) issued
-// back to back.  Left to itself the compiler pairs every exp with the FMA
-// that feeds it, so a single wave stalls on each pair; here all eight
-// arguments are computed first.  The trailing s_nop gives the wait state a
-// vector instruction needs before reading a transcendental result (one is
-// required, two are given), which the compiler cannot see through the asm
-// statement.
-__device__ __forceinline__ void exp2_x8(float (&e)[8], const float (&t)[8]) {
-  asm volatile(
-      "v_exp_f32 %0, %8\n v_exp_f32 %1, %9\n v_exp_f32 %2, %10\n v_exp_f32 %3, %11\n"
-      "v_exp_f32 %4, %12\n v_exp_f32 %5, %13\n v_exp_f32 %6, %14\n v_exp_f32 %7, %15\n s_nop 1"
-      : "=&v"(e[0]), "=&v"(e[1]), "=&v"(e[2]), "=&v"(e[3]), "=&v"(e[4]), "=&v"(e[5]), "=&v"(e[6]), "=&v"(e[7])
-      : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(t[4]), "v"(t[5]), "v"(t[6]), "v"(t[7]));
-}
-
 // 32-bit LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   const __attribute__((address_space(3))) char *q = (const __attribute__((address_space(3))) char *)p;
@@ -170,6 +155,45 @@ __device__ __forceinline__ void lds_wait(V (&a)[M]) {
   asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
 #pragma unroll
   for (int i = 0; i < M; i += 8) tie8(a + i, M - i < 8 ? M - i : 8);
+}
+
+// Eight independent 2^x (v_exp_f32, the instruction behind fast_exp2) issued
+// back to back.  Left to itself the compiler pairs every exp with the FMA
+// that feeds it, so a single wave stalls on each pair; here all eight
+// arguments are computed first.  The trailing s_nop gives the wait state a
+// vector instruction needs before reading a transcendental result (one is
+// required, two are given), which the compiler cannot see through the asm
+// statement.
+__device__ __forceinline__ void exp2_x8(float (&e)[8], const float (&t)[8]) {
+  asm volatile(
+      "v_exp_f32 %0, %8\n v_exp_f32 %1, %9\n v_exp_f32 %2, %10\n v_exp_f32 %3, %11\n"
+      "v_exp_f32 %4, %12\n v_exp_f32 %5, %13\n v_exp_f32 %6, %14\n v_exp_f32 %7, %15\n s_nop 1"
+      : "=&v"(e[0]), "=&v"(e[1]), "=&v"(e[2]), "=&v"(e[3]), "=&v"(e[4]), "=&v"(e[5]), "=&v"(e[6]), "=&v"(e[7])
+      : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(t[4]), "v"(t[5]), "v"(t[6]), "v"(t[7]));
+}
+
+// 2^x of N values in place, N a multiple of 8: every argument is computed
+// before the first v_exp_f32 and every result is used after the last one, so
+// the exponentials of a whole tile issue back to back and each consumer finds
+// its input long done (a transcendental takes far longer to deliver its
+// result than to issue: with eight in flight a lone wave waits on each group).
+// The s_nop is the wait state a vector instruction needs before reading a
+// transcendental result, which the compiler cannot see through the asm.
+template <int N>
+__device__ __forceinline__ void exp2_all(float (&x)[N]) {
+  static_assert(N % 8 == 0, "groups of eight");
+#pragma unroll
+  for (int g = 0; g < N; g += 8) tie8(x + g, 8);
+#pragma unroll
+  for (int g = 0; g < N; g += 8)
+    asm volatile(
+        "v_exp_f32 %0, %0\n v_exp_f32 %1, %1\n v_exp_f32 %2, %2\n v_exp_f32 %3, %3\n"
+        "v_exp_f32 %4, %4\n v_exp_f32 %5, %5\n v_exp_f32 %6, %6\n v_exp_f32 %7, %7"
+        : "+v"(x[g]), "+v"(x[g + 1]), "+v"(x[g + 2]), "+v"(x[g + 3]), "+v"(x[g + 4]), "+v"(x[g + 5]),
+          "+v"(x[g + 6]), "+v"(x[g + 7]));
+  asm volatile("s_nop 1");
+#pragma unroll
+  for (int g = 0; g < N; g += 8) tie8(x + g, 8);
 }
 
 // DS is the head-dim slice a wave works on: DS = D normally; for D = 512 two
@@ -745,35 +769,54 @@ struct Tile {
     }
     return (m == kNegInf) ? 0.0f : m;
   }
-  // Second half, for the 16 keys of value k-step T: numerators 2^(c*s - base)
-  // packed to bf16 into pk[T], their fp32 sum added to rs.
-  template <int T_>
-  __device__ static __forceinline__ void softmax_exp(const f32x16 (&s)[NKB], u32x4 (&pk)[NPV], float &rs,
-                                                     float c, float base) {
-    constexpr int kb = T_ >> 1, r0 = (T_ & 1) * 8;
-    float t[8], e[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = fmaf(s[kb][r0 + j], c, -base);
-    exp2_x8(e, t);
-    u32x4 x;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) x[q] = pack_bf16x2(e[2 * q], e[2 * q + 1]);
-    pk[T_] = x;
-    rs += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-  }
-  template <int T_ = 0>
+  // Second half: numerators 2^(c*s - base) of the tile, packed to bf16 into pk
+  // (value k-step T takes the 16 keys of block T/2, registers 8(T mod 2) ..
+  // +7), their fp32 sum added to rs.  GROUPED: the exponentials go in groups of
+  // eight, each group's results used before the next group's arguments are
+  // formed; otherwise all exponentials of the tile issue back to back (faster
+  // for a lone wave; the ping-pong kernels keep the groups, whose softmax phase
+  // then stays as long as the other group's MMA phase that it overlaps).
+  template <bool GROUPED>
   __device__ static __forceinline__ void softmax_exp_all(const f32x16 (&s)[NKB], u32x4 (&pk)[NPV], float &rs,
                                                          float c, float base) {
-    softmax_exp<T_>(s, pk, rs, c, base);
-    if constexpr (T_ + 1 < NPV) softmax_exp_all<T_ + 1>(s, pk, rs, c, base);
+    float e[16 * NKB];
+    auto pack_sum = [&](int t) {
+      const float *et = e + 8 * t;
+      u32x4 x;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = pack_bf16x2(et[2 * q], et[2 * q + 1]);
+      pk[t] = x;
+      rs += ((et[0] + et[1]) + (et[2] + et[3])) + ((et[4] + et[5]) + (et[6] + et[7]));
+    };
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int t = 0; t < NPV; ++t) {
+        float g[8], r[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) g[j] = fmaf(s[t >> 1][8 * (t & 1) + j], c, -base);
+        exp2_x8(r, g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[8 * t + j] = r[j];
+        pack_sum(t);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e[16 * kb + i] = fmaf(s[kb][i], c, -base);
+      exp2_all(e);
+#pragma unroll
+      for (int t = 0; t < NPV; ++t) pack_sum(t);
+    }
   }
   // The whole update on one tile (no overlap with other work).
+  template <bool GROUPED = false>
   __device__ static __forceinline__ void softmax_step(f32x16 (&s)[NKB], u32x4 (&pk)[NPV],
                                                       f32x16 (&o)[NDB], float &m, float &l,
                                                       float c) {
     const float base = softmax_max(s, o, m, l, c);
     float rs = 0.0f;
-    softmax_exp_all(s, pk, rs, c, base);
+    softmax_exp_all<GROUPED>(s, pk, rs, c, base);
     l += rs;
   }
 };
