@@ -116,6 +116,10 @@ __device__ __forceinline__ void store_rows(uint16_t *op, const f32x16 (&a)[NDB],
 
 // ---------------------------------------------------------------------------
 // dQ (and D).  NS: stages of the K/V ring.
+// With one wave per SIMD (NW = 4) P is computed between the dP MMAs; with two
+// the other wave hides the exponentials and the hook measured slower.
+template <int NW>
+constexpr bool kDqPHook = NW == 4;
 template <int D, int BN, bool CAUSAL, bool WINDOW, int NW, int NS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dq_kernel(BwdParams p) {
@@ -205,26 +209,54 @@ void bwd_dq_kernel(BwdParams p) {
       const uint32_t so = cur * STAGE;
       f32x16 s[T::NKB], dp[T::NKB];
       T::scores(s, qreg, ln, so);
-      T::scores(dp, dreg, ln, so + T::TILE_BYTES);
       // Every key of the tile visible to every row of the wave: no per-key test.
       const bool full = j0 + BN <= p.s_k && (!CAUSAL || j0 + BN - 1 <= w_lo + off) &&
                         (!WINDOW || j0 >= w_hi + off - p.window + 1);
-      if (full) {
-#pragma unroll
-        for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], p.c, -lse2)) * (dp[kb][i] - dd);
-      } else {
+      if constexpr (kDqPHook<NW>) {
+        // P = exp(scale*S - LSE) in groups of four between the MMAs of dP (a
+        // lone wave per SIMD has no other wave to hide its exponentials behind),
+        // then dS = P * (dP - D).
         const int lim = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
         const int lo = WINDOW ? row + off - p.window + 1 : 0;
+        auto p_group = [&](int gi) {
+          const int kb = gi >> 2, q4 = gi & 3;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            const float pv = fast_exp2(fmaf(s[kb][i], p.c, -lse2));
+            if (full) {
+              s[kb][i] = pv;
+            } else {
+              const int j = j0 + T::key_of(kb, i, hi);
+              s[kb][i] = (j > lim || j < lo) ? 0.0f : pv;
+            }
+          }
+        };
+        GroupHook<4 * T::NKB, T::NKK, decltype(p_group)> hp{p_group};
+        T::scores(dp, dreg, ln, so + T::TILE_BYTES, hp);
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = j0 + T::key_of(kb, i, hi);
-            const float pv = (j > lim || j < lo) ? 0.0f : fast_exp2(fmaf(s[kb][i], p.c, -lse2));
-            s[kb][i] = pv * (dp[kb][i] - dd);  // dS
-          }
+          for (int i = 0; i < 16; ++i) s[kb][i] *= dp[kb][i] - dd;
+      } else {
+        T::scores(dp, dreg, ln, so + T::TILE_BYTES);
+        if (full) {
+#pragma unroll
+          for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], p.c, -lse2)) * (dp[kb][i] - dd);
+        } else {
+          const int lim = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
+          const int lo = WINDOW ? row + off - p.window + 1 : 0;
+#pragma unroll
+          for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = j0 + T::key_of(kb, i, hi);
+              const float pv = (j > lim || j < lo) ? 0.0f : fast_exp2(fmaf(s[kb][i], p.c, -lse2));
+              s[kb][i] = pv * (dp[kb][i] - dd);  // dS
+            }
+        }
       }
       u32x4 pk[T::NPV];
       pack_operand(s, pk);
