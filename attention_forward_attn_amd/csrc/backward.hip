@@ -20,6 +20,7 @@ constexpr int BWD_NSQ = 2;
 constexpr int BWD_NSK = 2;
 constexpr int BWD_NSQ256 = 2;
 constexpr int BWD_NSK256 = 2;
+constexpr int BWD_BNQ256 = 64;  // keys per dQ tile at d = 256 (two stages of K and V: 128 KiB)
 // Rows per dQ workgroup, at its smallest over the head dims (sizes the
 // sink-gradient partials of the workspace, one per query tile).
 int backward_block_rows() { return 32 * BWD_NW256; }
@@ -30,9 +31,9 @@ hipError_t backward(int d, const BwdParams &p, bool causal, hipStream_t s) {
            : causal ? launch_backward<64, 64, true, false, BWD_NWQ, BWD_NWK, BWD_NSQ, BWD_NSK>(p, s)
                     : launch_backward<64, 64, false, false, BWD_NWQ, BWD_NWK, BWD_NSQ, BWD_NSK>(p, s);
   if (d == 256)
-    return window   ? launch_backward<256, 32, true, true, BWD_NW256, BWD_NW256, BWD_NSQ256, BWD_NSK256>(p, s)
-           : causal ? launch_backward<256, 32, true, false, BWD_NW256, BWD_NW256, BWD_NSQ256, BWD_NSK256>(p, s)
-                    : launch_backward<256, 32, false, false, BWD_NW256, BWD_NW256, BWD_NSQ256, BWD_NSK256>(p, s);
+    return window   ? launch_backward<256, 32, true, true, BWD_NW256, BWD_NW256, BWD_NSQ256, BWD_NSK256, BWD_BNQ256>(p, s)
+           : causal ? launch_backward<256, 32, true, false, BWD_NW256, BWD_NW256, BWD_NSQ256, BWD_NSK256, BWD_BNQ256>(p, s)
+                    : launch_backward<256, 32, false, false, BWD_NW256, BWD_NW256, BWD_NSQ256, BWD_NSK256, BWD_BNQ256>(p, s);
   return window   ? launch_backward<128, 64, true, true, BWD_NWQ, BWD_NWK, BWD_NSQ, BWD_NSK>(p, s)
          : causal ? launch_backward<128, 64, true, false, BWD_NWQ, BWD_NWK, BWD_NSQ, BWD_NSK>(p, s)
                   : launch_backward<128, 64, false, false, BWD_NWQ, BWD_NWK, BWD_NSQ, BWD_NSK>(p, s);

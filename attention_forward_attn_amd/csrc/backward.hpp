@@ -439,12 +439,13 @@ void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // NWQ waves per dQ workgroup (NWQ x 32 query rows), NWK per dK/dV workgroup
-// (NWK x 32 keys); NSQ and NSK stages in their rings.
-template <int D, int BN, bool CAUSAL, bool WINDOW, int NWQ, int NWK, int NSQ, int NSK>
+// (NWK x 32 keys); NSQ and NSK stages in their rings; BNQ keys per dQ tile,
+// BN query rows per dK/dV tile.
+template <int D, int BN, bool CAUSAL, bool WINDOW, int NWQ, int NWK, int NSQ, int NSK, int BNQ = BN>
 hipError_t launch_backward(const BwdParams &p, hipStream_t stream) {
   const int n_qt = (p.s_q + 32 * NWQ - 1) / (32 * NWQ), n_kt = (p.s_k + 32 * NWK - 1) / (32 * NWK);
   if (n_qt > 0) {  // dQ (zero when there are no keys), D and the sink partials
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BN, CAUSAL, WINDOW, NWQ, NSQ>), dim3(p.b * p.h_q * n_qt), dim3(NWQ * 64), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BNQ, CAUSAL, WINDOW, NWQ, NSQ>), dim3(p.b * p.h_q * n_qt), dim3(NWQ * 64), 0,
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
