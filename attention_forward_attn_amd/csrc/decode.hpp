@@ -26,7 +26,9 @@
 //
 // Decode streams K/V once, so the kernel is built to keep bytes in flight:
 // an LDS ring of STAGES tiles of which STAGES-1 are being loaded while one is
-// consumed.  Every iteration issues exactly one tile's loads (tiles past the
+// consumed.  The loads carry the non-temporal hint (kStreamOnce): lines read
+// once take no retention priority in L2 (about 3 % faster at d = 128 and 6 %
+// at d = 256).  Every iteration issues exactly one tile's loads (tiles past the
 // end get an empty buffer descriptor and load nothing), so the wait count is a
 // constant.
 //
@@ -235,16 +237,17 @@ void decode_split_kernel(DecodeParams p) {
   if constexpr (PAGED) TD::init_dma_paged(dl, p.k_st, p.v_st, wave, lane);
   else TD::init_dma(dl, p.k_st, p.v_st, wave, lane);
   auto load_tile = [&](uint16_t *stage, int t) {
+    uint8_t *stage8 = reinterpret_cast<uint8_t *>(stage);
     if constexpr (FP8 && PAGED)
-      F8::dma_paged(fl, reinterpret_cast<uint8_t *>(stage), kbase8, p.k_st, p.k_ps, vbase8, p.v_st, p.v_ps, pg,
-                    p.page_shift, p.n_pages, t * BN, n_keys, wave);
+      F8::template dma_paged<kStreamOnce>(fl, stage8, kbase8, p.k_st, p.k_ps, vbase8, p.v_st, p.v_ps, pg,
+                                          p.page_shift, p.n_pages, t * BN, n_keys, wave);
     else if constexpr (FP8)
-      F8::dma(fl, reinterpret_cast<uint8_t *>(stage), kbase8, p.k_st, vbase8, p.v_st, t * BN, n_keys, wave);
+      F8::template dma<kStreamOnce>(fl, stage8, kbase8, p.k_st, vbase8, p.v_st, t * BN, n_keys, wave);
     else if constexpr (PAGED)
-      TD::dma_paged(dl, stage, kbase, p.k_st, p.k_ps, vbase, p.v_st, p.v_ps, pg, p.page_shift, p.n_pages, t * BN,
-                    n_keys, wave);
+      TD::template dma_paged<kStreamOnce>(dl, stage, kbase, p.k_st, p.k_ps, vbase, p.v_st, p.v_ps, pg,
+                                          p.page_shift, p.n_pages, t * BN, n_keys, wave);
     else
-      TD::dma(dl, stage, kbase, p.k_st, vbase, p.v_st, t * BN, n_keys, wave);
+      TD::template dma<kStreamOnce>(dl, stage, kbase, p.k_st, vbase, p.v_st, t * BN, n_keys, wave);
   };
   typename TC::Lane ml;
   const uint32_t base = lds_offset(smem);

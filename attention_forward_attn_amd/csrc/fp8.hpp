@@ -102,7 +102,9 @@ struct Fp8Tile {
   }
 
   // This wave's DMA share of the tile of keys [j0, j0 + BN) into `stage`
-  // (K tile then V tile); rows at or past nkeys read as zero.
+  // (K tile then V tile); rows at or past nkeys read as zero.  CP is the
+  // loads' cache-policy operand.
+  template <int CP = 0>
   __device__ static __forceinline__ void dma(const Lane &ln, uint8_t *stage, const uint8_t *kbase, int64_t k_rs,
                                              const uint8_t *vbase, int64_t v_rs, int j0, int nkeys, int w) {
     const int rows = min(nkeys - j0, BN);
@@ -112,11 +114,11 @@ struct Fp8Tile {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(rows > 0 ? vbase + j0 * v_rs : vbase, vb);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(stage + (u * NW + w) * 1024), 16, ln.kg[u], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(stage + (u * NW + w) * 1024), 16, ln.kg[u], 0, 0, CP);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(stage + TILE_BYTES + (u * NW + w) * 1024), 16,
-                                               ln.vg[u], 0, 0, 0);
+                                               ln.vg[u], 0, 0, CP);
   }
 
   // Paged caches: a 1-KiB load holds RPL whole rows, which always sit in one
@@ -138,6 +140,7 @@ struct Fp8Tile {
   // readlane(pg, j >> shift), at head + page * page_rs + row * rs (bytes).
   // Rows at or past nkeys, and pages outside [0, n_pages), read as zero
   // without touching memory.
+  template <int CP = 0>
   __device__ static __forceinline__ void dma_paged(const Lane &ln, uint8_t *stage, const uint8_t *khead,
                                                    int64_t k_rs, int64_t k_page_rs, const uint8_t *vhead,
                                                    int64_t v_rs, int64_t v_page_rs, int pg, int shift, int n_pages,
@@ -152,10 +155,10 @@ struct Fp8Tile {
       const uint8_t *kb = khead + (int64_t)page * k_page_rs + slot * k_rs;
       const uint8_t *vb = vhead + (int64_t)page * v_page_rs + slot * v_rs;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(ok ? kb : khead, ok ? (uint32_t)((nv - 1) * k_rs + D) : 0u),
-                                               (lds_void *)(stage + (u * NW + w) * 1024), 16, ln.kg[u], 0, 0, 0);
+                                               (lds_void *)(stage + (u * NW + w) * 1024), 16, ln.kg[u], 0, 0, CP);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(ok ? vb : vhead, ok ? (uint32_t)((nv - 1) * v_rs + D) : 0u),
                                                (lds_void *)(stage + TILE_BYTES + (u * NW + w) * 1024), 16,
-                                               ln.vg[u], 0, 0, 0);
+                                               ln.vg[u], 0, 0, CP);
     }
   }
 

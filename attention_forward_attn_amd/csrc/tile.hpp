@@ -105,6 +105,9 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
 // access is coherent at device scope (a store is written through the XCD's
 // L2, a load does not take a line another XCD may have changed from it).
 constexpr int kDeviceCoherent = 16;
+// Cache-policy operand that sets nt: the data is streamed through once (the
+// decode's K/V), so its lines get no retention priority in the caches.
+constexpr int kStreamOnce = 2;
 
 // Buffer descriptor over [base, base + bytes) (gfx9 raw buffer, stride 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -319,7 +322,9 @@ struct Tile {
   // so its loads touch no memory and only write zeros to LDS.  Byte offsets
   // inside a tile must fit in 32 bits (row strides below 2^24 elements,
   // checked by the host).
-  // (is_v selects the V lane offsets; a constant at every call.)
+  // (is_v selects the V lane offsets; a constant at every call.)  CP is the
+  // loads' cache-policy operand.
+  template <int CP = 0>
   __device__ static __forceinline__ void dma1(const Lane &ln, bool is_v, uint16_t *dst, const uint16_t *base,
                                               int64_t rs, int j0, int nkeys, int w) {
     const int rows = min(nkeys - j0, BN);
@@ -336,7 +341,7 @@ struct Tile {
       } else {
         off = is_v ? ln.vg[u] : ln.kg[u];
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (u * NW + w) * 512), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (u * NW + w) * 512), 16, off, 0, 0, CP);
     }
   }
   __device__ static __forceinline__ void dma_k(const Lane &ln, uint16_t *dst, const uint16_t *base,
@@ -348,11 +353,12 @@ struct Tile {
     dma1(ln, true, dst, base, rs, j0, nkeys, w);
   }
   // K and V tiles of one key range into a stage laid out as [K tile][V tile].
+  template <int CP = 0>
   __device__ static __forceinline__ void dma(const Lane &ln, uint16_t *stage, const uint16_t *kbase,
                                              int64_t k_rs, const uint16_t *vbase, int64_t v_rs,
                                              int j0, int nkeys, int w) {
-    dma1(ln, false, stage, kbase, k_rs, j0, nkeys, w);
-    dma1(ln, true, stage + TILE_ELEMS, vbase, v_rs, j0, nkeys, w);
+    dma1<CP>(ln, false, stage, kbase, k_rs, j0, nkeys, w);
+    dma1<CP>(ln, true, stage + TILE_ELEMS, vbase, v_rs, j0, nkeys, w);
   }
   // Paged caches: a load's 64/CH consecutive tile rows always sit in one page
   // (pages hold at least 16 rows), so each load gets its own descriptor and
@@ -372,6 +378,7 @@ struct Tile {
   // readlane(pg, j >> shift) at `head` + page * page_rs + row * rs.  Rows at or
   // past nkeys, and pages outside [0, n_pages), read as zero without touching
   // memory.  jt and w must be wave-uniform.
+  template <int CP = 0>
   __device__ static __forceinline__ void dma1_paged(const Lane &ln, bool is_v, uint16_t *dst, const uint16_t *head,
                                                     int64_t rs, int64_t page_rs, int pg, int shift, int n_pages,
                                                     int jt, int nkeys, int w) {
@@ -386,15 +393,16 @@ struct Tile {
       const uint32_t bytes = ok ? (uint32_t)((nv - 1) * rs * 2 + D * 2) : 0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(ok ? base : head, bytes),
                                                (lds_void *)(dst + (u * NW + w) * 512), 16,
-                                               is_v ? ln.vg[u] : ln.kg[u], 0, 0, 0);
+                                               is_v ? ln.vg[u] : ln.kg[u], 0, 0, CP);
     }
   }
+  template <int CP = 0>
   __device__ static __forceinline__ void dma_paged(const Lane &ln, uint16_t *stage, const uint16_t *khead,
                                                    int64_t k_rs, int64_t k_page_rs, const uint16_t *vhead,
                                                    int64_t v_rs, int64_t v_page_rs, int pg, int shift,
                                                    int n_pages, int jt, int nkeys, int w) {
-    dma1_paged(ln, false, stage, khead, k_rs, k_page_rs, pg, shift, n_pages, jt, nkeys, w);
-    dma1_paged(ln, true, stage + TILE_ELEMS, vhead, v_rs, v_page_rs, pg, shift, n_pages, jt, nkeys, w);
+    dma1_paged<CP>(ln, false, stage, khead, k_rs, k_page_rs, pg, shift, n_pages, jt, nkeys, w);
+    dma1_paged<CP>(ln, true, stage + TILE_ELEMS, vhead, v_rs, v_page_rs, pg, shift, n_pages, jt, nkeys, w);
   }
   // The same loads, issued from inside an MMA schedule: step<G>() issues the
   // K share after MMA group GK and the V share after group GV.
