@@ -88,9 +88,9 @@ attn_status run_decode(attn::DecodeParams &p, const int32_t *kv_len, const float
   const int64_t unit_grid = attn::decode_grid_size(n_split, B, h_kv, n_hblk);
   if (unit_grid + (int64_t)B * h_kv * n_mblk > INT32_MAX)
     return fail(ATTN_ERR_SHAPE, "decode grid too large: splits x B x kv heads x head blocks must fit in int32");
-  // The kernels address one head block's partial rows through a 32-bit buffer range.
-  if ((int64_t)bm * n_split * d * 2 > (int64_t)UINT32_MAX)
-    return fail(ATTN_ERR_SHAPE, "too many splits (%lld): 128 x splits x d x 2 must fit in 32 bits",
+  // The merge addresses one sequence's partial rows through a 32-bit buffer range.
+  if ((int64_t)h_q * n_split * d * 2 > (int64_t)UINT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "too many splits (%lld): h_q x splits x d x 2 must fit in 32 bits",
                 (long long)n_split);
 
   const int64_t parts = (int64_t)B * h_q * n_split;
@@ -135,9 +135,9 @@ attn_status run_decode(attn::DecodeParams &p, const int32_t *kv_len, const float
   c.rows = B * h_q;
   c.n2 = h_q;
   c.d = d;
-  c.o_part_stride = d;
-  c.o_r1 = (int64_t)h_q * n_split * d;
-  c.o_r2 = n_split * d;
+  c.o_part_stride = (int64_t)h_q * d;  // split-major partial rows
+  c.o_r1 = (int64_t)n_split * h_q * d;
+  c.o_r2 = d;
   c.lse_part_stride = 1;
   c.lse_r1 = (int64_t)h_q * n_split;
   c.lse_r2 = n_split;

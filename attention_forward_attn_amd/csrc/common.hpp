@@ -78,7 +78,7 @@ struct DecodeParams {
   const int64_t *kv_start;
   const int32_t *kv_len;
   const float *sinks;
-  uint16_t *o_part;  // [B][h_q][n_split][D] bf16, normalised partial outputs
+  uint16_t *o_part;  // [B][n_split][h_q][D] bf16, normalised partial outputs
   float *lse_part;  // [B][h_q][n_split] fp32, natural-log LSE of each part
   int64_t q_sb, q_sh;
   int64_t k_st, k_sh;

@@ -144,17 +144,21 @@ __device__ void decode_merge(const DecodeParams &p, int m) {
   const int nh = min(MH, p.ratio - h0);
   const int r = threadIdx.x / CPR, ch = threadIdx.x % CPR;
   if (r >= nh) return;
-  const int64_t row0 = (int64_t)b * p.h_q + g * p.ratio + h0;  // partial row of the slice's first head
+  const int64_t row0 = (int64_t)b * p.h_q + g * p.ratio + h0;  // the slice's first head
+  // Partial rows are split-major per sequence: split i of head h at row
+  // (b * n_split + i) * h_q + h, so split i of this slice sits i * h_q rows on.
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(p.o_part + row0 * p.n_split * D, (uint32_t)((int64_t)nh * p.n_split * D * 2));
-  const uint32_t off = (uint32_t)(r * p.n_split * D * 2 + ch * 16);
+      make_rsrc(p.o_part + ((int64_t)b * p.n_split * p.h_q + g * p.ratio + h0) * D,
+                (uint32_t)(((int64_t)(n - 1) * p.h_q + nh) * D * 2));
+  const uint32_t off = (uint32_t)(r * D * 2 + ch * 16);
+  const uint32_t split_bytes = (uint32_t)(p.h_q * D * 2);
   const float *lp = p.lse_part + (row0 + r) * p.n_split;
   const int head = g * p.ratio + h0 + r;
   merge_parts<uint16_t, 16>(
       n, [&](int i) { return __hip_atomic_load(lp + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
       [&](int i) {
         Vec8<uint16_t> v;
-        v.a = __builtin_amdgcn_raw_buffer_load_b128(rs, off + (uint32_t)(i * D * 2), 0, kDeviceCoherent);
+        v.a = __builtin_amdgcn_raw_buffer_load_b128(rs, off + (uint32_t)i * split_bytes, 0, kDeviceCoherent);
         return v;
       },
       p.o_out + b * p.o_sb + (int64_t)head * p.o_sh + ch * 8,
@@ -336,12 +340,13 @@ void decode_split_kernel(DecodeParams p) {
       *reinterpret_cast<u32x2 *>(xw + lr * D * 2 + (chunk ^ (lr % SW)) * 16 + 8 * hi) = val;
     }
   __syncthreads();
-  // The head block's partial rows of this split, device-coherent: row h of
-  // the block at byte ((h * n_split) + split) * D * 2 of the descriptor.
-  const int64_t row0 = (int64_t)bi * p.h_q + g * p.ratio + hb * BM;
+  // The head block's partial rows of this split, device-coherent and
+  // contiguous (split-major rows, (bi * n_split + split) * h_q + head): the
+  // unit writes one run of nh * D * 2 bytes.
   const int nh = min(BM, p.ratio - hb * BM);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(p.o_part + row0 * p.n_split * D, (uint32_t)((int64_t)nh * p.n_split * D * 2));
+      make_rsrc(p.o_part + (((int64_t)bi * p.n_split + split) * p.h_q + g * p.ratio + hb * BM) * D,
+                (uint32_t)(nh * D * 2));
   const int cc = lane % NC;
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
@@ -349,8 +354,7 @@ void decode_split_kernel(DecodeParams p) {
     const u32x4 val = *reinterpret_cast<const u32x4 *>(xw + r * D * 2 + (cc ^ (r % SW)) * 16);
     const int hr = hgrp * 32 + r;  // head inside the head block
     if (hr < nh)
-      __builtin_amdgcn_raw_buffer_store_b128(val, rs, (uint32_t)((hr * p.n_split + split) * D * 2 + cc * 16), 0,
-                                             kDeviceCoherent);
+      __builtin_amdgcn_raw_buffer_store_b128(val, rs, (uint32_t)(hr * D * 2 + cc * 16), 0, kDeviceCoherent);
   }
   // Arrival: once every wave's partial stores are complete, count this split
   // in the counter of each merge slice of the head block.
