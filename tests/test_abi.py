@@ -260,6 +260,15 @@ def test_decode_noalloc_rejects(name, over, code):
     assert st == code, (st, lib.attn_last_error())
 
 
+def test_decode_rejects_partials_beyond_a_32_bit_range():
+    """The merge reads one sequence's partial rows through a 32-bit buffer range."""
+    lib = afa.load_library()
+    # h_q 128 x d 128 x 2 bytes x splits > 2^32 from 131073 splits of 64 keys
+    a = good_decode(split_size=64, max_kv_len=131073 * 64)
+    assert lib.attn_fwd_decode(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None) == 2
+    assert b"too many splits" in lib.attn_last_error()
+
+
 def test_decode_noalloc_rejects_sizes_beyond_its_scratch():
     lib = afa.load_library()
     # B = 64, h_q = 128, d = 256, 16384 keys in 512-key splits: 128 MiB of partials
