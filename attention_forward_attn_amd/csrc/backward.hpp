@@ -218,22 +218,31 @@ void bwd_dq_kernel(BwdParams p) {
         // then dS = P * (dP - D).
         const int lim = CAUSAL ? min(row + off, p.s_k - 1) : p.s_k - 1;
         const int lo = WINDOW ? row + off - p.window + 1 : 0;
-        auto p_group = [&](int gi) {
+        // Full tiles and masked tiles run separate copies of the dP product
+        // (a per-group branch inside one hook makes the compiler merge both
+        // versions of every group with register copies).
+        auto p_full = [&](int gi) {
+          const int kb = gi >> 2, q4 = gi & 3;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kb][4 * q4 + e] = fast_exp2(fmaf(s[kb][4 * q4 + e], p.c, -lse2));
+        };
+        auto p_masked = [&](int gi) {
           const int kb = gi >> 2, q4 = gi & 3;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * q4 + e;
             const float pv = fast_exp2(fmaf(s[kb][i], p.c, -lse2));
-            if (full) {
-              s[kb][i] = pv;
-            } else {
-              const int j = j0 + T::key_of(kb, i, hi);
-              s[kb][i] = (j > lim || j < lo) ? 0.0f : pv;
-            }
+            const int j = j0 + T::key_of(kb, i, hi);
+            s[kb][i] = (j > lim || j < lo) ? 0.0f : pv;
           }
         };
-        GroupHook<4 * T::NKB, T::NKK, decltype(p_group)> hp{p_group};
-        T::scores(dp, dreg, ln, so + T::TILE_BYTES, hp);
+        if (full) {
+          GroupHook<4 * T::NKB, T::NKK, decltype(p_full)> hp{p_full};
+          T::scores(dp, dreg, ln, so + T::TILE_BYTES, hp);
+        } else {
+          GroupHook<4 * T::NKB, T::NKK, decltype(p_masked)> hp{p_masked};
+          T::scores(dp, dreg, ln, so + T::TILE_BYTES, hp);
+        }
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
@@ -400,17 +409,22 @@ void bwd_dkdv_kernel(BwdParams p) {
           // Every row of the tile sees every key of the wave: no per-pair test.
           const bool full = i0 + BN <= p.s_q && w_key0 + 32 <= p.s_k && (!CAUSAL || w_key0 + 31 <= i0 + off) &&
                             (!WINDOW || w_key0 >= i0 + BN - 1 + off - p.window + 1);
-          auto p_group = [&](int g) {  // P = exp(scale*S - LSE) over the visible pairs, into s
+          // P = exp(scale*S - LSE), into s: over every pair (p_full), or
+          // over the visible pairs only (p_masked).  The two run in separate
+          // copies of the dP product: one hook that branched per group made
+          // the compiler merge both versions of every group with register
+          // copies (64 per tile).
+          auto p_full = [&](int g) {
+            const int rb = g >> 2, q4 = g & 3;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[rb][4 * q4 + e] = fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -lv[g][e]));
+          };
+          auto p_masked = [&](int g) {
             const int rb = g >> 2, q4 = g & 3, r4 = i0 + 32 * rb + 8 * q4 + 4 * hi;
-            if (full) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) s[rb][4 * q4 + e] = fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -lv[g][e]));
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float pv = fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -lv[g][e]));
-                s[rb][4 * q4 + e] = visible(r4 + e) ? pv : 0.0f;
-              }
+            for (int e = 0; e < 4; ++e) {
+              const float pv = fast_exp2(fmaf(s[rb][4 * q4 + e], p.c, -lv[g][e]));
+              s[rb][4 * q4 + e] = visible(r4 + e) ? pv : 0.0f;
             }
           };
           auto ds_group = [&](int g) {  // dS = P * (dP - D), into dp
@@ -419,8 +433,13 @@ void bwd_dkdv_kernel(BwdParams p) {
             for (int e = 0; e < 4; ++e) dp[rb][4 * q4 + e] = s[rb][4 * q4 + e] * (dp[rb][4 * q4 + e] - dv4[g][e]);
           };
           // dP = dO.V^T, with P computed between its MMAs
-          GroupHook<4 * T::NKB, T::NKK, decltype(p_group)> hp{p_group};
-          T::scores(dp, vreg, ln, so + T::TILE_BYTES, hp);
+          if (full) {
+            GroupHook<4 * T::NKB, T::NKK, decltype(p_full)> hp{p_full};
+            T::scores(dp, vreg, ln, so + T::TILE_BYTES, hp);
+          } else {
+            GroupHook<4 * T::NKB, T::NKK, decltype(p_masked)> hp{p_masked};
+            T::scores(dp, vreg, ln, so + T::TILE_BYTES, hp);
+          }
           u32x4 pp[T::NPV], pd[T::NPV];
           pack_operand(s, pp);
           // dV^T += dO^T . P, with dS computed between its MMAs
