@@ -63,6 +63,8 @@ SMALL = [
     (2, 8, 8, 128, [300, 5], 64),
     (2, 256, 2, 128, [129, 1030], 256),  # 128 query heads per kv head, two kv heads
     (3, 6, 2, 128, [17, 0, 90], 64),     # an empty sequence
+    (2, 320, 1, 128, [700, 1500], 512),  # three head blocks, the last one of 64 heads
+    (2, 96, 2, 256, [513, 40], 256),     # 48 heads per kv head: partial head block and merge slices
 ]
 
 
